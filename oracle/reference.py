@@ -1,0 +1,195 @@
+"""Plain fp64 definition of the attention-block forward (NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark, never by the product path.
+
+Every input is upcast exactly to float64 and nothing is rounded in between.
+Sources (page title, section):
+  [S5.4] "从文本到聊天模型" (onehacker.top), §5.4 Attention: q, k, v
+         projections with shapes Q (B,T,H,D), K and V (B,T,Hkv,D); the core is
+         score = Q K^T, weight = softmax(score), output = weight V.
+  [S5.5] same page, §5.5 Causal Attention: a causal mask keeps each position
+         from seeing later positions.
+  [S5.6] same page, §5.6 RoPE: q and k are rotated according to position so
+         that the scores see relative position.
+  [TBL]  "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io), §1 model
+         architecture table and the notes below it: RoPE as a rotation in
+         complex space; RMSNorm without learnable parameters; QK-norm applied
+         to q and k after RoPE; GQA (n_kv_head may be below n_head; groups of
+         query heads share K/V); sliding-window attention in an SSSL pattern
+         (short window = a quarter of the context).
+  [S10]  "从文本到聊天模型", §10.2-10.4: the new token's K and V are appended
+         to a per-layer cache, then its Q attends to every cached K/V.
+
+Readings where the pages are silent (each is listed with its pin in the design doc):
+  * RoPE pairs adjacent dims (2i, 2i+1), theta_i = base^(-2i/D), rotation by
+    +p*theta_i, positions 0-based (p = pos_offset + t).  Parity unpinned for
+    the pairing and the sign; the rest is pinned by closed forms/invariants.
+  * RMSNorm: y = x / sqrt(mean(x^2) + eps), eps = 1e-6.  Parity unpinned for eps.
+  * Scale 1/sqrt(D); no logit softcap inside attention (the +-15 softcap of the
+    table belongs to the LM head); no dropout.
+  * Window: key j is visible to query i iff 0 <= i - j < W (W keys including
+    the query itself); W >= T is full causal attention.
+  * GQA: query head h reads K/V head h // (H / Hkv).
+  * Decode: seqlens[b] = L counts the new token, which sits at index and
+    position L - 1; its normalised, rotated key and its raw value are written
+    to the cache first, then the query attends to keys
+    max(0, L - W) .. L - 1.  Older cache rows are used as stored.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+EPS = 1e-6
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a numpy array or torch tensor (bf16/fp32) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: bf16 and fp32 both upcast exactly
+        return x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def rope_inv_freq(D: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/D), i = 0 .. D/2-1, in float64 ([S5.6], [TBL])."""
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / D)
+
+
+def rope(x, positions, base: float) -> np.ndarray:
+    """Rotate each adjacent pair (x_2i, x_2i+1) by the angle p*theta_i.
+
+    x: (..., D); positions: integer array broadcastable to x.shape[:-1].
+    Returns float64 of x's shape.  ([S5.6], [TBL] RoPE row and note.)
+    """
+    x = _f64(x)
+    D = x.shape[-1]
+    p = np.asarray(positions, dtype=np.float64)
+    ang = p[..., None] * rope_inv_freq(D, base)          # (..., D/2)
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+def qk_norm(x, eps: float = EPS) -> np.ndarray:
+    """Parameter-free RMSNorm over the last (head) dimension ([TBL])."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rope_qknorm(q, k, base: float = 10000.0, pos_offset: int = 0):
+    """q (B,T,H,D), k (B,T,Hkv,D) -> (norm(rope(q)), norm(rope(k))).
+
+    The table places QK-norm after RoPE; positions are pos_offset + t.
+    """
+    q, k = _f64(q), _f64(k)
+    T = q.shape[1]
+    pos = (pos_offset + np.arange(T))[None, :, None]      # (1,T,1)
+    return qk_norm(rope(q, pos, base)), qk_norm(rope(k, pos, base))
+
+
+def band_mask(T: int, W: int) -> np.ndarray:
+    """visible[i, j] = 0 <= i - j < W ([S5.5] causal mask, [TBL] window)."""
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    d = i - j
+    return (d >= 0) & (d < W)
+
+
+def attention_core(qn, kn, v, W: int, return_probs: bool = False):
+    """softmax(q k^T / sqrt(D) restricted to the band) v, per (b, h).
+
+    qn (B,T,H,D) and kn (B,T,Hkv,D) are the already rotated and normalised
+    rows; v (B,T,Hkv,D) is raw.  Query head h reads K/V head h // (H/Hkv).
+    ([S5.4] score/softmax/output, [S5.5] causal, [TBL] GQA and window.)
+    """
+    qn, kn, v = _f64(qn), _f64(kn), _f64(v)
+    B, T, H, D = qn.shape
+    Hkv = kn.shape[2]
+    G = H // Hkv
+    vis = band_mask(T, W)
+    out = np.empty((B, T, H, D), dtype=np.float64)
+    probs = np.empty((B, H, T, T), dtype=np.float64) if return_probs else None
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            S = (qn[b, :, h, :] @ kn[b, :, g, :].T) * scale
+            S = np.where(vis, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            E = np.exp(S - m)
+            P = E / E.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = P @ v[b, :, g, :]
+            if return_probs:
+                probs[b, h] = P
+    return (out, probs) if return_probs else out
+
+
+def attn_fwd(q, k, v, window: int, base: float = 10000.0, pos_offset: int = 0,
+             return_probs: bool = False):
+    """The whole prefill forward from raw q, k, v: RoPE, QK-norm, attention."""
+    qn, kn = rope_qknorm(q, k, base, pos_offset)
+    return attention_core(qn, kn, v, window, return_probs)
+
+
+def attn_fwd_rows(q, k, v, rows, window: int, base: float = 10000.0,
+                  pos_offset: int = 0) -> np.ndarray:
+    """Output rows o[b, t, h, :] for a list of (b, t, h), one by one.
+
+    Same definition as attn_fwd, evaluated only for the requested query rows
+    (used to check full-size outputs on a sample).  Returns (len(rows), D).
+    """
+    D = q.shape[-1]
+    H, Hkv = q.shape[2], k.shape[2]
+    G = H // Hkv
+    res = np.empty((len(rows), D), dtype=np.float64)
+    for n, (b, t, h) in enumerate(rows):
+        g = h // G
+        lo = max(0, t - window + 1)
+        keys = np.arange(lo, t + 1)
+        qrow = _f64(q[b, t, h])
+        krows = _f64(k[b, lo:t + 1, g])                   # (nk, D)
+        vrows = _f64(v[b, lo:t + 1, g])
+        qn = qk_norm(rope(qrow, pos_offset + t, base))
+        kn = qk_norm(rope(krows, pos_offset + keys, base))
+        s = (kn @ qn) / math.sqrt(D)
+        e = np.exp(s - s.max())
+        res[n] = (e / e.sum()) @ vrows
+    return res
+
+
+def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window: int,
+                base: float = 10000.0):
+    """One decode step over a contiguous per-layer cache ([S10]).
+
+    q (B,H,D); k_new, v_new (B,Hkv,D) raw; caches (B,Tmax,Hkv,D) whose rows
+    before L-1 are used as stored; seqlens (B,) with L in [1, Tmax] counting
+    the new token.  Returns (o (B,H,D), k_cache_out, v_cache_out) where the
+    cache copies hold the appended row at index L-1.
+    """
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    L_all = np.asarray(_f64(seqlens), dtype=np.int64)
+    B, H, D = q.shape
+    Hkv = k_new.shape[1]
+    G = H // Hkv
+    o = np.empty((B, H, D), dtype=np.float64)
+    for b in range(B):
+        L = int(L_all[b])
+        p = L - 1
+        qn = qk_norm(rope(q[b], p, base))                  # (H, D)
+        kn = qk_norm(rope(k_new[b], p, base))              # (Hkv, D)
+        kc[b, p] = kn
+        vc[b, p] = v_new[b]
+        lo = max(0, L - window)
+        for h in range(H):
+            g = h // G
+            s = (kc[b, lo:L, g] @ qn[h]) / math.sqrt(D)
+            e = np.exp(s - s.max())
+            o[b, h] = (e / e.sum()) @ vc[b, lo:L, g]
+    return o, kc, vc

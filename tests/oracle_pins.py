@@ -1,0 +1,338 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when it
+disagrees with a closed form, an invariant the pages fix, a textbook library
+routine, or brute force.  ``ALL_PINS`` is run on the real oracle by
+``test_oracle_pins.py`` and on planted mutants of it by
+``test_oracle_mutants.py`` (every mutant must fail at least one pin).
+
+Sources of the facts (page title, section):
+  * "从文本到聊天模型" (onehacker.top) §5.4 (score, softmax, weighted sum of V;
+    Q (B,T,H,D), K/V (B,T,Hkv,D)), §5.5 (causal mask), §5.6 (RoPE gives
+    relative position), §10.2-10.4 (append new K/V, then attend).
+  * "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io) §1 table + notes
+    (RoPE as complex rotation, parameter-free RMSNorm, QK-norm after RoPE,
+    GQA, SSSL window of a quarter context).
+"""
+import math
+
+import numpy as np
+import torch
+
+from brute_ref import brute_attn
+
+TIGHT = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol=TIGHT, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# --------------------------------------------------------------- RoPE pins
+
+def pin_rope_position_zero_identity(O):
+    """RoPE at position 0 is the identity (a rotation by angle 0)."""
+    x = _rng(1).standard_normal((3, 5, 16))
+    _close(O.rope(x, 0, 10000.0), x, what="rope(x, 0)")
+
+
+def pin_rope_d2_closed_form(O):
+    """D=2 has theta_0 = base^0 = 1: (1, 0) at position p becomes (cos p, sin p)."""
+    for p in (1, 2, 7, 100, 2047):
+        got = O.rope(np.array([1.0, 0.0]), p, 10000.0)
+        _close(got, [math.cos(p), math.sin(p)], what=f"D=2 p={p}")
+        got = O.rope(np.array([0.0, 1.0]), p, 10000.0)
+        _close(got, [-math.sin(p), math.cos(p)], what=f"D=2 e1 p={p}")
+
+
+def pin_rope_frequency_closed_form(O):
+    """D=4: the second pair turns by p * base^(-2/4)."""
+    for base in (10000.0, 500.0):
+        th1 = base ** -0.5
+        for p in (3, 50):
+            got = O.rope(np.array([0.0, 0.0, 1.0, 0.0]), p, base)
+            _close(got, [0, 0, math.cos(p * th1), math.sin(p * th1)],
+                   what=f"D=4 base={base} p={p}")
+
+
+def pin_rope_complex_form(O):
+    """Adjacent pairs as complex numbers z_i = x_2i + i x_2i+1, times e^{i p theta_i}."""
+    D = 32
+    x = _rng(2).standard_normal((4, 7, D))
+    pos = np.arange(7)[None, :] * 13 + 5
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    theta = np.array([10000.0 ** (-2.0 * i / D) for i in range(D // 2)])
+    zr = z * np.exp(1j * pos[..., None] * theta)
+    want = np.empty_like(x)
+    want[..., 0::2] = zr.real
+    want[..., 1::2] = zr.imag
+    _close(O.rope(x, pos, 10000.0), want, tol=1e-11, what="complex form")
+
+
+def pin_rope_preserves_pair_norms(O):
+    D = 64
+    x = _rng(3).standard_normal((6, D))
+    y = O.rope(x, np.arange(6) * 311, 10000.0)
+    _close(np.hypot(y[:, 0::2], y[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]),
+           tol=1e-12, what="pair norms")
+
+
+def pin_rope_composition(O):
+    """rope(rope(x, a), b) = rope(x, a + b)."""
+    x = _rng(4).standard_normal((5, 32))
+    a, b = np.arange(5) * 17, np.arange(5) * 5 + 3
+    _close(O.rope(O.rope(x, a, 1e4), b, 1e4), O.rope(x, a + b, 1e4), tol=1e-11,
+           what="composition")
+
+
+def pin_rope_relative_position(O):
+    """<rope(q, m), rope(k, n)> depends only on m - n (the §5.6 purpose of RoPE)."""
+    r = _rng(5)
+    q, k = r.standard_normal(64), r.standard_normal(64)
+    base_dot = O.rope(q, 10, 1e4) @ O.rope(k, 3, 1e4)
+    for s in (1, 40, 1000):
+        _close(O.rope(q, 10 + s, 1e4) @ O.rope(k, 3 + s, 1e4), base_dot, tol=1e-10,
+               what=f"shift {s}")
+
+
+# --------------------------------------------------------------- norm pins
+
+def pin_norm_hand_example(O):
+    """x = (3, 4): mean of squares 12.5, so y = x / sqrt(12.5 + eps)."""
+    _close(O.qk_norm(np.array([3.0, 4.0])),
+           np.array([3.0, 4.0]) / math.sqrt(12.5 + 1e-6), what="norm (3,4)")
+
+
+def pin_norm_unit_rms(O):
+    """mean(y^2) = m / (m + eps) exactly, m = mean(x^2): unit RMS up to eps."""
+    x = _rng(6).standard_normal((10, 128)) * np.array([[0.1], [1], [3], [10], [1e-2],
+                                                        [5], [2], [7], [0.5], [100]])
+    y = O.qk_norm(x)
+    m = np.mean(x * x, axis=-1)
+    _close(np.mean(y * y, axis=-1), m / (m + 1e-6), tol=1e-12, what="unit rms")
+
+
+def pin_norm_commutes_with_rope(O):
+    """Rotation keeps the RMS, so norm(rope(x)) = rope(norm(x))."""
+    x = _rng(7).standard_normal((4, 6, 32)) * 3
+    pos = np.arange(6)[None, :] * 100
+    _close(O.qk_norm(O.rope(x, pos, 1e4)), O.rope(O.qk_norm(x), pos, 1e4),
+           tol=1e-12, what="norm o rope")
+
+
+# ---------------------------------------------------------- attention pins
+
+def _small(seed, B=2, T=12, H=4, Hkv=2, D=8, scale=1.0):
+    r = _rng(seed)
+    return (r.standard_normal((B, T, H, D)) * scale,
+            r.standard_normal((B, T, Hkv, D)) * scale,
+            r.standard_normal((B, T, Hkv, D)))
+
+
+def pin_brute_force(O):
+    """Oracle = scalar loops on tiny shapes, including GQA, windows and offsets."""
+    cases = [(1, 5, 2, 2, 4, 5, 0), (2, 6, 4, 2, 4, 2, 3), (1, 8, 3, 1, 6, 3, 0),
+             (1, 7, 2, 1, 2, 1, 9), (1, 8, 4, 4, 8, 100, 1)]
+    for n, (B, T, H, Hkv, D, W, off) in enumerate(cases):
+        q, k, v = _small(100 + n, B, T, H, Hkv, D, scale=2.0)
+        want = brute_attn(q.tolist(), k.tolist(), v.tolist(), W, 10000.0, off)
+        _close(O.attn_fwd(q, k, v, W, 10000.0, off), np.array(want), tol=1e-11,
+               what=f"brute case {n}")
+
+
+def pin_core_matches_sdpa_float64(O):
+    """The attention step equals torch SDPA (float64, CPU) with an explicit band
+    mask, scale 1/sqrt(D), and enable_gqa (contiguous head groups)."""
+    for (B, T, H, Hkv, D, W) in [(2, 33, 4, 4, 16, 33), (1, 40, 8, 2, 32, 7),
+                                 (2, 17, 6, 3, 8, 1), (1, 64, 4, 1, 64, 16)]:
+        r = _rng(T * 7 + W)
+        qn = r.standard_normal((B, T, H, D))
+        kn = r.standard_normal((B, T, Hkv, D))
+        v = r.standard_normal((B, T, Hkv, D))
+        i = np.arange(T)[:, None]
+        j = np.arange(T)[None, :]
+        mask = torch.from_numpy(((i - j) >= 0) & ((i - j) < W))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qn).transpose(1, 2), torch.from_numpy(kn).transpose(1, 2),
+            torch.from_numpy(v).transpose(1, 2), attn_mask=mask, scale=1.0 / math.sqrt(D),
+            enable_gqa=(H != Hkv)).transpose(1, 2).numpy()
+        _close(O.attention_core(qn, kn, v, W), ref, tol=1e-12, what=f"sdpa {B,T,H,Hkv,D,W}")
+
+
+def pin_single_token_returns_v(O):
+    """T = 1 (and row 0 in general): the only visible key is the query's own."""
+    q, k, v = _small(8, B=2, T=1, H=4, Hkv=2, D=16)
+    out = O.attn_fwd(q, k, v, 1)
+    _close(out, np.repeat(v, 2, axis=2), what="T=1")
+    q, k, v = _small(9, B=1, T=9, H=2, Hkv=2, D=16)
+    _close(O.attn_fwd(q, k, v, 9)[:, 0], v[:, 0], what="row 0")
+
+
+def pin_window_one_returns_v(O):
+    """W = 1: each query sees only itself, so o[t, h] = v[t, h // G]."""
+    q, k, v = _small(10, B=2, T=11, H=6, Hkv=3, D=8)
+    _close(O.attn_fwd(q, k, v, 1), np.repeat(v, 2, axis=2), what="W=1")
+
+
+def pin_constant_v(O):
+    q, k, _ = _small(11, B=1, T=10, H=2, Hkv=2, D=8)
+    v = np.broadcast_to(np.arange(8.0), (1, 10, 2, 8)).copy()
+    _close(O.attn_fwd(q, k, v, 4), v, what="constant v")
+
+
+def pin_probs_band_and_sum(O):
+    """Softmax rows sum to 1, are positive exactly on the band 0 <= i-j < W."""
+    q, k, v = _small(12, B=1, T=13, H=2, Hkv=1, D=8)
+    for W in (1, 3, 13, 50):
+        _, P = O.attn_fwd(q, k, v, W, return_probs=True)
+        _close(P.sum(axis=-1), np.ones((1, 2, 13)), what="row sums")
+        i = np.arange(13)[:, None]
+        j = np.arange(13)[None, :]
+        band = ((i - j) >= 0) & ((i - j) < W)
+        assert np.all((P > 0) == band[None, None]), f"band support W={W}"
+
+
+def pin_full_window_is_causal(O):
+    """Any W >= T reproduces full causal attention."""
+    q, k, v = _small(13, B=1, T=9, H=2, Hkv=2, D=8)
+    a = O.attn_fwd(q, k, v, 9)
+    _close(O.attn_fwd(q, k, v, 10), a, what="W=T+1")
+    _close(O.attn_fwd(q, k, v, 1000), a, what="W=1000")
+
+
+def pin_gqa_equals_repeated_mha(O):
+    """GQA equals MHA on K/V repeated G times per head group."""
+    q, k, v = _small(14, B=2, T=10, H=6, Hkv=2, D=8)
+    a = O.attn_fwd(q, k, v, 4)
+    b = O.attn_fwd(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), 4)
+    _close(a, b, what="gqa vs repeated mha")
+
+
+def pin_linear_in_v(O):
+    q, k, v1 = _small(15, B=1, T=10, H=2, Hkv=2, D=8)
+    v2 = _rng(16).standard_normal(v1.shape)
+    _close(O.attn_fwd(q, k, 2.0 * v1 - 3.0 * v2, 5),
+           2.0 * O.attn_fwd(q, k, v1, 5) - 3.0 * O.attn_fwd(q, k, v2, 5),
+           tol=1e-11, what="linearity")
+
+
+def pin_batch_independence(O):
+    q, k, v = _small(17, B=3, T=8, H=2, Hkv=1, D=8)
+    a = O.attn_fwd(q, k, v, 3)
+    perm = [2, 0, 1]
+    _close(O.attn_fwd(q[perm], k[perm], v[perm], 3), a[perm], what="batch perm")
+
+
+def pin_pos_offset_invariance(O):
+    """A shift of every position leaves the output unchanged (relative positions)."""
+    q, k, v = _small(18, B=1, T=12, H=2, Hkv=2, D=16, scale=3.0)
+    a = O.attn_fwd(q, k, v, 5, 1e4, 0)
+    _close(O.attn_fwd(q, k, v, 5, 1e4, 777), a, tol=1e-10, what="pos_offset")
+
+
+def pin_q_and_k_scale_invariance(O):
+    """QK-norm makes the output independent of the scale of q and of k rows
+    (up to the eps term, which moves scores by about eps/mean(x^2))."""
+    q, k, v = _small(19, B=1, T=10, H=2, Hkv=2, D=16)
+    a = O.attn_fwd(q, k, v, 10)
+    _close(O.attn_fwd(q * 37.0, k, v, 10), a, tol=1e-5, what="q scale")
+    _close(O.attn_fwd(q, k * 20.0, v, 10), a, tol=1e-5, what="k scale")
+
+
+def pin_rows_match_full(O):
+    """The one-row-at-a-time evaluation equals the full evaluation."""
+    q, k, v = _small(20, B=2, T=20, H=4, Hkv=2, D=16)
+    full = O.attn_fwd(q, k, v, 6, 1e4, 3)
+    rows = [(0, 0, 0), (1, 19, 3), (0, 7, 2), (1, 5, 1), (0, 19, 1)]
+    got = O.attn_fwd_rows(q, k, v, rows, 6, 1e4, 3)
+    _close(got, np.stack([full[b, t, h] for b, t, h in rows]), tol=1e-12, what="rows")
+
+
+# ------------------------------------------------------------- decode pins
+
+def _decode_case(seed, B=3, Tmax=12, H=4, Hkv=2, D=16):
+    r = _rng(seed)
+    return (r.standard_normal((B, H, D)), r.standard_normal((B, Hkv, D)),
+            r.standard_normal((B, Hkv, D)), r.standard_normal((B, Tmax, Hkv, D)),
+            r.standard_normal((B, Tmax, Hkv, D)))
+
+
+def pin_decode_matches_prefill(O):
+    """Decode of token L-1 over a cache holding the prefill's normalised, rotated
+    keys and raw values equals row L-1 of the prefill (append, then attend)."""
+    r = _rng(21)
+    B, T, H, Hkv, D = 2, 11, 4, 2, 16
+    q = r.standard_normal((B, T, H, D))
+    k = r.standard_normal((B, T, Hkv, D))
+    v = r.standard_normal((B, T, Hkv, D))
+    for W in (3, 11):
+        full = O.attn_fwd(q, k, v, W)
+        _, kn = O.rope_qknorm(q, k)
+        for L in (1, 4, 11):
+            kc = np.where(np.arange(T)[None, :, None, None] < L - 1, kn, 9.0)
+            vc = np.where(np.arange(T)[None, :, None, None] < L - 1, v, -9.0)
+            o, kco, vco = O.attn_decode(q[:, L - 1], k[:, L - 1], v[:, L - 1], kc, vc,
+                                        np.full(B, L), W)
+            _close(o, full[:, L - 1], tol=1e-11, what=f"decode L={L} W={W}")
+            _close(kco[:, L - 1], kn[:, L - 1], tol=1e-12, what="appended k")
+            _close(vco[:, L - 1], v[:, L - 1], tol=0, what="appended v")
+
+
+def pin_decode_first_token(O):
+    """L = 1: the new token attends only to itself, o = v_new of its group."""
+    q, kn, vn, kc, vc = _decode_case(22)
+    o, _, _ = O.attn_decode(q, kn, vn, kc, vc, np.ones(3, dtype=int), 5)
+    _close(o, np.repeat(vn, 2, axis=1), what="L=1")
+
+
+def pin_decode_touches_only_row(O):
+    q, kn, vn, kc, vc = _decode_case(23)
+    L = np.array([5, 12, 1])
+    _, kco, vco = O.attn_decode(q, kn, vn, kc, vc, L, 4)
+    for b in range(3):
+        keep = np.arange(12) != L[b] - 1
+        _close(kco[b, keep], kc[b, keep], tol=0, what="k rows kept")
+        _close(vco[b, keep], vc[b, keep], tol=0, what="v rows kept")
+
+
+def pin_decode_brute(O):
+    """Decode against scalar loops over the visible keys."""
+    q, kn, vn, kc, vc = _decode_case(24, B=2, Tmax=9, H=4, Hkv=2, D=6)
+    L = np.array([9, 6])
+    W = 4
+    o, _, _ = O.attn_decode(q, kn, vn, kc, vc, L, W)
+    for b in range(2):
+        p = L[b] - 1
+        # rotate + normalise by hand (adjacent pairs, +p*theta, eps 1e-6)
+        def rn(row):
+            out = []
+            for i in range(3):
+                a = p * 10000.0 ** (-(2.0 * i) / 6)
+                x, y = row[2 * i], row[2 * i + 1]
+                out += [x * math.cos(a) - y * math.sin(a), x * math.sin(a) + y * math.cos(a)]
+            r = 1.0 / math.sqrt(sum(z * z for z in out) / 6 + 1e-6)
+            return [z * r for z in out]
+        for h in range(4):
+            g = h // 2
+            qh = rn(list(q[b, h]))
+            ss, vs = [], []
+            for j in range(max(0, L[b] - W), L[b]):
+                kj = rn(list(kn[b, g])) if j == p else list(kc[b, j, g])
+                vj = list(vn[b, g]) if j == p else list(vc[b, j, g])
+                ss.append(sum(a * c for a, c in zip(qh, kj)) / math.sqrt(6))
+                vs.append(vj)
+            mx = max(ss)
+            ws = [math.exp(s - mx) for s in ss]
+            want = [sum(w * vv[d] for w, vv in zip(ws, vs)) / sum(ws) for d in range(6)]
+            _close(o[b, h], want, tol=1e-12, what=f"decode brute b={b} h={h}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

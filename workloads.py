@@ -1,0 +1,161 @@
+"""Seeded synthetic workloads for the attention-block forward.
+
+This module holds only shapes and seeded random draws. It contains none of the
+method's arithmetic (no RoPE, no normalisation, no softmax), so both the fp64
+oracle under ``oracle/`` and the HIP path may take their inputs from here
+without sharing any of the computation.
+
+Shapes follow the nanochat pages:
+  * d12 layer: hidden 768, 6 heads -> head dim 128, context 2048
+    ("约100美元训出对话模型，nanochat源码全链路拆解" (ikfou.com), sections on
+    the GPT forward and on tensor shapes B/T/H/D).
+  * sliding-window pattern SSSL: three short layers with a quarter of the
+    context, one full layer ("Nanochat与nanoGPT对比：关键升级"
+    (lzwjava.github.io), model-architecture table, sliding-window row and the
+    note below it).
+  * hidden 1024 with 16 query heads -> head dim 64 (the sns.style "Nano Chat"
+    article, model-configuration section); here with 4 K/V heads for GQA.
+  * decode over a per-layer KV cache of capacity T ("从文本到聊天模型"
+    (onehacker.top), sections 10.2-10.4).
+
+The pages' own workloads are end-to-end training and evaluation runs on public
+datasets with trained weights; seeded N(0,1) tensors of the same shapes stand
+in for those activations. After QK-norm every q/k row has unit RMS whatever
+the input scale, so N(0,1) inputs exercise the same operand ranges.
+
+Seed scheme: seed = 20260000 + 100*config + 10*layer + tensor, where tensor is
+0 q, 1 k, 2 v, 3 k_cache, 4 v_cache, 5 seqlens. Draws use
+``torch.Generator('cpu')`` and ``torch.randn`` in float32, then an RNE cast to
+bfloat16 where the config is bf16. The same host bits feed both sides.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SEED_BASE = 20260000
+T_Q, T_K, T_V, T_KCACHE, T_VCACHE, T_SEQLENS = range(6)
+
+
+def seed_for(config: int, layer: int, tensor: int) -> int:
+    return SEED_BASE + 100 * config + 10 * layer + tensor
+
+
+def randn(shape, seed: int, dtype: torch.dtype) -> torch.Tensor:
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def randint(low: int, high_inclusive: int, shape, seed: int) -> torch.Tensor:
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randint(low, high_inclusive + 1, tuple(shape), generator=g,
+                         dtype=torch.int64).to(torch.int32)
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    idx: int
+    name: str
+    B: int
+    T: int
+    H: int
+    Hkv: int
+    D: int
+    windows: tuple  # one entry per layer call
+    dtype: torch.dtype
+    rope_base: float = 10000.0
+    pos_offset: int = 0
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    idx: int
+    name: str
+    B: int
+    Tmax: int
+    H: int
+    Hkv: int
+    D: int
+    windows: tuple  # each window is run separately on the same inputs
+    dtype: torch.dtype
+    rope_base: float = 10000.0
+
+
+CONFIGS = {
+    0: PrefillConfig(0, "tiny-fp32", B=1, T=64, H=2, Hkv=2, D=32, windows=(64,),
+                     dtype=torch.float32),
+    1: PrefillConfig(1, "d12-L-prefill", B=8, T=2048, H=6, Hkv=6, D=128,
+                     windows=(2048,), dtype=torch.bfloat16),
+    2: PrefillConfig(2, "d12-SSSL", B=8, T=2048, H=6, Hkv=6, D=128,
+                     windows=(512, 512, 512, 2048), dtype=torch.bfloat16),
+    3: PrefillConfig(3, "gqa-SSSL", B=16, T=2048, H=16, Hkv=4, D=64,
+                     windows=(512, 512, 512, 2048), dtype=torch.bfloat16),
+    4: DecodeConfig(4, "decode", B=64, Tmax=2048, H=6, Hkv=6, D=128,
+                    windows=(512, 2048), dtype=torch.bfloat16),
+}
+
+
+def prefill_inputs(cfg: PrefillConfig, layer: int = 0, B=None, T=None):
+    """q (B,T,H,D), k and v (B,T,Hkv,D); optional B/T override for samples."""
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    q = randn((B, T, cfg.H, cfg.D), seed_for(cfg.idx, layer, T_Q), cfg.dtype)
+    k = randn((B, T, cfg.Hkv, cfg.D), seed_for(cfg.idx, layer, T_K), cfg.dtype)
+    v = randn((B, T, cfg.Hkv, cfg.D), seed_for(cfg.idx, layer, T_V), cfg.dtype)
+    return q, k, v
+
+
+def decode_inputs(cfg: DecodeConfig, set_idx: int = 0):
+    """q (B,H,D), k_new/v_new (B,Hkv,D), caches (B,Tmax,Hkv,D), seqlens (B,).
+
+    set_idx selects an independent input set (used to rotate sets so that a
+    repeated timing loop does not run out of the last-level cache).
+    Sequence lengths L_b are uniform in [1, Tmax]; L_b counts the new token.
+    """
+    c = cfg.idx + 10 * set_idx
+    q = randn((cfg.B, cfg.H, cfg.D), seed_for(c, 0, T_Q), cfg.dtype)
+    k_new = randn((cfg.B, cfg.Hkv, cfg.D), seed_for(c, 0, T_K), cfg.dtype)
+    v_new = randn((cfg.B, cfg.Hkv, cfg.D), seed_for(c, 0, T_V), cfg.dtype)
+    k_cache = randn((cfg.B, cfg.Tmax, cfg.Hkv, cfg.D), seed_for(c, 0, T_KCACHE), cfg.dtype)
+    v_cache = randn((cfg.B, cfg.Tmax, cfg.Hkv, cfg.D), seed_for(c, 0, T_VCACHE), cfg.dtype)
+    seqlens = randint(1, cfg.Tmax, (cfg.B,), seed_for(c, 0, T_SEQLENS))
+    return q, k_new, v_new, k_cache, v_cache, seqlens
+
+
+def small_prefill(B, T, H, Hkv, D, seed, dtype=torch.bfloat16, scale=1.0):
+    """Seeded small case for parity sweeps (ragged T, odd windows, ...)."""
+    q = randn((B, T, H, D), seed, torch.float32) * scale
+    k = randn((B, T, Hkv, D), seed + 1, torch.float32) * scale
+    v = randn((B, T, Hkv, D), seed + 2, torch.float32)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+# ---- counting helpers (pure combinatorics of the band mask, no arithmetic of
+# ---- the method itself): unmasked (query, key) pairs per (b, h).
+
+def unmasked_pairs(T: int, W: int) -> int:
+    """Number of (i, j) with 0 <= i - j < W and 0 <= j <= i < T."""
+    if W >= T:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def prefill_flops(B, T, H, D, W) -> int:
+    """4*D flops per unmasked pair (2D for q.k, 2D for p*v)."""
+    return 4 * D * unmasked_pairs(T, W) * B * H
+
+
+def decode_bytes(seqlens, Hkv, D, W, H, elem_bytes=2) -> int:
+    """Algorithmic HBM bytes of one decode call.
+
+    K and V rows visible under the window (the appended row included, read
+    from registers but counted once as its cache write), plus q, o, k_new,
+    v_new.
+    """
+    vis = sum(min(int(L), W) for L in seqlens)
+    kv = vis * Hkv * D * 2 * elem_bytes
+    B = len(seqlens)
+    small = (2 * B * H * D + 2 * B * Hkv * D) * elem_bytes
+    return kv + small
