@@ -1,0 +1,151 @@
+/*
+ * nc_attn.h -- C ABI of the MI355X (gfx950) causal self-attention block
+ * forward of the nanochat GPT: RoPE, parameter-free QK RMSNorm after RoPE,
+ * GQA attention with a per-layer sliding window, and a one-token decode step
+ * over a contiguous per-layer KV cache.
+ *
+ * Sources (page title, section):
+ *   [S5.4]  "从文本到聊天模型" (onehacker.top), §5.4 Attention: Q (B,T,H,D),
+ *           K and V (B,T,Hkv,D); score = Q K^T, softmax, weighted sum of V.
+ *   [S5.5]  same page, §5.5 Causal Attention: causal mask.
+ *   [S5.6]  same page, §5.6 RoPE: rotate q and k by position.
+ *   [S10]   same page, §10.2-10.4: per-layer KV cache of shape
+ *           (batch, seq_len, heads, head_dim); decode computes the new token's
+ *           q, k, v, appends k and v to the cache, then attends to all of it.
+ *   [TBL]   "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io), §1 model
+ *           architecture table and notes: RoPE, RMSNorm without parameters,
+ *           QK-norm after RoPE, GQA, SSSL sliding window (short = 1/4 context).
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   RoPE rotates adjacent pairs (x[2i], x[2i+1]) by +p*theta_i with
+ *   theta_i = rope_base^(-2i/D) and 0-based positions p = pos_offset + t;
+ *   QK-norm is y = x / sqrt(mean(x^2) + 1e-6); scores are scaled by 1/sqrt(D);
+ *   key j is visible to query i iff 0 <= i - j < window (window >= T is full
+ *   causal attention); query head h reads K/V head h / (H / Hkv).
+ *
+ * Memory and ownership, for every entry point:
+ *   - every tensor argument is a caller-owned DEVICE pointer to a contiguous,
+ *     row-major array, 16-byte aligned;
+ *   - element type is bfloat16 (NC_BF16) or float32 (NC_F32) for all float
+ *     tensors of one call; arithmetic is float32 (bf16 MFMA operands with
+ *     float32 accumulation on the bf16 path);
+ *   - ws is a caller-owned device workspace of at least the size reported by
+ *     the matching *_workspace_bytes query (it may be NULL when that is 0);
+ *     its contents on entry do not matter and are clobbered;
+ *   - stream is a hipStream_t (NULL = the default stream); all work is
+ *     enqueued asynchronously on it and nothing is allocated, freed or
+ *     synchronised; the library keeps no state between calls and is
+ *     thread-safe;
+ *   - inputs are not modified, except the two caches of nc_attn_decode
+ *     (exactly one row per sequence and K/V head).
+ *
+ * Errors: arguments are validated on the host before any HIP call. A non-OK
+ * status means nothing was enqueued. NC_ERR_INVALID: bad pointer, size,
+ * alignment, window, offset, base, dtype or workspace. NC_ERR_UNSUPPORTED:
+ * head dim other than 32, 64 or 128, or more query heads per K/V head than
+ * supported. NC_ERR_HIP: a launch failed (nc_last_error() has the HIP
+ * message). Faults inside kernels surface from the caller's next sync.
+ * nc_last_error() returns a thread-local description of the last failure of
+ * the calling thread. No function aborts, throws or prints.
+ */
+#ifndef NC_ATTN_H
+#define NC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NC_OK = 0,
+  NC_ERR_INVALID = 1,
+  NC_ERR_UNSUPPORTED = 2,
+  NC_ERR_HIP = 3
+} nc_status;
+
+typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
+
+/* RMSNorm epsilon inside QK-norm. */
+#define NC_QKNORM_EPS 1e-6
+
+/* ABI version of this header (bumped on any signature change). */
+#define NC_ABI_VERSION 1
+int nc_abi_version(void);
+
+/* Static description of a status code. Never NULL. */
+const char* nc_status_string(nc_status status);
+
+/* Detail of the calling thread's last failure ("" if none). Never NULL. */
+const char* nc_last_error(void);
+
+/*
+ * nc_rope_qknorm -- RoPE then parameter-free RMSNorm on q and k
+ * ([S5.6] rotation by position; [TBL] QK-norm after RoPE).
+ *
+ *   q      (B, T, H,   D)  input rows; position of row t is pos_offset + t
+ *   k      (B, T, Hkv, D)
+ *   q_out  (B, T, H,   D)  norm(rope(q)); may alias q exactly (in place)
+ *   k_out  (B, T, Hkv, D)  norm(rope(k)); may alias k exactly
+ * Any other overlap between inputs and outputs is undefined.
+ * Requires B, T, H, Hkv >= 1, D in {32, 64, 128}, pos_offset >= 0,
+ * pos_offset + T <= 2^30, rope_base finite and > 0.
+ */
+size_t nc_rope_qknorm_workspace_bytes(int T, int D, int pos_offset);
+nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
+                         int B, int T, int H, int Hkv, int D,
+                         double rope_base, int pos_offset, nc_dtype dtype,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_fwd -- prefill forward of one attention layer from RAW q, k, v
+ * ([S5.4] scores, softmax, weighted sum; [S5.5] causal mask; [S5.6] RoPE;
+ * [TBL] QK-norm after RoPE, GQA, sliding window).
+ *
+ *   q  (B, T, H,   D)  raw query projections
+ *   k  (B, T, Hkv, D)  raw key projections
+ *   v  (B, T, Hkv, D)  values
+ *   o  (B, T, H,   D)  output, o[b,t,h] = sum_j softmax_j(q'.k'_j / sqrt(D)) v_j
+ *                      over keys j with 0 <= t - j < window, q' and k' the
+ *                      rotated (positions pos_offset + t) and normalised rows
+ * Requires H % Hkv == 0, window >= 1 (window >= T: full causal), the sizes
+ * of nc_rope_qknorm, and o not overlapping any input.
+ */
+size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset);
+nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                      int B, int T, int H, int Hkv, int D, int window,
+                      double rope_base, int pos_offset, nc_dtype dtype,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_decode -- one decode step per sequence over a contiguous KV cache
+ * ([S10] append the new token's K/V, then attend; cache per layer of shape
+ * (batch, seq_len, heads, head_dim)).
+ *
+ *   q        (B, H,   D)        raw query of the new token
+ *   k_new    (B, Hkv, D)        raw key of the new token
+ *   v_new    (B, Hkv, D)        value of the new token
+ *   k_cache  (B, Tmax, Hkv, D)  rows 0 .. L-2 hold rotated, normalised keys;
+ *                               row L-1 is overwritten with norm(rope(k_new))
+ *   v_cache  (B, Tmax, Hkv, D)  row L-1 is overwritten with v_new
+ *   seqlens  (B,) int32 DEVICE array, L = seqlens[b] in [1, Tmax] counts the
+ *                               new token, whose position is L-1
+ *   o        (B, H, D)          softmax over keys max(0, L-window) .. L-1
+ * seqlens values outside [1, Tmax] are a precondition violation: the kernels
+ * clamp them to that range instead of reading out of bounds.
+ * Requires H % Hkv == 0, H / Hkv <= 64, window >= 1, Tmax >= 1, D in
+ * {32, 64, 128}; q, k_new, v_new and o must not overlap the caches.
+ */
+size_t nc_attn_decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
+nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* seqlens,
+                         void* o, int B, int Tmax, int H, int Hkv, int D,
+                         int window, double rope_base, nc_dtype dtype,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NC_ATTN_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_rope_amd as nc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nc_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(nc_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_is_built():
+    assert os.path.exists(nc.library_path()), "run __graft_entry__.build() first"
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    L = ctypes.CDLL(nc.library_path())
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in nc_attn.h but not exported"
+    # and the binding knows every one of them
+    assert set(names) == set(nc._SIGS), (set(names) ^ set(nc._SIGS))
+
+
+def test_version_and_strings():
+    L = nc.lib()
+    assert L.nc_abi_version() == 1
+    for s in range(4):
+        assert L.nc_status_string(s)
+    assert b"unknown" in L.nc_status_string(99)
+
+
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced on these paths
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, B=1, T=8, H=2, Hkv=2, D=64, window=8, base=1e4, off=0, dt=0,
+             ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    L = nc.lib()
+    return L.nc_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["H"], a["Hkv"], a["D"],
+                         a["window"], a["base"], a["off"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(v=P + 4), 1, "not 16-byte aligned"),
+    (dict(B=0), 1, "sizes"),
+    (dict(T=-1), 1, "sizes"),
+    (dict(H=3, Hkv=2), 1, "multiple"),
+    (dict(D=48), 2, "head dim"),
+    (dict(D=256), 2, "head dim"),
+    (dict(window=0), 1, "window"),
+    (dict(off=-5), 1, "pos_offset"),
+    (dict(base=0.0), 1, "rope_base"),
+    (dict(base=float("inf")), 1, "rope_base"),
+    (dict(base=float("nan")), 1, "rope_base"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(wsb=16), 1, "workspace"),
+    (dict(ws=None), 1, "ws is NULL"),
+    (dict(B=1 << 20, T=1 << 12, H=1 << 4), 1, "exceed"),
+])
+def test_attn_fwd_validation(kw, status, frag):
+    assert _fwd(**kw) == status
+    assert frag in nc.lib().nc_last_error().decode()
+
+
+def test_rope_qknorm_validation():
+    L = nc.lib()
+    assert L.nc_rope_qknorm(P, P, None, P, 1, 4, 2, 2, 32, 1e4, 0, 0, None, 0, None) == 1
+    assert b"q_out is NULL" in L.nc_last_error()
+    assert L.nc_rope_qknorm(P, P, P, P, 1, 4, 2, 2, 96, 1e4, 0, 0, None, 0, None) == 2
+    assert L.nc_rope_qknorm(P, P, P, P, 1, 4, 2, 2, 32, -1.0, 0, 0, None, 0, None) == 1
+    assert L.nc_rope_qknorm(P, P, P, P, 1, 4, 2, 2, 32, 1e4, (1 << 30), 0, None, 0, None) == 1
+    assert b"exceeds" in L.nc_last_error()
+
+
+def _dec(**kw):
+    a = dict(q=P, kn=P, vn=P, kc=P, vc=P, sl=P, o=P, B=4, Tmax=2048, H=8, Hkv=2, D=128,
+             window=512, base=1e4, dt=0, ws=P, wsb=1 << 24, stream=None)
+    a.update(kw)
+    L = nc.lib()
+    return L.nc_attn_decode(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["sl"], a["o"], a["B"],
+                            a["Tmax"], a["H"], a["Hkv"], a["D"], a["window"], a["base"], a["dt"],
+                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(sl=None), 1, "seqlens is NULL"),
+    (dict(sl=P + 2), 1, "4-byte"),
+    (dict(kc=None), 1, "k_cache is NULL"),
+    (dict(Tmax=0), 1, "sizes"),
+    (dict(H=256, Hkv=2), 2, "exceed 64"),
+    (dict(window=-1), 1, "window"),
+    (dict(D=16), 2, "head dim"),
+    (dict(ws=None), 1, "ws is NULL"),
+    (dict(wsb=8), 1, "workspace"),
+])
+def test_decode_validation(kw, status, frag):
+    assert _dec(**kw) == status
+    assert frag in nc.lib().nc_last_error().decode()
+
+
+def test_workspace_queries():
+    L = nc.lib()
+    assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
+    # one (cos, sin) fp32 pair per position and frequency, rounded to 256 bytes
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0) == 2048 * 64 * 8
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0) == 512  # 3*16*8 = 384 -> 512
+    n = L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048)
+    assert n > 0 and n % 256 == 0
+    assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 32)
+    with pytest.raises(ValueError, match="GPU"):
+        nc.attn_fwd(q, q, q, window=4)
+    with pytest.raises(ValueError, match="GPU"):
+        nc.rope_qknorm(q, q)

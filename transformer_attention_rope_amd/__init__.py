@@ -1,0 +1,205 @@
+"""Python binding of libnc_attn.so, the MI355X (gfx950) attention-block forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/nc_attn.h``. Tensors must be
+contiguous CUDA (HIP) tensors in bfloat16 or float32; work is enqueued on the
+current torch stream of the tensors' device. There is no CPU fallback: if the
+library is not built, or a tensor is not on the GPU, the call raises.
+
+    rope_qknorm(q, k, rope_base=1e4, pos_offset=0)          -> (q', k')
+    attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
+    attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window=..., rope_base=1e4) -> o
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_decode",
+    "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes", "rope_qknorm_workspace_bytes",
+    "NC_OK", "NC_ERR_INVALID", "NC_ERR_UNSUPPORTED", "NC_ERR_HIP", "NC_BF16", "NC_F32",
+]
+
+NC_OK, NC_ERR_INVALID, NC_ERR_UNSUPPORTED, NC_ERR_HIP = 0, 1, 2, 3
+NC_BF16, NC_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libnc_attn.so"
+_lib = None
+
+_vp, _i, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+_SIGS = {
+    "nc_abi_version": (_i, []),
+    "nc_status_string": (ctypes.c_char_p, [_i]),
+    "nc_last_error": (ctypes.c_char_p, []),
+    "nc_rope_qknorm_workspace_bytes": (_sz, [_i, _i, _i]),
+    "nc_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
+    "nc_attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
+    "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
+                            _vp, _sz, _vp]),
+}
+
+
+class NcError(RuntimeError):
+    """A non-OK status from the C ABI, with the library's detail message."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {message}")
+
+
+def _status_name(s):
+    return {0: "NC_OK", 1: "NC_ERR_INVALID", 2: "NC_ERR_UNSUPPORTED", 3: "NC_ERR_HIP"}.get(s, str(s))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree shared library (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _call(name, *args):
+    L = lib()
+    st = getattr(L, name)(*args)
+    if st != NC_OK:
+        raise NcError(st, L.nc_last_error().decode(errors="replace"))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NC_BF16
+    if t.dtype == torch.float32:
+        return NC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _gpu(t: torch.Tensor, name: str, ndim: int, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def rope_qknorm_workspace_bytes(T: int, D: int, pos_offset: int = 0) -> int:
+    return int(lib().nc_rope_qknorm_workspace_bytes(T, D, pos_offset))
+
+
+def attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset=0) -> int:
+    return int(lib().nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset))
+
+
+def attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window) -> int:
+    return int(lib().nc_attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds fewer than the {nbytes} bytes required")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def rope_qknorm(q, k, *, rope_base: float = 10000.0, pos_offset: int = 0, q_out=None, k_out=None):
+    """norm(rope(q)), norm(rope(k)); q (B,T,H,D), k (B,T,Hkv,D). Outputs may be q / k."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    q_out = torch.empty_like(q) if q_out is None else _gpu(q_out, "q_out", 4, q.dtype)
+    k_out = torch.empty_like(k) if k_out is None else _gpu(k_out, "k_out", 4, q.dtype)
+    if q_out.shape != q.shape or k_out.shape != k.shape:
+        raise ValueError("output shapes must match the inputs")
+    ws = _workspace(rope_qknorm_workspace_bytes(T, D, pos_offset), q.device, None)
+    _call("nc_rope_qknorm", _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, T, H, Hkv, D,
+          float(rope_base), int(pos_offset), _dt(q), _ptr(ws), 0 if ws is None else ws.numel(),
+          _stream(q))
+    return q_out, k_out
+
+
+def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: int = 0,
+             out=None, workspace=None):
+    """Prefill attention from raw q (B,T,H,D), k, v (B,T,Hkv,D) -> o (B,T,H,D)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset)
+    ws = _workspace(need, q.device, workspace)
+    _call("nc_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
+          float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o
+
+
+def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, *, window: int,
+                rope_base: float = 10000.0, out=None, workspace=None):
+    """One decode step: appends norm(rope(k_new)) and v_new at index seqlens-1 of the
+    caches (in place), then attends. q (B,H,D); k_new, v_new (B,Hkv,D);
+    caches (B,Tmax,Hkv,D); seqlens (B,) int32 on the GPU -> o (B,H,D)."""
+    q = _gpu(q, "q", 3)
+    k_new = _gpu(k_new, "k_new", 3, q.dtype)
+    v_new = _gpu(v_new, "v_new", 3, q.dtype)
+    k_cache = _gpu(k_cache, "k_cache", 4, q.dtype)
+    v_cache = _gpu(v_cache, "v_cache", 4, q.dtype)
+    seqlens = _gpu(seqlens, "seqlens", 1, torch.int32)
+    B, H, D = q.shape
+    Hkv = k_new.shape[1]
+    Tmax = k_cache.shape[1]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(k_cache.shape) != (B, Tmax, Hkv, D) or tuple(v_cache.shape) != (B, Tmax, Hkv, D)
+            or tuple(seqlens.shape) != (B,)):
+        raise ValueError("decode tensor shapes are inconsistent")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 3, q.dtype)
+    need = attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window)
+    ws = _workspace(need, q.device, workspace)
+    _call("nc_attn_decode", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+          _ptr(seqlens), _ptr(o), B, Tmax, H, Hkv, D, int(window), float(rope_base), _dt(q),
+          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o

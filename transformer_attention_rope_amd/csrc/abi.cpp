@@ -1,0 +1,185 @@
+// C ABI of the attention-block library: host-side validation, workspace
+// sizing and kernel dispatch. Every check runs before the first HIP call, so
+// argument errors are reported without touching the device.
+#include "../../include/nc_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+nc_status fail(nc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+nc_status ok() {
+  g_err[0] = '\0';
+  return NC_OK;
+}
+
+nc_status hip_fail(hipError_t e, const char* what) {
+  return fail(NC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+nc_status check_common(int B, int T, int H, int Hkv, int D, nc_dtype dt, const char* tname) {
+  if (dt != NC_BF16 && dt != NC_F32) return fail(NC_ERR_INVALID, "dtype %d is not NC_BF16 or NC_F32", (int)dt);
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || D < 1)
+    return fail(NC_ERR_INVALID, "sizes must be >= 1 (B=%d %s=%d H=%d Hkv=%d D=%d)", B, tname, T, H, Hkv, D);
+  if (H % Hkv != 0) return fail(NC_ERR_INVALID, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (D != 32 && D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
+  // every element index must fit comfortably in 63 bits and every row index in 31
+  const long long rows_q = (long long)B * T * H;
+  const long long rows_k = (long long)B * T * Hkv;
+  if (rows_q > 0x7fffffffLL || rows_k > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "B*%s*H=%lld rows exceed 2^31-1", tname, rows_q);
+  return NC_OK;
+}
+
+nc_status check_rope(double rope_base, int pos_offset, int T) {
+  if (!std::isfinite(rope_base) || !(rope_base > 0.0))
+    return fail(NC_ERR_INVALID, "rope_base must be finite and > 0 (got %g)", rope_base);
+  if (pos_offset < 0) return fail(NC_ERR_INVALID, "pos_offset must be >= 0 (got %d)", pos_offset);
+  if ((long long)pos_offset + T > (1LL << 30))
+    return fail(NC_ERR_INVALID, "pos_offset + T = %lld exceeds 2^30", (long long)pos_offset + T);
+  return NC_OK;
+}
+
+nc_status check_ptrs(const char* names[], const void* ptrs[], int n) {
+  for (int i = 0; i < n; ++i) {
+    if (ptrs[i] == nullptr) return fail(NC_ERR_INVALID, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(NC_ERR_INVALID, "%s is not 16-byte aligned", names[i]);
+  }
+  return NC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nc_abi_version(void) { return NC_ABI_VERSION; }
+
+const char* nc_status_string(nc_status s) {
+  switch (s) {
+    case NC_OK: return "NC_OK";
+    case NC_ERR_INVALID: return "NC_ERR_INVALID: invalid argument";
+    case NC_ERR_UNSUPPORTED: return "NC_ERR_UNSUPPORTED: unsupported shape";
+    case NC_ERR_HIP: return "NC_ERR_HIP: HIP runtime error";
+    default: return "unknown nc_status";
+  }
+}
+
+const char* nc_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------ rope_qknorm
+size_t nc_rope_qknorm_workspace_bytes(int T, int D, int pos_offset) {
+  (void)T;
+  (void)D;
+  (void)pos_offset;
+  return 0;
+}
+
+nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B, int T,
+                         int H, int Hkv, int D, double rope_base, int pos_offset, nc_dtype dt,
+                         void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  if (s != NC_OK) return s;
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  const char* names[] = {"q", "k", "q_out", "k_out"};
+  const void* ptrs[] = {q, k, q_out, k_out};
+  if ((s = check_ptrs(names, ptrs, 4)) != NC_OK) return s;
+  hipError_t e = nc::launch_rope_qknorm(q, k, q_out, k_out, B, T, H, Hkv, D, rope_base, pos_offset,
+                                        dt == NC_BF16 ? nc::kBF16 : nc::kF32, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rope_qknorm launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_fwd
+size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset) {
+  (void)B;
+  (void)H;
+  (void)Hkv;
+  (void)pos_offset;
+  if (T < 1 || D < 2) return 0;
+  return round_up(nc::rope_table_bytes(T, D));
+}
+
+nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T, int H,
+                      int Hkv, int D, int window, double rope_base, int pos_offset, nc_dtype dt,
+                      void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  if ((long long)T * (D / 2) > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
+  const char* names[] = {"q", "k", "v", "o", "ws"};
+  const void* ptrs[] = {q, k, v, o, ws};
+  if ((s = check_ptrs(names, ptrs, 5)) != NC_OK) return s;
+  const size_t need = nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset);
+  if (ws_bytes < need)
+    return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = nc::launch_rope_table(ws, T, D, rope_base, pos_offset, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  e = nc::launch_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, ws,
+                          dt == NC_BF16 ? nc::kBF16 : nc::kF32, st);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  return ok();
+}
+
+// -------------------------------------------------------------- attn_decode
+size_t nc_attn_decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window) {
+  if (B < 1 || Tmax < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || window < 1) return 0;
+  const size_t n = nc::decode_workspace_bytes(B, Tmax, H, Hkv, D, window);
+  return n ? round_up(n) : 0;
+}
+
+nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax, int H,
+                         int Hkv, int D, int window, double rope_base, nc_dtype dt, void* ws,
+                         size_t ws_bytes, void* stream) {
+  nc_status s = check_common(B, Tmax, H, Hkv, D, dt, "Tmax");
+  if (s != NC_OK) return s;
+  if (H / Hkv > 64) return fail(NC_ERR_UNSUPPORTED, "H/Hkv=%d query heads per K/V head exceed 64", H / Hkv);
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, 0, Tmax)) != NC_OK) return s;
+  const char* names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o"};
+  const void* ptrs[] = {q, k_new, v_new, k_cache, v_cache, o};
+  if ((s = check_ptrs(names, ptrs, 6)) != NC_OK) return s;
+  if (seqlens == nullptr) return fail(NC_ERR_INVALID, "seqlens is NULL");
+  if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+    return fail(NC_ERR_INVALID, "seqlens is not 4-byte aligned");
+  const size_t need = nc_attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window);
+  if (need > 0) {
+    if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL but %zu bytes are required", need);
+    if (!aligned16(ws)) return fail(NC_ERR_INVALID, "ws is not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+  }
+  hipError_t e = nc::launch_attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, o, B, Tmax, H,
+                                        Hkv, D, window, rope_base,
+                                        dt == NC_BF16 ? nc::kBF16 : nc::kF32, ws,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
+  return ok();
+}
+
+}  // extern "C"

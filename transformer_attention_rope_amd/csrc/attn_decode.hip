@@ -1,0 +1,424 @@
+// One-token decode step over a contiguous per-layer KV cache, split over the
+// key range ("split-KV"), for gfx950.
+//
+// What is computed ("从文本到聊天模型" (onehacker.top) §10.2-10.4: compute the
+// new token's q, k, v, append k and v to the cache, then let q attend to every
+// cached key; §10.3: one cache per layer of shape (batch, seq, heads, dim);
+// "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io) §1 table: QK-norm after
+// RoPE, GQA, sliding window):
+//   L = seqlens[b] (counts the new token), p = L - 1,
+//   k_cache[b, p] = RMSNorm(RoPE(k_new[b], p)),  v_cache[b, p] = v_new[b],
+//   o[b, h] = softmax_j( q'.k_j / sqrt(D) ) v_j  over j in [max(0, L-W), L-1],
+//   q' = RMSNorm(RoPE(q[b, h], p)).
+//
+// Design: decode reads every visible K/V row once, so it is bound by HBM.
+// Workgroups own (sequence b, K/V head g, up to GP query heads of g, a chunk
+// of C consecutive keys). Each group of CPR lanes streams one 16-byte chunk
+// of a K row and of a V row per key, so a wave reads whole 256-byte rows with
+// unit-stride loads; scores use a cross-lane sum over the CPR lanes. The
+// softmax is the running-maximum form (cache rows are caller data, so no
+// bound on the scores is assumed). Partial (max, sum, unnormalised output)
+// triples are merged across lanes with shuffles, across waves in LDS, and
+// across chunks by a second small kernel. The chunk holding key L-1 writes
+// the appended row and uses it from registers, so no workgroup waits on
+// another's write. A sequence whose visible range fits one chunk writes its
+// final output directly.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nc {
+
+struct DecArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* seqlens;
+  void* o;
+  float* part;  // [B][H][nsplit][D + 2]: o-partial (D), max, sum
+  int B, Tmax, H, Hkv, G, W;
+  int C;        // keys per chunk
+  int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
+  int ngh;      // head groups per K/V head = ceil(G / GP)
+  double rope_base;
+};
+
+template <typename Elem>
+struct ElemTraits;
+template <>
+struct ElemTraits<uint16_t> {
+  static constexpr int EPC = 8;
+  __device__ static void unpack(const u32x4_t& w, float* x) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x[2 * m] = bf_lo(w[m]);
+      x[2 * m + 1] = bf_hi(w[m]);
+    }
+  }
+  __device__ static u32x4_t pack(const float* x) {
+    u32x4_t w;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m], x[2 * m + 1]);
+    return w;
+  }
+  __device__ static float to_f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+  __device__ static uint16_t from_f(float x) { return (uint16_t)(pack_bf2(x, 0.f) & 0xffffu); }
+};
+template <>
+struct ElemTraits<float> {
+  static constexpr int EPC = 4;
+  __device__ static void unpack(const u32x4_t& w, float* x) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
+  }
+  __device__ static u32x4_t pack(const float* x) {
+    return u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                   __float_as_uint(x[3])};
+  }
+  __device__ static float to_f(float x) { return x; }
+  __device__ static float from_f(float x) { return x; }
+};
+
+__device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
+
+__device__ __forceinline__ int num_chunks(int L, int W, int C) {
+  const int lo = L > W ? L - W : 0;
+  return (L - lo + C - 1) / C;
+}
+
+template <int D, int GP, typename Elem>
+__global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
+  using TR = ElemTraits<Elem>;
+  constexpr int EPC = TR::EPC;
+  constexpr int CPR = D / EPC;        // lanes per key row
+  constexpr int KPW = 64 / CPR;       // keys per wave per step
+  constexpr int KPS = 4 * KPW;        // keys per workgroup per step
+  constexpr int U = 2;                // steps in flight per iteration
+
+  __shared__ float qs[GP][D];         // q' * log2(e)/sqrt(D)
+  __shared__ float knew_s[D];         // appended key (rounded to the cache type)
+  __shared__ float vnew_s[D];
+  __shared__ float2 cs[D / 2];
+  __shared__ float red_m[4][GP], red_l[4][GP];
+  __shared__ float red_o[4][GP][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = (int)blockIdx.x % a.nsplit;
+  const int rest = (int)blockIdx.x / a.nsplit;
+  const int hg = rest % a.ngh;
+  const int bg = rest / a.ngh;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+
+  const int L = clamp_len(a.seqlens[b], a.Tmax);
+  const int pos = L - 1;
+  const int lo = L > a.W ? L - a.W : 0;
+  const int nch = (L - lo + a.C - 1) / a.C;
+  if (split >= nch) return;
+  const int ks0 = lo + split * a.C;
+  const int ks1 = min(ks0 + a.C, L);
+  const bool owns_new = ks1 == L;
+
+  const int h0 = g * a.G + hg * GP;
+  const int nh = min(GP, a.G - hg * GP);
+
+  const Elem* qg = (const Elem*)a.q;
+  Elem* kc = (Elem*)a.k_cache;
+  Elem* vc = (Elem*)a.v_cache;
+
+  // ---- cos/sin at position pos (angles in fp64)
+  if (tid < D / 2) {
+    const double theta = pow(a.rope_base, -2.0 * (double)tid / D);
+    double s, c;
+    sincos((double)pos * theta, &s, &c);
+    cs[tid] = make_float2((float)c, (float)s);
+  }
+  __syncthreads();
+
+  // ---- q' for the nh heads, and the appended row if this chunk owns it:
+  // one wave per row, one (even, odd) pair per lane (D/2 <= 64)
+  const float qscale = kLog2e / sqrtf((float)D);
+  const int nrows = nh + (owns_new ? 1 : 0);
+  for (int r = wave; r < nrows; r += 4) {
+    const bool is_k = r == nh;
+    const Elem* src = is_k ? (const Elem*)a.k_new + ((size_t)b * a.Hkv + g) * D
+                           : qg + ((size_t)b * a.H + h0 + r) * D;
+    const int i = lane;  // pair index
+    float ye = 0.f, yo = 0.f;
+    if (i < D / 2) {
+      const float xe = TR::to_f(src[2 * i]), xo = TR::to_f(src[2 * i + 1]);
+      const float2 c = cs[i];
+      ye = xe * c.x - xo * c.y;
+      yo = xe * c.y + xo * c.x;
+    }
+    const float ss = group_sum<64>(ye * ye + yo * yo);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
+    if (i < D / 2) {
+      if (is_k) {
+        const Elem ke = TR::from_f(ye * inv), ko = TR::from_f(yo * inv);
+        knew_s[2 * i] = TR::to_f(ke);
+        knew_s[2 * i + 1] = TR::to_f(ko);
+        Elem* dst = kc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
+        dst[2 * i] = ke;
+        dst[2 * i + 1] = ko;
+        const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
+        Elem* vdst = vc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
+        const Elem v0 = vsrc[2 * i], v1 = vsrc[2 * i + 1];
+        vdst[2 * i] = v0;
+        vdst[2 * i + 1] = v1;
+        vnew_s[2 * i] = TR::to_f(v0);
+        vnew_s[2 * i + 1] = TR::to_f(v1);
+      } else {
+        qs[r][2 * i] = ye * inv * qscale;
+        qs[r][2 * i + 1] = yo * inv * qscale;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- stream the chunk's keys
+  const int cc = lane % CPR;        // chunk within the row
+  const int kl = lane / CPR;        // key slot within the wave
+  float qv[GP][EPC];
+#pragma unroll
+  for (int i = 0; i < GP; ++i)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qv[i][e] = i < nh ? qs[i][cc * EPC + e] : 0.f;
+
+  float m[GP], l[GP], acc[GP][EPC];
+#pragma unroll
+  for (int i = 0; i < GP; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[i][e] = 0.f;
+  }
+
+  const size_t row = (size_t)a.Hkv * D;
+  const Elem* kb = kc + ((size_t)b * a.Tmax * a.Hkv + g) * D + cc * EPC;
+  const Elem* vb = vc + ((size_t)b * a.Tmax * a.Hkv + g) * D + cc * EPC;
+
+  for (int base = ks0; base < ks1; base += KPS * U) {
+    u32x4_t kw[U], vw[U];
+    int keys[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPS + wave * KPW + kl;
+      keys[u] = key;
+      // the appended row is taken from LDS, never re-read from memory
+      if (key < ks1 && key != pos) {
+        kw[u] = ld16(kb + (size_t)key * row);
+        vw[u] = ld16(vb + (size_t)key * row);
+      } else {
+        kw[u] = u32x4_t{0, 0, 0, 0};
+        vw[u] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = keys[u];
+      float kx[EPC], vx[EPC];
+      if (key == pos) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          kx[e] = knew_s[cc * EPC + e];
+          vx[e] = vnew_s[cc * EPC + e];
+        }
+      } else {
+        TR::unpack(kw[u], kx);
+        TR::unpack(vw[u], vx);
+      }
+      const bool live = key < ks1;
+#pragma unroll
+      for (int i = 0; i < GP; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s += qv[i][e] * kx[e];
+        s = group_sum<CPR>(s);
+        if (live && i < nh) {
+          const float mn = fmaxf(m[i], s);
+          const float alpha = fast_exp2(m[i] - mn);  // m = -inf -> 0
+          const float pe = fast_exp2(s - mn);
+          l[i] = l[i] * alpha + pe;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[i][e] = acc[i][e] * alpha + pe * vx[e];
+          m[i] = mn;
+        }
+      }
+    }
+  }
+
+  // ---- merge the key slots of a wave (lanes kl differ by multiples of CPR)
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      const float mo = __shfl_xor(m[i], off, 64);
+      const float lo_ = __shfl_xor(l[i], off, 64);
+      const float mn = fmaxf(m[i], mo);
+      const float a0 = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
+      const float a1 = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
+      l[i] = l[i] * a0 + lo_ * a1;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float ao = __shfl_xor(acc[i][e], off, 64);
+        acc[i][e] = acc[i][e] * a0 + ao * a1;
+      }
+      m[i] = mn;
+    }
+  }
+  if (kl == 0) {
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      if (cc == 0) {
+        red_m[wave][i] = m[i];
+        red_l[wave][i] = l[i];
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red_o[wave][i][cc * EPC + e] = acc[i][e];
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves; write the final output or this chunk's partial
+  const bool single = nch == 1;
+  for (int idx = tid; idx < nh * D; idx += 256) {
+    const int i = idx / D, d = idx - (idx / D) * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_m[w][i]);
+    float lsum = 0.f, osum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = red_m[w][i] == -INFINITY ? 0.f : fast_exp2(red_m[w][i] - mx);
+      lsum += red_l[w][i] * sc;
+      osum += red_o[w][i][d] * sc;
+    }
+    const int h = h0 + i;
+    if (single) {
+      ((Elem*)a.o)[((size_t)b * a.H + h) * D + d] = TR::from_f(osum / lsum);
+    } else {
+      float* pp = a.part + (((size_t)b * a.H + h) * a.nsplit + split) * (D + 2);
+      pp[d] = osum;
+      if (d == 0) {
+        pp[D] = mx;
+        pp[D + 1] = lsum;
+      }
+    }
+  }
+}
+
+// One wave per (b, h) with more than one chunk: merge the chunk partials.
+template <int D, typename Elem>
+__global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
+  const int wid = ((int)blockIdx.x * 256 + (int)threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wid >= a.B * a.H) return;
+  const int b = wid / a.H, h = wid - (wid / a.H) * a.H;
+  const int L = clamp_len(a.seqlens[b], a.Tmax);
+  const int nch = num_chunks(L, a.W, a.C);
+  if (nch <= 1) return;
+  const float* pp = a.part + ((size_t)b * a.H + h) * a.nsplit * (D + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < nch; ++s) mx = fmaxf(mx, pp[s * (D + 2) + D]);
+  float lsum = 0.f;
+  constexpr int PER = (D + 63) / 64;
+  float o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  for (int s = 0; s < nch; ++s) {
+    const float* ps = pp + s * (D + 2);
+    const float sc = fast_exp2(ps[D] - mx);
+    lsum += ps[D + 1] * sc;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = e * 64 + lane;
+      if (d < D) o[e] += ps[d] * sc;
+    }
+  }
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = e * 64 + lane;
+    if (d < D) ((Elem*)a.o)[((size_t)b * a.H + h) * D + d] = ElemTraits<Elem>::from_f(o[e] * inv);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+static int decode_gp(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8)); }
+
+static int decode_chunk(int B, int Tmax, int H, int Hkv, int W) {
+  // aim for about 2048 busy workgroups; chunk is a power of two in [64, 1024]
+  const int G = H / Hkv;
+  const int ngh = (G + decode_gp(G) - 1) / decode_gp(G);
+  const long long span = (long long)(W < Tmax ? W : Tmax);
+  const long long keys = (long long)B * Hkv * ngh * span / 2;  // average visible keys
+  long long c = 64;
+  while (c < 1024 && keys / c > 2048) c <<= 1;
+  return (int)c;
+}
+
+static int decode_nsplit(int Tmax, int W, int C) {
+  const int span = W < Tmax ? W : Tmax;
+  return (span + C - 1) / C;
+}
+
+size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window) {
+  const int C = decode_chunk(B, Tmax, H, Hkv, window);
+  const int ns = decode_nsplit(Tmax, window, C);
+  if (ns <= 1) return 0;
+  return (size_t)B * H * ns * (D + 2) * sizeof(float);
+}
+
+template <int D, typename Elem>
+static hipError_t decode_d(DecArgs a, hipStream_t stream) {
+  const int GP = decode_gp(a.G);
+  a.ngh = (a.G + GP - 1) / GP;
+  const long long grid = (long long)a.B * a.Hkv * a.ngh * a.nsplit;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  switch (GP) {
+    case 1: hipLaunchKernelGGL((attn_decode_kernel<D, 1, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_decode_kernel<D, 2, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 4, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_decode_kernel<D, 8, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit <= 1) return e;
+  const long long waves = (long long)a.B * a.H;
+  const unsigned cgrid = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<D, Elem>), dim3(cgrid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
+                              int H, int Hkv, int D, int window, double rope_base, Dtype dt,
+                              void* ws, hipStream_t stream) {
+  DecArgs a{};
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.seqlens = seqlens;
+  a.o = o;
+  a.part = (float*)ws;
+  a.B = B;
+  a.Tmax = Tmax;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.G = H / Hkv;
+  a.W = window;
+  a.C = decode_chunk(B, Tmax, H, Hkv, window);
+  a.nsplit = decode_nsplit(Tmax, window, a.C);
+  a.rope_base = rope_base;
+  const bool bf = dt == kBF16;
+  switch (D) {
+    case 32: return bf ? decode_d<32, uint16_t>(a, stream) : decode_d<32, float>(a, stream);
+    case 64: return bf ? decode_d<64, uint16_t>(a, stream) : decode_d<64, float>(a, stream);
+    case 128: return bf ? decode_d<128, uint16_t>(a, stream) : decode_d<128, float>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nc

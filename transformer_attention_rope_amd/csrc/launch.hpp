@@ -1,0 +1,33 @@
+// Internal host-side launch interface between the C ABI (abi.cpp) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nc {
+
+enum Dtype { kBF16 = 0, kF32 = 1 };
+
+// ---- RoPE cos/sin table: tab[t][i] = (cos, sin)((pos_offset + t) * theta_i),
+// ---- computed in fp64 and stored as fp32 pairs.
+size_t rope_table_bytes(int T, int D);
+hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
+                             hipStream_t stream);
+
+hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
+                              int T, int H, int Hkv, int D, double rope_base, int pos_offset,
+                              Dtype dt, hipStream_t stream);
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T,
+                           int H, int Hkv, int D, int window, const void* tab, Dtype dt,
+                           hipStream_t stream);
+
+size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
+hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
+                              int H, int Hkv, int D, int window, double rope_base, Dtype dt,
+                              void* ws, hipStream_t stream);
+
+}  // namespace nc

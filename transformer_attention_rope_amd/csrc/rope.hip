@@ -1,0 +1,174 @@
+// RoPE + parameter-free QK RMSNorm kernels for gfx950.
+//
+// What is computed ("从文本到聊天模型" (onehacker.top) §5.6: q and k are rotated
+// by position; "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io) §1 table:
+// RMSNorm without learnable parameters applied to q and k after RoPE):
+//   x'[2i]   = x[2i] cos(p th_i) - x[2i+1] sin(p th_i)
+//   x'[2i+1] = x[2i] sin(p th_i) + x[2i+1] cos(p th_i),  th_i = base^(-2i/D)
+//   y = x' / sqrt(mean(x'^2) + 1e-6)
+// Angles are formed and reduced in fp64 so that large positions keep full
+// fp32 accuracy in cos/sin; the rotation and the norm run in fp32.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nc {
+
+// ---------------------------------------------------------------- table
+// tab[t * D/2 + i] = (cos, sin)((pos_offset + t) * base^(-2i/D)), fp32.
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tab, int T,
+                                                          int half, double inv_d2,
+                                                          double rope_base, int pos_offset) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx - t * half;
+  const double theta = pow(rope_base, -(double)i * inv_d2);
+  double s, c;
+  sincos((double)(pos_offset + t) * theta, &s, &c);
+  tab[idx] = make_float2((float)c, (float)s);
+}
+
+size_t rope_table_bytes(int T, int D) { return (size_t)T * (size_t)(D / 2) * sizeof(float2); }
+
+hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
+                             hipStream_t stream) {
+  const int half = D / 2;
+  const long long n = (long long)T * half;
+  const int grid = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, stream, (float2*)tab, T, half,
+                     2.0 / D, rope_base, pos_offset);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- rope + qknorm
+// One workgroup per (position t, block of up to BB batch rows). Every (b, t)
+// has H + Hkv rows of D elements; each thread owns 16-byte chunks, the CPR
+// chunks of one row sit in consecutive lanes and reduce their sum of squares
+// with cross-lane adds. The D/2 (cos, sin) pairs of the position are formed
+// once per workgroup in LDS. In-place use (out == in) is safe: each thread
+// writes back exactly the chunk it read.
+template <int D, typename Elem>
+__global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* __restrict__ q,
+                                                           const Elem* __restrict__ k,
+                                                           Elem* q_out, Elem* k_out, int B, int T,
+                                                           int H, int Hkv, double rope_base,
+                                                           int pos_offset, int BB, int nbb) {
+  constexpr bool kBf = sizeof(Elem) == 2;
+  constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;      // chunks per row
+  __shared__ float2 cs[D / 2];
+
+  const int t = (int)blockIdx.x / nbb;
+  const int b0 = ((int)blockIdx.x - t * nbb) * BB;
+  const int nb = min(BB, B - b0);
+  const int tid = threadIdx.x;
+  if (tid < D / 2) {
+    const double theta = pow(rope_base, -2.0 * (double)tid / D);
+    double s, c;
+    sincos((double)(pos_offset + t) * theta, &s, &c);
+    cs[tid] = make_float2((float)c, (float)s);
+  }
+  __syncthreads();
+
+  const int R = H + Hkv;
+  const int total = nb * R * CPR;
+  const int passes = (total + 255) / 256;
+  for (int it = 0; it < passes; ++it) {
+    const int ci = it * 256 + tid;
+    const bool ok = ci < total;
+    const int row = ok ? ci / CPR : 0;
+    const int cc = ci - row * CPR;
+    const int bb = row / R, rr = row - bb * R;
+    const int b = b0 + bb;
+    const Elem* src;
+    Elem* dst;
+    if (rr < H) {
+      const size_t off = (((size_t)b * T + t) * H + rr) * D + (size_t)cc * EPC;
+      src = q + off;
+      dst = q_out + off;
+    } else {
+      const size_t off = (((size_t)b * T + t) * Hkv + (rr - H)) * D + (size_t)cc * EPC;
+      src = k + off;
+      dst = k_out + off;
+    }
+    float x[EPC];
+    if (ok) {
+      const u32x4_t w = ld16(src);
+      if constexpr (kBf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          x[2 * m] = bf_lo(w[m]);
+          x[2 * m + 1] = bf_hi(w[m]);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < EPC; ++m) x[m] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < EPC / 2; ++m) {
+      const float2 r = cs[cc * (EPC / 2) + m];
+      const float xe = x[2 * m], xo = x[2 * m + 1];
+      const float ye = xe * r.x - xo * r.y;
+      const float yo = xe * r.y + xo * r.x;
+      x[2 * m] = ye;
+      x[2 * m + 1] = yo;
+      ss += ye * ye + yo * yo;
+    }
+    ss = group_sum<CPR>(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
+    if (ok) {
+      u32x4_t w;
+      if constexpr (kBf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = __float_as_uint(x[m] * inv);
+      }
+      st16(dst, w);
+    }
+  }
+}
+
+template <int D>
+static hipError_t rope_qknorm_d(const void* q, const void* k, void* q_out, void* k_out, int B,
+                                int T, int H, int Hkv, double rope_base, int pos_offset, Dtype dt,
+                                hipStream_t stream) {
+  // Enough rows per workgroup to amortise the per-position angles, while
+  // keeping at least T * ceil(B / BB) workgroups.
+  const int rows_per_b = H + Hkv;
+  int BB = (64 + rows_per_b - 1) / rows_per_b;
+  if (BB > B) BB = B;
+  if (BB < 1) BB = 1;
+  const int nbb = (B + BB - 1) / BB;
+  const long long nblk = (long long)T * nbb;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)nblk);
+  if (dt == kBF16) {
+    hipLaunchKernelGGL((rope_qknorm_kernel<D, uint16_t>), grid, dim3(256), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (uint16_t*)q_out,
+                       (uint16_t*)k_out, B, T, H, Hkv, rope_base, pos_offset, BB, nbb);
+  } else {
+    hipLaunchKernelGGL((rope_qknorm_kernel<D, float>), grid, dim3(256), 0, stream,
+                       (const float*)q, (const float*)k, (float*)q_out, (float*)k_out, B, T, H,
+                       Hkv, rope_base, pos_offset, BB, nbb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
+                              int T, int H, int Hkv, int D, double rope_base, int pos_offset,
+                              Dtype dt, hipStream_t stream) {
+  switch (D) {
+    case 32: return rope_qknorm_d<32>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset, dt, stream);
+    case 64: return rope_qknorm_d<64>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset, dt, stream);
+    case 128: return rope_qknorm_d<128>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset, dt, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nc
