@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention-block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+
+A step is one ``nc_attn_fwd`` call (RoPE + QK-norm + banded attention, the
+prefill path end to end, including its RoPE table build) over the d12 L-layer
+batch: B=8, T=2048, H=Hkv=6, D=128, full causal window, bf16, inputs resident
+in HBM. Four independent input sets are rotated so repeated steps do not run
+out of the 256 MB last-level cache. ``value`` is attention-forward TFLOP/s
+counting 4*D flops per unmasked (query, key) pair.
+
+The same run also times, with HIP events on the launch stream:
+  * the attention kernel alone (``nc_attn_fwd_tab`` with a prebuilt table),
+    the basis of ``roofline`` (against the 2516.6 TFLOP/s bf16 dense peak);
+  * the split-KV decode over a 2048-slot cache (B=64, H=Hkv=6, D=128) at
+    window 512 and 2048, as HBM GB/s of algorithmic bytes;
+  * ``nc_rope_qknorm`` on the d12 q and k, as HBM GB/s;
+  * the d12 SSSL and GQA SSSL stacks (4 layer calls sharing one RoPE table);
+and, on the host, the fp64 oracle on a bounded sample (``cpu_baseline``).
+
+Only rank 0 of a 1-GPU job exists here: ``--gpus`` above 1 exits.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s (unmasked pairs) + % bf16 MFMA peak; decode HBM GB/s"
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d12_pmc.txt")
+KERNEL_SOURCES = ["transformer_attention_rope_amd/csrc/attn_fwd.hip",
+                  "transformer_attention_rope_amd/csrc/device_common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the attention kernel from the committed PMC
+    summary, or None when missing or taken on a different kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    kv = {}
+    for line in open(PMC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def event_time_ms(fn, n, torch):
+    """Average ms per call of fn() over n back-to-back calls on the current
+    stream, bracketed by synchronisations."""
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(n):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def cpu_baseline(budget_s: float):
+    """fp64 oracle on the d12 L-layer workload, one (b, h) head (full T=2048)
+    at a time, until every head is done or about budget_s seconds passed."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = wl.CONFIGS[1]
+    W = cfg.windows[0]
+    q, k, v = wl.prefill_inputs(cfg, 0)
+    t0 = time.perf_counter()
+    n = 0
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            g = h // (cfg.H // cfg.Hkv)
+            oracle.attn_fwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], W)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = wl.prefill_flops(1, cfg.T, n, cfg.D, W)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"d12 L-layer prefill, {n} of {cfg.B * cfg.H} (b,h) heads "
+                      f"(T=2048, D=128, full causal), fp64 NumPy, {dt:.1f} s wall",
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
+    ap.add_argument("--only", default="all",
+                    choices=["all", "fwd", "fwd_tab", "decode", "rope", "stacks", "copy"],
+                    help="run one part (used for profiler runs); 'copy' runs a plain "
+                         "1 GiB device copy for counter calibration")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the attention forward shards over batch or K/V heads with no exchange). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_rope_amd as nc
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    K, Wm = args.steps, args.warmup
+    out = {}
+
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    # ------------------------------------------------ step: d12 L-layer prefill
+    cfg = wl.CONFIGS[1]
+    W = cfg.windows[0]
+    flops = wl.prefill_flops(cfg.B, cfg.T, cfg.H, cfg.D, W)
+    if args.only in ("all", "fwd", "fwd_tab"):
+        sets = []
+        for s in range(args.sets):
+            q, k, v = wl.prefill_inputs(cfg, layer=s)  # set s uses layer index s in the seed
+            sets.append((q.to(dev), k.to(dev), v.to(dev), torch.empty_like(q, device=dev)))
+        ws = torch.empty(nc.attn_fwd_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Hkv, cfg.D),
+                         dtype=torch.uint8, device=dev)
+        tab = nc.rope_table(cfg.T, cfg.D, device=dev)
+
+        def step(i):
+            q, k, v, o = sets[i % len(sets)]
+            nc.attn_fwd(q, k, v, window=W, out=o, workspace=ws)
+
+        def kern(i):
+            q, k, v, o = sets[i % len(sets)]
+            nc.attn_fwd_tab(q, k, v, tab, window=W, out=o)
+
+        if args.only in ("all", "fwd"):
+            for i in range(Wm):
+                step(i)
+            ms = event_time_ms(step, K, torch)
+            out["step_ms"] = ms
+        if args.only in ("all", "fwd_tab"):
+            for i in range(Wm):
+                kern(i)
+            out["kern_ms"] = event_time_ms(kern, K, torch)
+        del sets
+
+    if args.only in ("fwd", "fwd_tab"):
+        print(json.dumps(out))
+        return
+
+    # ------------------------------------------------------------ decode
+    dec = {}
+    if args.only in ("all", "decode"):
+        dcfg = wl.CONFIGS[4]
+        dsets = []
+        for s in range(args.sets):
+            q, kn, vn, kc, vc, L = wl.decode_inputs(dcfg, set_idx=s)
+            dsets.append([t.to(dev) for t in (q, kn, vn, kc, vc, L)] + [torch.empty_like(q, device=dev)])
+        for Wd in dcfg.windows:
+            wsd = torch.empty(max(nc.attn_decode_workspace_bytes(dcfg.B, dcfg.Tmax, dcfg.H, dcfg.Hkv,
+                                                                 dcfg.D, Wd), 1),
+                              dtype=torch.uint8, device=dev)
+
+            def dstep(i, Wd=Wd, wsd=wsd):
+                q, kn, vn, kc, vc, L, o = dsets[i % len(dsets)]
+                nc.attn_decode(q, kn, vn, kc, vc, L, window=Wd, out=o, workspace=wsd)
+
+            for i in range(Wm):
+                dstep(i)
+            ms = event_time_ms(dstep, K, torch)
+            nbytes = sum(wl.decode_bytes(ds[5].cpu().tolist(), dcfg.Hkv, dcfg.D, Wd, dcfg.H)
+                         for ds in dsets) / len(dsets)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            dec[f"W{Wd}"] = {"us_per_call": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
+                             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": int(nbytes)}
+        del dsets
+        if args.only == "decode":
+            print(json.dumps(dec))
+            return
+
+    # ------------------------------------------------------- rope_qknorm
+    rope = {}
+    if args.only in ("all", "rope"):
+        rsets = []
+        for s in range(args.sets):
+            q, k, _ = wl.prefill_inputs(cfg, layer=s)
+            rsets.append((q.to(dev), k.to(dev), torch.empty_like(q, device=dev),
+                          torch.empty_like(k, device=dev)))
+
+        def rstep(i):
+            q, k, qo, ko = rsets[i % len(rsets)]
+            nc.rope_qknorm(q, k, q_out=qo, k_out=ko)
+
+        for i in range(Wm):
+            rstep(i)
+        ms = event_time_ms(rstep, K, torch)
+        nbytes = 2 * (rsets[0][0].numel() + rsets[0][1].numel()) * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rope = {"workload": "q,k of the d12 layer (8x2048x6x128 each), bf16, read + write",
+                "us_per_call": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del rsets
+        if args.only == "rope":
+            print(json.dumps(rope))
+            return
+
+    # -------------------------------------------------- SSSL / GQA stacks
+    stacks = {}
+    if args.only in ("all", "stacks"):
+        for cidx in (2, 3):
+            c = wl.CONFIGS[cidx]
+            layers = [tuple(t.to(dev) for t in wl.prefill_inputs(c, layer=l)) for l in range(4)]
+            outs = [torch.empty_like(l[0]) for l in layers]
+            tabc = nc.rope_table(c.T, c.D, device=dev)
+
+            def sstep(i, layers=layers, outs=outs, tabc=tabc, c=c):
+                for l, (q, k, v) in enumerate(layers):
+                    nc.attn_fwd_tab(q, k, v, tabc, window=c.windows[l], out=outs[l])
+
+            for i in range(Wm):
+                sstep(i)
+            ms = event_time_ms(sstep, K, torch)
+            fl = sum(wl.prefill_flops(c.B, c.T, c.H, c.D, w) for w in c.windows)
+            tf = fl / (ms * 1e-3) / 1e12
+            stacks[c.name] = {"shape": f"B={c.B} T={c.T} H={c.H} Hkv={c.Hkv} D={c.D} "
+                                       f"windows={list(c.windows)}",
+                              "us_per_stack": round(ms * 1e3, 2), "TFLOP_per_s": round(tf, 1),
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del layers, outs
+        if args.only == "stacks":
+            print(json.dumps(stacks))
+            return
+
+    # ---------------------------------------------------------------- line
+    step_ms = out["step_ms"]
+    value = flops / (step_ms * 1e-3) / 1e12
+    kern_tf = flops / (out["kern_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "d12 L-layer prefill attention forward (RoPE + QK-norm fused), "
+                               "B=8 T=2048 H=Hkv=6 D=128 window=2048 (full causal), bf16",
+                   "B": cfg.B, "T": cfg.T, "H": cfg.H, "Hkv": cfg.Hkv, "D": cfg.D, "window": W,
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(kern_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(),
+                     "kernel": "attn_fwd_bf16_kernel<128>",
+                     "kernel_us": round(out["kern_ms"] * 1e3, 2),
+                     "flops_per_launch": flops},
+        "decode": dec,
+        "rope_qknorm": rope,
+        "stacks": stacks,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

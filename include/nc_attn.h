@@ -110,13 +110,40 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
  *                      over keys j with 0 <= t - j < window, q' and k' the
  *                      rotated (positions pos_offset + t) and normalised rows
  * Requires H % Hkv == 0, window >= 1 (window >= T: full causal), the sizes
- * of nc_rope_qknorm, and o not overlapping any input.
+ * of nc_rope_qknorm, T * Hkv * D * sizeof(element) < 2^32 (one sequence's K
+ * or V is addressed with 32-bit byte offsets), and o not overlapping any input.
  */
 size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset);
 nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
                       int B, int T, int H, int Hkv, int D, int window,
                       double rope_base, int pos_offset, nc_dtype dtype,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_rope_table / nc_attn_fwd_tab -- the same prefill forward split in two
+ * calls, for callers that run several layers over the same positions (the
+ * SSSL stack of the nanochat pages runs every layer at one T): the RoPE
+ * cos/sin table is built once and shared by every layer's nc_attn_fwd_tab.
+ * nc_attn_fwd(...) is exactly nc_rope_table into its workspace followed by
+ * nc_attn_fwd_tab.
+ *
+ *   tab  device buffer of nc_rope_table_bytes(T, D) bytes, 16-byte aligned,
+ *        caller-owned. nc_rope_table writes, for a_ti =
+ *        (pos_offset + t) * rope_base^(-2i/D), t < T, i < D/2, row-major:
+ *          part 1 (T*D/2 float pairs): (cos a_ti, sin a_ti) in fp32;
+ *          part 2 (T*D/2 pairs of bf16x2 words): (cos, -sin) and (sin, cos),
+ *        with a_ti formed and reduced modulo 2*pi in fp64.
+ * nc_attn_fwd_tab takes the q/k/v/o arguments of nc_attn_fwd and a table
+ * built for at least T positions with the wanted rope_base and pos_offset;
+ * the table is only read.
+ */
+size_t nc_rope_table_bytes(int T, int D);
+nc_status nc_rope_table(void* tab, size_t tab_bytes, int T, int D, double rope_base,
+                        int pos_offset, void* stream);
+nc_status nc_attn_fwd_tab(const void* q, const void* k, const void* v, void* o,
+                          int B, int T, int H, int Hkv, int D, int window,
+                          const void* tab, size_t tab_bytes, nc_dtype dtype,
+                          void* stream);
 
 /*
  * nc_attn_decode -- one decode step per sequence over a contiguous KV cache

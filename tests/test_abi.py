@@ -70,6 +70,7 @@ def _fwd(**kw):
     (dict(wsb=16), 1, "workspace"),
     (dict(ws=None), 1, "ws is NULL"),
     (dict(B=1 << 20, T=1 << 12, H=1 << 4), 1, "exceed"),
+    (dict(T=1 << 22, H=8, Hkv=8, D=128), 2, "2^32"),
 ])
 def test_attn_fwd_validation(kw, status, frag):
     assert _fwd(**kw) == status
@@ -115,9 +116,11 @@ def test_decode_validation(kw, status, frag):
 def test_workspace_queries():
     L = nc.lib()
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
-    # one (cos, sin) fp32 pair per position and frequency, rounded to 256 bytes
-    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0) == 2048 * 64 * 8
-    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0) == 512  # 3*16*8 = 384 -> 512
+    # fp32 (cos, sin) and bf16 {(cos,-sin),(sin,cos)} per position and
+    # frequency (16 bytes), rounded up to 256 bytes
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0) == 2048 * 64 * 16
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0) == 768  # 3*16*16 = 768
+    assert L.nc_rope_table_bytes(3, 32) == 768
     n = L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048)
     assert n > 0 and n % 256 == 0
     assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0

@@ -31,6 +31,7 @@ def _err(got, ref):
 
 def _check(got, ref, dtype, what):
     mx, mn = _err(got, ref)
+    print(f"[err] {what}: max {mx:.3e} mean {mn:.3e}", flush=True)
     if dtype == torch.float32:
         assert mx <= F32_MAX, f"{what}: max abs {mx:.3e} > {F32_MAX}"
     else:

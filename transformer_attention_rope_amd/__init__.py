@@ -19,6 +19,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_decode",
+    "rope_table", "attn_fwd_tab",
     "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes", "rope_qknorm_workspace_bytes",
     "NC_OK", "NC_ERR_INVALID", "NC_ERR_UNSUPPORTED", "NC_ERR_HIP", "NC_BF16", "NC_F32",
 ]
@@ -39,6 +40,9 @@ _SIGS = {
     "nc_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
+    "nc_rope_table_bytes": (_sz, [_i, _i]),
+    "nc_rope_table": (_i, [_vp, _sz, _i, _i, _d, _i, _vp]),
+    "nc_attn_fwd_tab": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
                             _vp, _sz, _vp]),
@@ -175,6 +179,33 @@ def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: in
     _call("nc_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
           float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o
+
+
+def rope_table(T: int, D: int, *, rope_base: float = 10000.0, pos_offset: int = 0,
+               device="cuda", out=None):
+    """(cos, sin) fp32 table for positions pos_offset .. pos_offset+T-1, shape (T, D/2, 2)."""
+    n = int(lib().nc_rope_table_bytes(T, D))
+    tab = torch.empty(max(n // 4, 1), dtype=torch.float32, device=device) if out is None else out
+    _gpu(tab, "out", tab.dim(), torch.float32)
+    _call("nc_rope_table", _ptr(tab), tab.numel() * 4, int(T), int(D), float(rope_base),
+          int(pos_offset), _stream(tab))
+    return tab
+
+
+def attn_fwd_tab(q, k, v, tab, *, window: int, out=None):
+    """attn_fwd with a prebuilt rope_table (shared by layers at the same positions)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    tab = _gpu(tab, "tab", tab.dim(), torch.float32)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
+    _call("nc_attn_fwd_tab", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
+          _ptr(tab), tab.numel() * 4, _dt(q), _stream(q))
     return o
 
 

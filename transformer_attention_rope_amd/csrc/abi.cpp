@@ -60,6 +60,14 @@ nc_status check_rope(double rope_base, int pos_offset, int T) {
   return NC_OK;
 }
 
+// one sequence's K or V must be addressable with 32-bit byte offsets
+nc_status check_seq_bytes(int T, int Hkv, int D, nc_dtype dt) {
+  const long long bytes = (long long)T * Hkv * D * (dt == NC_BF16 ? 2 : 4);
+  if (bytes >= (1LL << 32))
+    return fail(NC_ERR_UNSUPPORTED, "T*Hkv*D*elem = %lld bytes per sequence reaches 2^32", bytes);
+  return NC_OK;
+}
+
 nc_status check_ptrs(const char* names[], const void* ptrs[], int n) {
   for (int i = 0; i < n; ++i) {
     if (ptrs[i] == nullptr) return fail(NC_ERR_INVALID, "%s is NULL", names[i]);
@@ -130,6 +138,7 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
   if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
   if ((long long)T * (D / 2) > 0x7fffffffLL)
     return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
+  if ((s = check_seq_bytes(T, Hkv, D, dt)) != NC_OK) return s;
   const char* names[] = {"q", "k", "v", "o", "ws"};
   const void* ptrs[] = {q, k, v, o, ws};
   if ((s = check_ptrs(names, ptrs, 5)) != NC_OK) return s;
@@ -141,6 +150,52 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   e = nc::launch_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, ws,
                           dt == NC_BF16 ? nc::kBF16 : nc::kF32, st);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  return ok();
+}
+
+// ------------------------------------------------- rope table + attn_fwd_tab
+size_t nc_rope_table_bytes(int T, int D) {
+  if (T < 1 || D < 2) return 0;
+  return round_up(nc::rope_table_bytes(T, D));
+}
+
+nc_status nc_rope_table(void* tab, size_t tab_bytes, int T, int D, double rope_base,
+                        int pos_offset, void* stream) {
+  if (T < 1) return fail(NC_ERR_INVALID, "T must be >= 1 (got %d)", T);
+  if (D != 32 && D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
+  nc_status s = check_rope(rope_base, pos_offset, T);
+  if (s != NC_OK) return s;
+  if ((long long)T * (D / 2) > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
+  const char* names[] = {"tab"};
+  const void* ptrs[] = {tab};
+  if ((s = check_ptrs(names, ptrs, 1)) != NC_OK) return s;
+  const size_t need = nc_rope_table_bytes(T, D);
+  if (tab_bytes < need)
+    return fail(NC_ERR_INVALID, "table of %zu bytes is below the required %zu", tab_bytes, need);
+  hipError_t e = nc::launch_rope_table(tab, T, D, rope_base, pos_offset, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return ok();
+}
+
+nc_status nc_attn_fwd_tab(const void* q, const void* k, const void* v, void* o, int B, int T,
+                          int H, int Hkv, int D, int window, const void* tab, size_t tab_bytes,
+                          nc_dtype dt, void* stream) {
+  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((long long)T * (D / 2) > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
+  if ((s = check_seq_bytes(T, Hkv, D, dt)) != NC_OK) return s;
+  const char* names[] = {"q", "k", "v", "o", "tab"};
+  const void* ptrs[] = {q, k, v, o, tab};
+  if ((s = check_ptrs(names, ptrs, 5)) != NC_OK) return s;
+  const size_t need = nc::rope_table_bytes(T, D);
+  if (tab_bytes < need)
+    return fail(NC_ERR_INVALID, "table of %zu bytes is below the %zu needed for T=%d", tab_bytes, need, T);
+  hipError_t e = nc::launch_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, tab,
+                                     dt == NC_BF16 ? nc::kBF16 : nc::kF32, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   return ok();
 }

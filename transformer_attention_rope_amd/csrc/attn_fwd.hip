@@ -19,12 +19,14 @@
 //    lane then holds 16 keys of ONE query column, so the softmax needs no
 //    cross-lane work per tile, and the accumulator registers feed the P.V
 //    product directly as its B operand (O^T = V^T P^T).
-//  * Fixed-offset softmax: after QK-norm |q'|, |k'| <= sqrt(D), hence
-//    |q'.k'/sqrt(D)| <= sqrt(D). exp(s - sqrt(D)) therefore never overflows
-//    and is at least e^(-2 sqrt(D)) (~1.5e-10 at D=128), far from fp32/bf16
-//    underflow, so the softmax needs no running maximum and no rescaling of
-//    the output accumulators; the offset is preloaded into the accumulator.
-//    The result equals the textbook max-subtracted softmax up to rounding.
+//  * Softmax without a running maximum: after QK-norm |q'|, |k'| <= sqrt(D),
+//    hence |q'.k'/sqrt(D)| <= sqrt(D) and, in the log2 domain used here,
+//    |s| <= sqrt(D)*log2(e) (16.3 at D=128). 2^s then lies in
+//    [2^-16.3, 2^16.3] and the row sum below T * 2^16.3, far inside the fp32
+//    and bf16 ranges, so the numerators need no max subtraction and the
+//    output accumulators are never rescaled. The normalisation by the row
+//    sum cancels any common factor, so the result equals the textbook
+//    max-subtracted softmax up to rounding.
 //  * V is transposed into LDS (V^T[d][key]) with keys permuted so that each
 //    MFMA A-operand fetch is one 16-byte LDS read matching the key order the
 //    score accumulator hands over.
@@ -32,9 +34,11 @@
 //    inside skip the mask. Heaviest query tiles are dispatched first.
 //
 // fp32 path: exact fp32 arithmetic on the vector ALUs (one thread per query
-// column), same band, same fixed-offset softmax.
+// column), same band, same softmax without a running maximum.
 #include "device_common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace nc {
 
@@ -43,7 +47,8 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
-  const float2* tab;  // [T][D/2] (cos, sin) for positions pos_offset + t
+  const float2* tabq;  // [T][D/2] (cos, sin) fp32 for positions pos_offset + t
+  const uint2* tabk;   // [T][D/2] bf16 pairs {(cos, -sin), (sin, cos)}
   int B, T, H, Hkv, W;
   int G;         // H / Hkv
   int hpw_log2;  // log2(query heads per workgroup)
@@ -51,7 +56,6 @@ struct FwdArgs {
   int nqt;       // query tiles per (b, head group)
   int bp_log2;   // log2(positions per workgroup)
   float qscale;  // log2(e) / sqrt(D): folded into q'
-  float offset;  // sqrt(D) * log2(e): fixed softmax offset (log2 domain)
 };
 
 // =====================================================================
@@ -59,19 +63,22 @@ struct FwdArgs {
 // =====================================================================
 template <int D>
 struct BfCfg {
-  static constexpr int NT = 256;       // threads per workgroup
-  static constexpr int NC = 128;       // query columns per workgroup
-  static constexpr int BN = 64;        // keys per tile
-  static constexpr int KS = D / 16;    // MFMA k-steps of Q.K^T
-  static constexpr int DB = D / 32;    // 32-row blocks of O^T
-  static constexpr int RB = BN / 32;   // 32-key blocks per tile
-  static constexpr int PS = BN / 16;   // MFMA k-steps of P.V
-  static constexpr int KLD = D + 8;    // LDS row stride of K (bf16), +16 B against bank conflicts
-  static constexpr int VLD = BN + 8;   // LDS row stride of V^T (bf16)
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int RPP = NT / CPR; // K rows staged per pass
-  static constexpr int NKP = BN / RPP; // K staging passes
-  static constexpr int NMB = (BN / 4) * CPR;  // 4-key x 8-dim V micro-blocks
+  static constexpr int NW = 8;          // waves per workgroup
+  static constexpr int NT = 64 * NW;    // threads per workgroup
+  static constexpr int NC = 32 * NW;    // query columns per workgroup
+  static constexpr int BN = 64;         // keys per tile
+  static constexpr int KS = D / 16;     // MFMA k-steps of Q.K^T
+  static constexpr int DB = D / 32;     // 32-row blocks of O^T
+  static constexpr int RB = BN / 32;    // 32-key blocks per tile
+  static constexpr int PS = BN / 16;    // MFMA k-steps of P.V
+  static constexpr int KLD = D + 8;     // LDS row stride of K (bf16), +16 B against bank conflicts
+  static constexpr int VLD = BN + 8;    // LDS row stride of V^T (bf16)
+  static constexpr int CPR = D / 8;     // 16-byte chunks per K row
+  static constexpr int KCH = BN * CPR;  // K chunks per tile
+  static constexpr int NKP = (KCH + NT - 1) / NT;  // K chunks per thread
+  static constexpr int NMB = (BN / 4) * (D / 4);   // 4-key x 4-dim V micro-blocks per tile
+  static constexpr int KBUF = BN * KLD; // bf16 elements per K buffer
+  static constexpr int VBUF = D * VLD;  // bf16 elements per V^T buffer
 };
 
 // Position of key kk (0..BN-1) inside a V^T row. The score accumulator of
@@ -85,17 +92,16 @@ __device__ __forceinline__ int vt_pos(int kk) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(FwdArgs p) {
+__global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   using C = BfCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[C::BN * C::KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * C::VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * C::VBUF];
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)p.v;
   uint16_t* __restrict__ og = (uint16_t*)p.o;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 31, hf = lane >> 5;
 
   // ---- work item: heaviest (latest) query tiles first
@@ -115,11 +121,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(FwdArgs p) {
   const bool tvalid = t < p.T;
   const int tc = tvalid ? t : p.T - 1;
 
-  // ---- Q: load, RoPE, RMSNorm, fold log2(e)/sqrt(D), pack as MFMA B operand
+  // ---- Q: load, RoPE (fp32 table), RMSNorm, fold log2(e)/sqrt(D), pack as
+  // ---- the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7)
   bf16x8_t bq[C::KS];
   {
     const uint16_t* qrow = qg + (((size_t)b * p.T + tc) * p.H + h) * D;
-    const float2* trow = p.tab + (size_t)tc * (D / 2);
+    const float2* trow = p.tabq + (size_t)tc * (D / 2);
     float x[C::KS][8];
     float ss = 0.f;
 #pragma unroll
@@ -139,8 +146,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(FwdArgs p) {
         ss += ye * ye + yo * yo;
       }
     }
-    ss += __shfl_xor(ss, 32, 64);
-    const float sc = p.qscale / sqrtf(ss * (1.0f / D) + kEps);
+    ss = sum_halves(ss);
+    const float sc = p.qscale * rsq(ss * (1.0f / D) + kEps);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       u32x4_t w;
@@ -154,75 +161,94 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(FwdArgs p) {
   const int k_first = max(0, q0 - p.W + 1);
   const int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
 
-  // ---- staging assignment
-  const int kc = tid % C::CPR, kr0 = tid / C::CPR;          // K chunks
-  const bool vact = tid < C::NMB;
-  const int vgp = tid & 15, vc = tid >> 4;                  // V micro-block: keys 4*vgp.., dims 8*vc..
-  const size_t kv_row = (size_t)p.Hkv * D;                  // elements between consecutive tokens
-  const uint16_t* kbase = kg + ((size_t)b * p.T * p.Hkv + g) * D;
-  const uint16_t* vbase = vg + ((size_t)b * p.T * p.Hkv + g) * D;
+  // ---- staging: buffer resources whose ranges end at token T (reads past
+  // ---- the tail return zeros), per-thread byte offsets, per-tile SGPR offsets
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const size_t kv_base = ((size_t)b * p.T * p.Hkv + g) * D;
+  const uint32_t kv_records = (uint32_t)(((size_t)p.T * p.Hkv - g) * D * 2);
+  const char* kseq = (const char*)((const uint16_t*)p.k + kv_base);
+  const char* vseq = (const char*)((const uint16_t*)p.v + kv_base);
+  const uint32_t tab_row = (D / 2) * 8;
+  const uint32_t tab_records = (uint32_t)p.T * tab_row;
 
-  u32x4_t kraw[C::NKP];
-  f32x4_t ktab[C::NKP][2];
-  u32x4_t vraw[4];
+  uint32_t k_voff[C::NKP], t_voff[C::NKP], k_lds[C::NKP];
+  bool k_act[C::NKP];
+#pragma unroll
+  for (int j = 0; j < C::NKP; ++j) {
+    const int idx = tid + C::NT * j;
+    const int kr = idx / C::CPR, kc = idx % C::CPR;
+    k_act[j] = idx < C::KCH;
+    k_voff[j] = (uint32_t)kr * row_bytes + kc * 16;
+    t_voff[j] = (uint32_t)kr * (D / 2) * 8 + kc * 32;
+    k_lds[j] = kr * C::KLD + kc * 8;
+  }
+  const bool v_act = tid < C::NMB;
+  const int vgp = tid & 15, vd = tid >> 4;  // V micro-block: keys 4*vgp.., dims 4*vd..
+  const uint32_t v_voff = (uint32_t)(4 * vgp) * row_bytes + vd * 8;
+  const int v_lds = (4 * vd) * C::VLD + vt_pos(4 * vgp);
 
+  u32x4_t kw[C::NKP], kt_[C::NKP][2];
+  u32x2_t vw[4];
+
+  // Resources rebased on the tile's first key: rows past token T (and only
+  // those) fall beyond num_records and read as zero.
   auto gload = [&](int kt) {
-    const int j0 = kt * C::BN;
+    // a tile past the sequence (staged but never used) gets empty ranges
+    const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
+    const uint32_t st = (uint32_t)kt * C::BN * tab_row;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
+    const uint32_t nt = __builtin_amdgcn_readfirstlane(st < tab_records ? tab_records - st : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq + so, nk);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc((const char*)p.tabk + st, nt);
 #pragma unroll
     for (int j = 0; j < C::NKP; ++j) {
-      const int key = j0 + kr0 + C::RPP * j;
-      if (key < p.T) {
-        kraw[j] = ld16(kbase + (size_t)key * kv_row + kc * 8);
-        const float2* tr = p.tab + (size_t)key * (D / 2) + kc * 4;
-        ktab[j][0] = *reinterpret_cast<const f32x4_t*>(tr);
-        ktab[j][1] = *reinterpret_cast<const f32x4_t*>(tr + 2);
-      } else {
-        kraw[j] = u32x4_t{0, 0, 0, 0};
-        ktab[j][0] = f32x4_t{1.f, 0.f, 1.f, 0.f};
-        ktab[j][1] = f32x4_t{1.f, 0.f, 1.f, 0.f};
+      if (C::NKP * C::NT == C::KCH || k_act[j]) {
+        kw[j] = bload16(rk, k_voff[j], 0);
+        kt_[j][0] = bload16(rt, t_voff[j], 0);
+        kt_[j][1] = bload16(rt, t_voff[j] + 16, 0);
       }
     }
-    if (vact) {
+    if (C::NMB >= C::NT || v_act) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * vgp + r;
-        vraw[r] = key < p.T ? ld16(vbase + (size_t)key * kv_row + vc * 8) : u32x4_t{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r) vw[r] = bload8(rv, v_voff + r * row_bytes, 0);
     }
   };
 
-  auto stage = [&]() {
+  // RoPE + RMSNorm of the staged K chunks (bf16 pair dot products against the
+  // (cos,-sin)/(sin,cos) table), and the V micro-block transposed into V^T.
+  auto stage = [&](int buf) {
+    uint16_t* kb = Ks + buf * C::KBUF;
+    uint16_t* vb = Vt + buf * C::VBUF;
 #pragma unroll
     for (int j = 0; j < C::NKP; ++j) {
-      float y[8];
-      float ss = 0.f;
-      const float cs[8] = {ktab[j][0][0], ktab[j][0][1], ktab[j][0][2], ktab[j][0][3],
-                           ktab[j][1][0], ktab[j][1][1], ktab[j][1][2], ktab[j][1][3]};
+      if (C::NKP * C::NT == C::KCH || k_act[j]) {
+        float ss = dot2bf(kw[j][0], kw[j][0], 0.f);
+        ss = dot2bf(kw[j][1], kw[j][1], ss);
+        ss = dot2bf(kw[j][2], kw[j][2], ss);
+        ss = dot2bf(kw[j][3], kw[j][3], ss);  // a rotation keeps the sum of squares
+        ss = dpp_group_sum<C::CPR>(ss);
+        const float inv = rsq(ss * (1.0f / D) + kEps);
+        u32x4_t w;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float xe = bf_lo(kraw[j][m]), xo = bf_hi(kraw[j][m]);
-        const float c = cs[2 * m], sn = cs[2 * m + 1];
-        y[2 * m] = xe * c - xo * sn;
-        y[2 * m + 1] = xe * sn + xo * c;
-        ss += xe * xe + xo * xo;  // a rotation keeps the sum of squares
+        for (int m = 0; m < 4; ++m) {
+          const u32x4_t& tt = kt_[j][m >> 1];
+          const float xe = dot2bf(kw[j][m], tt[2 * (m & 1)], 0.f);
+          const float xo = dot2bf(kw[j][m], tt[2 * (m & 1) + 1], 0.f);
+          w[m] = pack_bf2(xe * inv, xo * inv);
+        }
+        st16(kb + k_lds[j], w);
       }
-      ss = group_sum<C::CPR>(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
-      u32x4_t w;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) w[m] = pack_bf2(y[2 * m] * inv, y[2 * m + 1] * inv);
-      st16(&Ks[(kr0 + C::RPP * j) * C::KLD + kc * 8], w);
     }
-    if (vact) {
-      const int pos0 = vt_pos(4 * vgp);
+    if (C::NMB >= C::NT || v_act) {
+      // rows 4vd..4vd+3 of V^T, 4 consecutive (permuted) key slots each
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // dims 2m (low halves) and 2m+1 (high halves) of the 4 keys
-        const uint32_t a0 = vraw[0][m], a1 = vraw[1][m], a2 = vraw[2][m], a3 = vraw[3][m];
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t a0 = vw[0][m], a1 = vw[1][m], a2 = vw[2][m], a3 = vw[3][m];
         const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
         const u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        st8(&Vt[(vc * 8 + 2 * m) * C::VLD + pos0], lo);
-        st8(&Vt[(vc * 8 + 2 * m + 1) * C::VLD + pos0], hi);
+        st8(vb + v_lds + (2 * m) * C::VLD, lo);
+        st8(vb + v_lds + (2 * m + 1) * C::VLD, hi);
       }
     }
   };
@@ -234,68 +260,119 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(FwdArgs p) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float lsum = 0.f;
 
-  gload(kt0);
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    __syncthreads();  // previous tile's LDS reads are done
-    stage();
-    __syncthreads();
-    if (kt < kt1) gload(kt + 1);  // next tile's global loads overlap this tile's math
+  // Positions covered by this wave (its 32 columns): [tw0, tw1].
+  const int tw0 = q0 + ((wave * 32) >> p.hpw_log2);
+  const int tw1 = min(q0 + ((wave * 32 + 31) >> p.hpw_log2), p.T - 1);
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
-    // S^T - offset = K Q^T - offset  (log2 domain)
-    f32x16_t sacc[C::RB];
+  // Scores of one 32-key block: S^T = K Q^T (MFMA, log2 domain).
+  auto scores = [&](const uint16_t* kb, int rb) {
+    f32x16_t acc;
 #pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[rb][r] = -p.offset;
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(&Ks[(rb * 32 + n) * C::KLD + 16 * s + 8 * hf]);
-        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[rb], 0, 0, 0);
-      }
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc, 0, 0, 0);
     }
-
-    // P = 2^(S - offset) on the band, 0 elsewhere
-    const int j0 = kt * C::BN;
-    const bool full = (j0 + C::BN - 1 <= q0) && (q_last - j0 < p.W);
-    bf16x8_t pb[C::PS];
+    return acc;
+  };
+  // Softmax numerators 2^S packed as the two bf16 P operands of the block,
+  // their sum accumulated with bf16 pair dot products (the same rounded
+  // values the P.V product uses), then O^T += V^T P^T.
+  auto accumulate = [&](const uint16_t* vb, int rb, const f32x16_t& sc) {
+    bf16x8_t pb[2];
 #pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      float e[16];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4_t w;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(sacc[rb][r]);
-        if (!full) {
-          const int key = j0 + rb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int dl = t - key;
-          x = (dl >= 0 && dl < p.W) ? x : 0.f;
-        }
-        e[r] = x;
-        lsum += x;
+      for (int m = 0; m < 4; ++m) {
+        w[m] = pack_bf2(fast_exp2(sc[8 * s2 + 2 * m]), fast_exp2(sc[8 * s2 + 2 * m + 1]));
+        lsum = dot2bf(w[m], kOnes, lsum);
       }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4_t w;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(e[8 * s2 + 2 * m], e[8 * s2 + 2 * m + 1]);
-        pb[2 * rb + s2] = __builtin_bit_cast(bf16x8_t, w);
-      }
+      pb[s2] = __builtin_bit_cast(bf16x8_t, w);
     }
-
-    // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
-      for (int ks = 0; ks < C::PS; ++ks) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(&Vt[(db * 32 + n) * C::VLD + 16 * ks + 8 * hf]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            vb + (db * 32 + n) * C::VLD + 16 * (2 * rb + s2) + 8 * hf);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], oacc[db], 0, 0, 0);
       }
     }
+  };
+
+  // Tile entirely inside the band for every column of the workgroup.
+  auto compute_full = [&](int buf) {
+    const uint16_t* kb = Ks + buf * C::KBUF;
+    const uint16_t* vb = Vt + buf * C::VBUF;
+    f32x16_t sc[C::RB];
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) sc[rb] = scores(kb, rb);
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) accumulate(vb, rb, sc[rb]);
+  };
+
+  // Tile crossing the band edge: per wave and 32-key block, skip blocks the
+  // wave cannot see at all, mask blocks it sees in part.
+  auto compute_edge = [&](int buf, int kt) {
+    const uint16_t* kb = Ks + buf * C::KBUF;
+    const uint16_t* vb = Vt + buf * C::VBUF;
+    // key of register r in block rb is kt*BN + rb*32 + 8*(r/4) + 4*hf + r%4
+    const int dl0 = t - kt * C::BN - 4 * hf;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      const int kb0 = kt * C::BN + rb * 32;
+      const bool none = kb0 > tw1 || tw0 - (kb0 + 31) >= p.W;
+      if (none) continue;
+      f32x16_t sc = scores(kb, rb);
+      const bool all = kb0 + 31 <= tw0 && tw1 - kb0 < p.W;
+      if (!all) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dl = dl0 - (rb * 32 + 8 * (r >> 2) + (r & 3));
+          sc[r] = ((unsigned)dl < (unsigned)p.W) ? sc[r] : -INFINITY;  // 2^-inf = 0
+        }
+      }
+      accumulate(vb, rb, sc);
+    }
+  };
+
+  // ---- double-buffered main loop: tile kt is computed from one LDS buffer
+  // ---- while tile kt+1 is rotated/normalised into the other and tile kt+2
+  // ---- is in flight from memory; one barrier per tile. Staging runs
+  // ---- unconditionally (past kt1 it reads zeros). The band splits into
+  // ---- leading window-edge tiles, full tiles and trailing diagonal tiles;
+  // ---- each range runs its own loop so every loop body is straight-line.
+  gload(kt0);
+  stage(0);
+  gload(kt0 + 1);
+  __syncthreads();
+  auto run = [&](int ka, int kb_, bool edge) {
+    for (int kt = ka; kt <= kb_; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      if (edge) compute_edge(cur, kt); else compute_full(cur);
+      stage(cur ^ 1);
+      gload(kt + 2);
+      __syncthreads();
+    }
+  };
+  // full tiles: j0 + BN - 1 <= q0 (every key at or before every query) and
+  // q_last - j0 < W (every key inside every query's window)
+  const int ktA = max(kt0, (q_last - p.W + 1 + C::BN - 1 >= 0) ? (q_last - p.W + C::BN) / C::BN : 0);
+  const int ktB = min(kt1, (q0 + 1) / C::BN - 1);
+  if (ktA <= ktB) {
+    run(kt0, ktA - 1, true);
+    run(ktA, ktB, false);
+    run(ktB + 1, kt1, true);
+  } else {
+    run(kt0, kt1, true);
   }
 
   // ---- epilogue: normalise by the row sum and store bf16 (B, T, H, D)
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = sum_halves(lsum);
   const float inv_l = 1.0f / lsum;
   if (tvalid) {
     uint16_t* orow = og + (((size_t)b * p.T + t) * p.H + h) * D;
@@ -341,7 +418,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   float qv[D];
   {
     const float* qrow = qg + (((size_t)b * p.T + tc) * p.H + h) * D;
-    const float2* trow = p.tab + (size_t)tc * (D / 2);
+    const float2* trow = p.tabq + (size_t)tc * (D / 2);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
@@ -374,7 +451,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
       float ss = 0.f;
       if (key < p.T) {
         const float* krow = kg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
-        const float2* trow = p.tab + (size_t)key * (D / 2) + part * (D / 8);
+        const float2* trow = p.tabq + (size_t)key * (D / 2) + part * (D / 8);
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
           const float2 cs = trow[i];
@@ -409,7 +486,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s += qv[d] * Kf[jj][d];
-      const float e = exp2f(s - p.offset);
+      const float e = exp2f(s);
       lsum += e;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] += e * Vf[jj][d];
@@ -435,7 +512,6 @@ static int ilog2(int x) {
 template <int D>
 static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
   a.qscale = kLog2e / sqrtf((float)D);
-  a.offset = sqrtf((float)D) * kLog2e;
   if (dt == kBF16) {
     // heads per workgroup: largest power of two dividing G, at most 32
     int hpw = 1;
@@ -446,7 +522,8 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
     a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
     const long long grid = (long long)a.nqt * a.B * a.ngroups;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(BfCfg<D>::NT), 0, stream,
+                       a);
   } else {
     a.hpw_log2 = 0;
     a.ngroups = a.H;
@@ -467,7 +544,8 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
   a.k = k;
   a.v = v;
   a.o = o;
-  a.tab = (const float2*)tab;
+  a.tabq = (const float2*)tab;
+  a.tabk = (const uint2*)((const char*)tab + rope_table_half_bytes(T, D));
   a.B = B;
   a.T = T;
   a.H = H;

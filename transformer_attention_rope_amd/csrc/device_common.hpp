@@ -49,6 +49,53 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// DPP lane moves within a row of 16 lanes (row_mask/bank_mask all lanes).
+template <int ctrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
+                                                               0xF, 0xF, false));
+}
+
+// Sum over groups of `width` consecutive lanes, width in {1, 2, 4, 8, 16},
+// with DPP moves only: quad_perm swaps within quads, then half-row and row
+// mirrors, which pair every lane with one of the other half once the halves
+// below it hold uniform sums.
+template <int width>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+  static_assert(width == 1 || width == 2 || width == 4 || width == 8 || width == 16, "width");
+  if constexpr (width >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (width >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (width >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (width >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  return x;
+}
+
+// x[lane] + x[lane ^ 32].
+__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// dot of two bf16 pairs plus an fp32 addend (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Raw buffer loads: offsets are bytes from the resource base; a load whose
+// VGPR offset is at or beyond num_records reads zero (used for ragged tails
+// instead of branches). The SGPR offset is not part of that range check, so
+// callers move tile offsets into the resource base, never into soffset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
 

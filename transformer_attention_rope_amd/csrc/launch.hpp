@@ -10,8 +10,9 @@ namespace nc {
 
 enum Dtype { kBF16 = 0, kF32 = 1 };
 
-// ---- RoPE cos/sin table: tab[t][i] = (cos, sin)((pos_offset + t) * theta_i),
-// ---- computed in fp64 and stored as fp32 pairs.
+// ---- RoPE cos/sin tables for positions pos_offset + t: fp32 (cos, sin) pairs
+// ---- followed by bf16 {(cos,-sin), (sin,cos)} pairs, each [T][D/2].
+size_t rope_table_half_bytes(int T, int D);
 size_t rope_table_bytes(int T, int D);
 hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
                              hipStream_t stream);

@@ -11,31 +11,49 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <cmath>
+
 namespace nc {
 
 // ---------------------------------------------------------------- table
-// tab[t * D/2 + i] = (cos, sin)((pos_offset + t) * base^(-2i/D)), fp32.
-__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tab, int T,
-                                                          int half, double inv_d2,
-                                                          double rope_base, int pos_offset) {
+// Two tables over positions p = pos_offset + t, t < T, pairs i < D/2:
+//   tabq[t][i] = (cos, sin)(p * theta_i) in fp32 (for q rows, read once), and
+//   tabk[t][i] = bf16 pairs {(cos, -sin), (sin, cos)} (for k rows, read on every
+//                key-tile visit: each rotated output is one bf16 pair dot product).
+// theta_i = base^(-2i/D); the angle p*theta_i is formed in fp64 and reduced
+// modulo 2*pi with a two-constant Cody-Waite step in fp64, so cos/sin come
+// from an fp32 evaluation on [-pi, pi] whatever the position.
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tabq,
+                                                          uint2* __restrict__ tabk, int T,
+                                                          int half, double log2_base,
+                                                          int pos_offset) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= T * half) return;
   const int t = idx / half, i = idx - t * half;
-  const double theta = pow(rope_base, -(double)i * inv_d2);
-  double s, c;
-  sincos((double)(pos_offset + t) * theta, &s, &c);
-  tab[idx] = make_float2((float)c, (float)s);
+  const double theta = exp2(-(double)i / (double)half * log2_base);
+  const double a = (double)(pos_offset + t) * theta;
+  const double kq = rint(a * 0.15915494309189535);        // a / (2 pi)
+  double r = fma(-kq, 6.283185307179586, a);              // 2 pi, high part
+  r = fma(-kq, 2.4492935982947064e-16, r);                // 2 pi, low part
+  float sn, cs;
+  sincosf((float)r, &sn, &cs);
+  tabq[idx] = make_float2(cs, sn);
+  tabk[idx] = make_uint2(pack_bf2(cs, -sn), pack_bf2(sn, cs));
 }
 
-size_t rope_table_bytes(int T, int D) { return (size_t)T * (size_t)(D / 2) * sizeof(float2); }
+size_t rope_table_half_bytes(int T, int D) {
+  return (size_t)T * (size_t)(D / 2) * sizeof(float2);
+}
+size_t rope_table_bytes(int T, int D) { return 2 * rope_table_half_bytes(T, D); }
 
 hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
                              hipStream_t stream) {
   const int half = D / 2;
   const long long n = (long long)T * half;
   const int grid = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, stream, (float2*)tab, T, half,
-                     2.0 / D, rope_base, pos_offset);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, stream, (float2*)tab,
+                     (uint2*)((char*)tab + rope_table_half_bytes(T, D)), T, half,
+                     std::log2(rope_base), pos_offset);
   return hipGetLastError();
 }
 
