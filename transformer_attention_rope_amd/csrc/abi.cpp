@@ -1,7 +1,7 @@
 // C ABI of the attention-block library: host-side validation, workspace
 // sizing and kernel dispatch. Every check runs before the first HIP call, so
 // argument errors are reported without touching the device.
-#include "../../include/nc_attn.h"
+#include "nc_attn.h"
 
 #include <hip/hip_runtime.h>
 

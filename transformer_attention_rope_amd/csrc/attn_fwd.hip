@@ -91,6 +91,41 @@ __device__ __forceinline__ int vt_pos(int kk) {
   return (blk16 << 4) | (((w >> 2) & 1) << 3) | ((w >> 3) << 2) | (w & 3);
 }
 
+// Instruction order of a full tile for D = 128 and D = 64. Step m issues
+// one MFMA -- the score MFMAs S0[0..KS), S1[0..KS) of the two 32-key blocks,
+// then the P.V MFMAs of block 0 and of block 1 -- followed by up to two
+// slices of vector work that do not depend on it:
+//   0..4*NKP-1   RoPE + RMSNorm of the next tile's K chunk id/4, part id%4
+//   100, 101     transposition of the next tile's V micro-block, half 0/1
+//   200+8*rb+i   2^S of score registers 2i, 2i+1 of block rb, packed into
+//                the P operand, and their contribution to the row sum
+// A block's exponentials start two MFMAs after its last score MFMA, and
+// each P.V MFMA comes after the four slices that produce its P operand.
+template <int D>
+struct FullSched;
+template <>
+struct FullSched<128> {
+  static constexpr int NM = 32;
+  static constexpr short v[NM][2] = {
+      {0, -1},   {1, -1},   {2, -1},   {3, -1},   {4, -1},   {5, -1},   {6, -1},   {7, -1},
+      {100, -1}, {101, -1}, {200, -1}, {201, -1}, {202, -1}, {203, -1}, {204, -1}, {205, -1},
+      {206, -1}, {207, -1}, {208, -1}, {209, -1}, {210, -1}, {211, -1}, {212, -1}, {213, -1},
+      {214, -1}, {215, -1}, {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1}};
+};
+template <>
+struct FullSched<32> {  // not used: D = 32 tiles run the generic order
+  static constexpr int NM = 8;
+  static constexpr short v[NM][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1},
+                                     {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
+};
+template <>
+struct FullSched<64> {
+  static constexpr int NM = 16;
+  static constexpr short v[NM][2] = {
+      {0, -1},    {1, -1},    {2, -1},    {3, -1},    {100, -1},  {101, -1}, {200, 201}, {202, 203},
+      {204, 205}, {206, 207}, {208, 209}, {210, 211}, {212, 213}, {214, 215}, {-1, -1},  {-1, -1}};
+};
+
 template <int D>
 __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   using C = BfCfg<D>;
@@ -340,6 +375,113 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     }
   };
 
+  // Full tile in a fixed instruction order (FullSched): compute tile `buf`
+  // while the next tile's K and V, already in registers, are rotated,
+  // normalised and transposed between the MFMAs, then written to the other
+  // buffer. LDS fragments are read three MFMAs ahead.
+  auto tile_full_sched = [&](int buf) {
+    using SCH = FullSched<D>;
+    constexpr int NS = C::KS, NP = 2 * C::DB, NM = 2 * NS + 2 * NP, LA = 8;
+    static_assert(SCH::NM == NM, "schedule length");
+    const uint16_t* kb = Ks + buf * C::KBUF;
+    const uint16_t* vb = Vt + buf * C::VBUF;
+    f32x16_t sacc[2];
+    u32x4_t pbu[2][2];
+    float kss[C::NKP], kinv[C::NKP];
+    u32x4_t kout[C::NKP];
+    u32x2_t vlo[2], vhi[2];
+    bf16x8_t fr[LA + 1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[0][r] = 0.f;
+      sacc[1][r] = 0.f;
+    }
+    auto frag = [&](int m) -> bf16x8_t {
+      if (m < 2 * NS) {
+        const int rb = m / NS, s = m % NS;
+        return *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
+      }
+      const int idx = m - 2 * NS, rb = idx / NP, i = idx % NP;
+      const int db = i % C::DB, s2 = i / C::DB;
+      return *reinterpret_cast<const bf16x8_t*>(vb + (db * 32 + n) * C::VLD + 16 * (2 * rb + s2) +
+                                                8 * hf);
+    };
+    auto slice = [&](int id) {
+      if (id < 0) return;
+      if (id < 100) {
+        const int j = id >> 2, part = id & 3;
+        if (part == 0) {
+          float ss = dot2bf(kw[j][0], kw[j][0], 0.f);
+          ss = dot2bf(kw[j][1], kw[j][1], ss);
+          ss = dot2bf(kw[j][2], kw[j][2], ss);
+          kss[j] = dot2bf(kw[j][3], kw[j][3], ss);  // a rotation keeps the sum of squares
+          pin(kss[j]);
+        } else if (part == 1) {
+          kinv[j] = rsq(dpp_group_sum<C::CPR>(kss[j]) * (1.0f / D) + kEps);
+          pin(kinv[j]);
+        } else {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const int m = 2 * (part - 2) + mm;
+            const u32x4_t& tt = kt_[j][m >> 1];
+            const float xe = dot2bf(kw[j][m], tt[2 * (m & 1)], 0.f);
+            const float xo = dot2bf(kw[j][m], tt[2 * (m & 1) + 1], 0.f);
+            uint32_t w = pack_bf2(xe * kinv[j], xo * kinv[j]);
+            pin(w);
+            kout[j][m] = w;
+          }
+        }
+      } else if (id < 200) {
+        const int m = id - 100;
+        const uint32_t a0 = vw[0][m], a1 = vw[1][m], a2 = vw[2][m], a3 = vw[3][m];
+        uint32_t l0 = (a0 & 0xffffu) | (a1 << 16), l1 = (a2 & 0xffffu) | (a3 << 16);
+        uint32_t h0 = (a0 >> 16) | (a1 & 0xffff0000u), h1 = (a2 >> 16) | (a3 & 0xffff0000u);
+        pin(l0);
+        pin(l1);
+        pin(h0);
+        pin(h1);
+        vlo[m] = u32x2_t{l0, l1};
+        vhi[m] = u32x2_t{h0, h1};
+      } else {
+        const int rb = (id - 200) >> 3, i = (id - 200) & 7;
+        const uint32_t w = pack_bf2(fast_exp2(sacc[rb][2 * i]), fast_exp2(sacc[rb][2 * i + 1]));
+        lsum = dot2bf(w, kOnes, lsum);
+        pbu[rb][i >> 2][i & 3] = w;
+      }
+    };
+#pragma unroll
+    for (int m = 0; m < LA; ++m) fr[m] = frag(m);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m + LA < NM) fr[(m + LA) % (LA + 1)] = frag(m + LA);
+      const bf16x8_t a = fr[m % (LA + 1)];
+      if (m < 2 * NS) {
+        const int rb = m / NS, s = m % NS;
+        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[rb], 0, 0, 0);
+      } else {
+        const int idx = m - 2 * NS, rb = idx / NP, i = idx % NP;
+        const int db = i % C::DB, s2 = i / C::DB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, pbu[rb][s2]), oacc[db], 0, 0, 0);
+      }
+      slice(SCH::v[m][0]);
+      slice(SCH::v[m][1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next tile's K' and V^T into the other buffer
+    uint16_t* kbw = Ks + (buf ^ 1) * C::KBUF;
+    uint16_t* vbw = Vt + (buf ^ 1) * C::VBUF;
+#pragma unroll
+    for (int j = 0; j < C::NKP; ++j) st16(kbw + k_lds[j], kout[j]);
+    if (C::NMB >= C::NT || v_act) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        st8(vbw + v_lds + (2 * m) * C::VLD, vlo[m]);
+        st8(vbw + v_lds + (2 * m + 1) * C::VLD, vhi[m]);
+      }
+    }
+  };
+
   // ---- double-buffered main loop: tile kt is computed from one LDS buffer
   // ---- while tile kt+1 is rotated/normalised into the other and tile kt+2
   // ---- is in flight from memory; one barrier per tile. Staging runs
@@ -353,8 +495,17 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   auto run = [&](int ka, int kb_, bool edge) {
     for (int kt = ka; kt <= kb_; ++kt) {
       const int cur = (kt - kt0) & 1;
-      if (edge) compute_edge(cur, kt); else compute_full(cur);
-      stage(cur ^ 1);
+      if constexpr (D >= 64) {
+        if (edge) {
+          compute_edge(cur, kt);
+          stage(cur ^ 1);
+        } else {
+          tile_full_sched(cur);
+        }
+      } else {
+        if (edge) compute_edge(cur, kt); else compute_full(cur);
+        stage(cur ^ 1);
+      }
       gload(kt + 2);
       __syncthreads();
     }

@@ -75,6 +75,12 @@ __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 
 
 __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Materialise a value in a VGPR at this point of the program (an empty asm
+// statement that reads and writes it), so that its computation cannot be
+// sunk towards a later use and stays where it was placed in the schedule.
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // dot of two bf16 pairs plus an fp32 addend (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
