@@ -201,9 +201,7 @@ def main():
             q, kn, vn, kc, vc, L = wl.decode_inputs(dcfg, set_idx=s)
             dsets.append([t.to(dev) for t in (q, kn, vn, kc, vc, L)] + [torch.empty_like(q, device=dev)])
         for Wd in dcfg.windows:
-            wsd = torch.empty(max(nc.attn_decode_workspace_bytes(dcfg.B, dcfg.Tmax, dcfg.H, dcfg.Hkv,
-                                                                 dcfg.D, Wd), 1),
-                              dtype=torch.uint8, device=dev)
+            wsd = nc.decode_workspace(dcfg.B, dcfg.Tmax, dcfg.H, dcfg.Hkv, dcfg.D, Wd, device=dev)
 
             def dstep(i, Wd=Wd, wsd=wsd):
                 q, kn, vn, kc, vc, L, o = dsets[i % len(dsets)]

@@ -161,6 +161,9 @@ nc_status nc_attn_fwd_tab(const void* q, const void* k, const void* v, void* o,
  *   o        (B, H, D)          softmax over keys max(0, L-window) .. L-1
  * seqlens values outside [1, Tmax] are a precondition violation: the kernels
  * clamp them to that range instead of reading out of bounds.
+ * Workspace: the key range of a sequence is split into chunks processed in
+ * parallel; ws holds each chunk's softmax state until a second kernel merges
+ * them. Calls that overlap in time must not share a workspace.
  * Requires H % Hkv == 0, H / Hkv <= 64, window >= 1, Tmax >= 1, D in
  * {32, 64, 128}; q, k_new, v_new and o must not overlap the caches.
  */

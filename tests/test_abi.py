@@ -121,8 +121,11 @@ def test_workspace_queries():
     assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0) == 2048 * 64 * 16
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0) == 768  # 3*16*16 = 768
     assert L.nc_rope_table_bytes(3, 32) == 768
-    n = L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048)
+    # few (sequence, head) pairs: the key range is split and needs chunk states
+    n = L.nc_attn_decode_workspace_bytes(2, 2048, 6, 6, 128, 2048)
     assert n > 0 and n % 256 == 0
+    # one workgroup per (sequence, head) already fills the device: no split
+    assert L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048) == 0
     assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0
 
 

@@ -285,3 +285,24 @@ def test_decode_matches_prefill_gpu():
             torch.cuda.synchronize()
             mx, mn = _err(o, o_pre[:, Lv - 1].double().cpu().numpy())
             assert mx <= BF_MAX and mn <= BF_MEAN, f"W={W} L={Lv}: {mx} {mn}"
+
+
+def test_decode_workspace_reused_across_calls():
+    """One workspace serves consecutive calls with different lengths and shapes."""
+    _say("decode workspace reuse")
+    ws = nc.decode_workspace(8, 2048, 8, 2, 128, 2048, device=DEV)
+    g = torch.Generator().manual_seed(99)
+    for it, (B, Tmax, H, Hkv, W) in enumerate([(8, 2048, 8, 2, 2048), (8, 2048, 8, 2, 2048),
+                                               (4, 1500, 4, 2, 700), (8, 2048, 8, 2, 300)]):
+        q = torch.randn(B, H, 128, generator=g).bfloat16()
+        kn = torch.randn(B, Hkv, 128, generator=g).bfloat16()
+        vn = torch.randn(B, Hkv, 128, generator=g).bfloat16()
+        kc = torch.randn(B, Tmax, Hkv, 128, generator=g).bfloat16()
+        vc = torch.randn(B, Tmax, Hkv, 128, generator=g).bfloat16()
+        L = torch.randint(1, Tmax + 1, (B,), generator=g, dtype=torch.int32)
+        o = nc.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), kc.to(DEV), vc.to(DEV), L.to(DEV),
+                           window=W, workspace=ws)
+        torch.cuda.synchronize()
+        ro, _, _ = oracle.attn_decode(q, kn, vn, kc, vc, L, W)
+        _check(o, ro, torch.bfloat16, f"decode reuse call {it}")
+    assert nc.attn_decode_workspace_bytes(8, 2048, 8, 2, 128, 2048) > 0

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_decode",
-    "rope_table", "attn_fwd_tab",
+    "rope_table", "attn_fwd_tab", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes", "rope_qknorm_workspace_bytes",
     "NC_OK", "NC_ERR_INVALID", "NC_ERR_UNSUPPORTED", "NC_ERR_HIP", "NC_BF16", "NC_F32",
 ]
@@ -140,6 +140,12 @@ def _workspace(nbytes: int, device, workspace):
             raise ValueError(f"workspace holds fewer than the {nbytes} bytes required")
         return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_workspace(B, Tmax, H, Hkv, D, window, device="cuda"):
+    """A decode workspace for these sizes, reusable by later calls on one stream."""
+    n = attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def rope_qknorm(q, k, *, rope_base: float = 10000.0, pos_offset: int = 0, q_out=None, k_out=None):

@@ -12,17 +12,20 @@
 //   q' = RMSNorm(RoPE(q[b, h], p)).
 //
 // Design: decode reads every visible K/V row once, so it is bound by HBM.
-// Workgroups own (sequence b, K/V head g, up to GP query heads of g, a chunk
-// of C consecutive keys). Each group of CPR lanes streams one 16-byte chunk
-// of a K row and of a V row per key, so a wave reads whole 256-byte rows with
-// unit-stride loads; scores use a cross-lane sum over the CPR lanes. The
-// softmax is the running-maximum form (cache rows are caller data, so no
-// bound on the scores is assumed). Partial (max, sum, unnormalised output)
-// triples are merged across lanes with shuffles, across waves in LDS, and
-// across chunks by a second small kernel. The chunk holding key L-1 writes
-// the appended row and uses it from registers, so no workgroup waits on
-// another's write. A sequence whose visible range fits one chunk writes its
-// final output directly.
+// A workgroup owns (sequence b, K/V head g, up to GP query heads of g, a chunk
+// of C consecutive keys). CPR lanes stream one 16-byte piece of a K row and of
+// a V row per key, so a wave reads whole rows with unit-stride loads; each
+// lane group keeps U keys in flight per iteration and rescales its running
+// softmax state once per U keys (the scores of cache rows are not assumed
+// bounded, so this path keeps a running maximum). Partial (max, sum,
+// unnormalised output) states are merged across lanes with DPP/shuffles and
+// across waves in LDS. A sequence whose visible range fits one chunk writes
+// its output directly; otherwise each chunk stores its state in the
+// workspace and a second small kernel merges the states (the kernel boundary
+// makes every chunk's state visible across the chip's L2 caches at once,
+// which a per-workgroup device-scope release would pay for many times). The
+// chunk holding key L-1 writes the appended row and uses it from LDS, so no
+// workgroup waits on another's write.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -36,9 +39,9 @@ struct DecArgs {
   void* v_cache;
   const int32_t* seqlens;
   void* o;
-  float* part;  // [B][H][nsplit][D + 2]: o-partial (D), max, sum
+  float* part;  // [B][H][nsplit][D + 2]: unnormalised o (D), max, sum
   int B, Tmax, H, Hkv, G, W;
-  int C;        // keys per chunk
+  int C;        // keys per chunk (multiple of the keys per workgroup step)
   int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
   int ngh;      // head groups per K/V head = ceil(G / GP)
   double rope_base;
@@ -56,12 +59,6 @@ struct ElemTraits<uint16_t> {
       x[2 * m + 1] = bf_hi(w[m]);
     }
   }
-  __device__ static u32x4_t pack(const float* x) {
-    u32x4_t w;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m], x[2 * m + 1]);
-    return w;
-  }
   __device__ static float to_f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
   __device__ static uint16_t from_f(float x) { return (uint16_t)(pack_bf2(x, 0.f) & 0xffffu); }
 };
@@ -72,19 +69,28 @@ struct ElemTraits<float> {
 #pragma unroll
     for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
   }
-  __device__ static u32x4_t pack(const float* x) {
-    return u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                   __float_as_uint(x[3])};
-  }
   __device__ static float to_f(float x) { return x; }
   __device__ static float from_f(float x) { return x; }
 };
 
 __device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
 
-__device__ __forceinline__ int num_chunks(int L, int W, int C) {
-  const int lo = L > W ? L - W : 0;
-  return (L - lo + C - 1) / C;
+// Sum over groups of `width` consecutive lanes, width a power of two <= 64.
+template <int width>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  if constexpr (width <= 16) {
+    return dpp_group_sum<width>(x);
+  } else {
+    x = dpp_group_sum<16>(x);
+#pragma unroll
+    for (int off = 16; off < width; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+  }
+}
+
+// Merge softmax states (m, l, acc) of two disjoint key sets.
+__device__ __forceinline__ float merge_scale(float m, float mn) {
+  return m == -INFINITY ? 0.f : fast_exp2(m - mn);
 }
 
 template <int D, int GP, typename Elem>
@@ -93,8 +99,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   constexpr int EPC = TR::EPC;
   constexpr int CPR = D / EPC;        // lanes per key row
   constexpr int KPW = 64 / CPR;       // keys per wave per step
-  constexpr int KPS = 4 * KPW;        // keys per workgroup per step
-  constexpr int U = 2;                // steps in flight per iteration
+  constexpr int U = 4;                // keys in flight per lane group
+  constexpr int KPI = 4 * KPW * U;    // keys per workgroup iteration
 
   __shared__ float qs[GP][D];         // q' * log2(e)/sqrt(D)
   __shared__ float knew_s[D];         // appended key (rounded to the cache type)
@@ -103,7 +109,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   __shared__ float red_m[4][GP], red_l[4][GP];
   __shared__ float red_o[4][GP][D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = (int)blockIdx.x % a.nsplit;
   const int rest = (int)blockIdx.x / a.nsplit;
   const int hg = rest % a.ngh;
@@ -126,12 +133,41 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   Elem* kc = (Elem*)a.k_cache;
   Elem* vc = (Elem*)a.v_cache;
 
-  // ---- cos/sin at position pos (angles in fp64)
+  // ---- the chunk's K/V rows as buffer loads relative to key ks0; rows past
+  // ---- ks1 (the chunk end) read as zero and are masked out of the softmax.
+  // ---- The first iteration's loads are issued before the RoPE prologue so
+  // ---- that their latency overlaps it; later iterations are double-buffered.
+  const int cc = lane % CPR;        // 16-byte piece within the row
+  const int kl = lane / CPR;        // key slot within the wave
+  const uint32_t row_bytes = (uint32_t)a.Hkv * D * sizeof(Elem);
+  const size_t base_el = (((size_t)b * a.Tmax + ks0) * a.Hkv + g) * D;
+  const uint32_t nrec = (uint32_t)(ks1 - ks0) * row_bytes;  // the chunk's keys only
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + base_el, nrec);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base_el, nrec);
+  const int slot = wave * KPW + kl;   // key slot within a workgroup step
+  const int nkeys = ks1 - ks0;
+  u32x4_t kw[2][U], vw[2][U];
+  auto issue = [&](int it, int set) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)(it * KPI + u * 4 * KPW + slot) * row_bytes + cc * 16;
+      kw[set][u] = bload16(rk, off, 0);
+      vw[set][u] = bload16(rv, off, 0);
+    }
+  };
+  issue(0, 0);
+
+  // ---- cos/sin at position pos: the angle is formed and reduced modulo
+  // ---- 2*pi in fp64, then evaluated in fp32 on [-pi, pi]
   if (tid < D / 2) {
-    const double theta = pow(a.rope_base, -2.0 * (double)tid / D);
-    double s, c;
-    sincos((double)pos * theta, &s, &c);
-    cs[tid] = make_float2((float)c, (float)s);
+    const double theta = exp2(-(double)tid / (D / 2) * log2(a.rope_base));
+    const double ang = (double)pos * theta;
+    const double kq = rint(ang * 0.15915494309189535);
+    double r = fma(-kq, 6.283185307179586, ang);
+    r = fma(-kq, 2.4492935982947064e-16, r);
+    float sn, c;
+    sincosf((float)r, &sn, &c);
+    cs[tid] = make_float2(c, sn);
   }
   __syncthreads();
 
@@ -176,9 +212,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   __syncthreads();
 
-  // ---- stream the chunk's keys
-  const int cc = lane % CPR;        // chunk within the row
-  const int kl = lane / CPR;        // key slot within the wave
   float qv[GP][EPC];
 #pragma unroll
   for (int i = 0; i < GP; ++i)
@@ -194,58 +227,65 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     for (int e = 0; e < EPC; ++e) acc[i][e] = 0.f;
   }
 
-  const size_t row = (size_t)a.Hkv * D;
-  const Elem* kb = kc + ((size_t)b * a.Tmax * a.Hkv + g) * D + cc * EPC;
-  const Elem* vb = vc + ((size_t)b * a.Tmax * a.Hkv + g) * D + cc * EPC;
-
-  for (int base = ks0; base < ks1; base += KPS * U) {
-    u32x4_t kw[U], vw[U];
-    int keys[U];
+  auto consume = [&](int it, int set) {
+    float kx[U][EPC], vx[U][EPC];
+    bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = base + u * KPS + wave * KPW + kl;
-      keys[u] = key;
-      // the appended row is taken from LDS, never re-read from memory
-      if (key < ks1 && key != pos) {
-        kw[u] = ld16(kb + (size_t)key * row);
-        vw[u] = ld16(vb + (size_t)key * row);
-      } else {
-        kw[u] = u32x4_t{0, 0, 0, 0};
-        vw[u] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = keys[u];
-      float kx[EPC], vx[EPC];
-      if (key == pos) {
+      const int key = ks0 + it * KPI + u * 4 * KPW + slot;
+      live[u] = key < ks1;
+      if (key == pos) {  // the appended row, from LDS (its cache row may not be written yet)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          kx[e] = knew_s[cc * EPC + e];
-          vx[e] = vnew_s[cc * EPC + e];
+          kx[u][e] = knew_s[cc * EPC + e];
+          vx[u][e] = vnew_s[cc * EPC + e];
         }
       } else {
-        TR::unpack(kw[u], kx);
-        TR::unpack(vw[u], vx);
-      }
-      const bool live = key < ks1;
-#pragma unroll
-      for (int i = 0; i < GP; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s += qv[i][e] * kx[e];
-        s = group_sum<CPR>(s);
-        if (live && i < nh) {
-          const float mn = fmaxf(m[i], s);
-          const float alpha = fast_exp2(m[i] - mn);  // m = -inf -> 0
-          const float pe = fast_exp2(s - mn);
-          l[i] = l[i] * alpha + pe;
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[i][e] = acc[i][e] * alpha + pe * vx[e];
-          m[i] = mn;
-        }
+        TR::unpack(kw[set][u], kx[u]);
+        TR::unpack(vw[set][u], vx[u]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      if (i >= nh) break;
+      float sc[U];
+      float mx = m[i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s += qv[i][e] * kx[u][e];
+        s = lane_group_sum<CPR>(s);
+        sc[u] = live[u] ? s : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      if (mx == -INFINITY) continue;  // no live key for this lane group yet
+      const float alpha = merge_scale(m[i], mx);
+      float ps = 0.f, pe[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pe[u] = fast_exp2(sc[u] - mx);  // 2^-inf = 0 for dead slots
+        ps += pe[u];
+      }
+      l[i] = l[i] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        float t = acc[i][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) t += pe[u] * vx[u][e];
+        acc[i][e] = t;
+      }
+      m[i] = mx;
+    }
+  };
+
+  const int niter = (nkeys + KPI - 1) / KPI;
+  for (int it = 0; it < niter; it += 2) {
+    if (it + 1 < niter) issue(it + 1, 1);
+    consume(it, 0);
+    if (it + 1 >= niter) break;
+    if (it + 2 < niter) issue(it + 2, 0);
+    consume(it + 1, 1);
   }
 
   // ---- merge the key slots of a wave (lanes kl differ by multiples of CPR)
@@ -256,8 +296,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
       const float mo = __shfl_xor(m[i], off, 64);
       const float lo_ = __shfl_xor(l[i], off, 64);
       const float mn = fmaxf(m[i], mo);
-      const float a0 = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
-      const float a1 = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
+      const float a0 = merge_scale(m[i], mn), a1 = merge_scale(mo, mn);
       l[i] = l[i] * a0 + lo_ * a1;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
@@ -280,7 +319,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   __syncthreads();
 
-  // ---- merge the 4 waves; write the final output or this chunk's partial
+  // ---- merge the 4 waves; write the output, or this chunk's state
   const bool single = nch == 1;
   for (int idx = tid; idx < nh * D; idx += 256) {
     const int i = idx / D, d = idx - (idx / D) * D;
@@ -290,7 +329,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     float lsum = 0.f, osum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float sc = red_m[w][i] == -INFINITY ? 0.f : fast_exp2(red_m[w][i] - mx);
+      const float sc = merge_scale(red_m[w][i], mx);
       lsum += red_l[w][i] * sc;
       osum += red_o[w][i][d] * sc;
     }
@@ -308,7 +347,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
 }
 
-// One wave per (b, h) with more than one chunk: merge the chunk partials.
+// One wave per (b, h) whose visible range spans more than one chunk: merge
+// the chunk states in one pass (running maximum), lanes over the head dim.
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
   const int wid = ((int)blockIdx.x * 256 + (int)threadIdx.x) >> 6;
@@ -316,25 +356,44 @@ __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
   if (wid >= a.B * a.H) return;
   const int b = wid / a.H, h = wid - (wid / a.H) * a.H;
   const int L = clamp_len(a.seqlens[b], a.Tmax);
-  const int nch = num_chunks(L, a.W, a.C);
+  const int lo = L > a.W ? L - a.W : 0;
+  const int nch = (L - lo + a.C - 1) / a.C;
   if (nch <= 1) return;
-  const float* pp = a.part + ((size_t)b * a.H + h) * a.nsplit * (D + 2);
-  float mx = -INFINITY;
-  for (int s = 0; s < nch; ++s) mx = fmaxf(mx, pp[s * (D + 2) + D]);
-  float lsum = 0.f;
   constexpr int PER = (D + 63) / 64;
-  float o[PER];
+  constexpr int NB = 8;  // chunk states loaded per batch
+  const float* pp = a.part + ((size_t)b * a.H + h) * a.nsplit * (D + 2);
+  float mx = -INFINITY, lsum = 0.f, o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int s = 0; s < nch; ++s) {
-    const float* ps = pp + s * (D + 2);
-    const float sc = fast_exp2(ps[D] - mx);
-    lsum += ps[D + 1] * sc;
+  for (int s0 = 0; s0 < nch; s0 += NB) {
+    float ms[NB], ls[NB], os[NB][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = e * 64 + lane;
-      if (d < D) o[e] += ps[d] * sc;
+    for (int j = 0; j < NB; ++j) {
+      const bool ok = s0 + j < nch;
+      const float* ps = pp + (ok ? s0 + j : 0) * (D + 2);
+      ms[j] = ok ? ps[D] : -INFINITY;
+      ls[j] = ok ? ps[D + 1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = e * 64 + lane;
+        os[j][e] = (ok && d < D) ? ps[d] : 0.f;
+      }
     }
+    float mn = mx;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) mn = fmaxf(mn, ms[j]);
+    const float a0 = merge_scale(mx, mn);
+    lsum *= a0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] *= a0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float aj = merge_scale(ms[j], mn);
+      lsum += ls[j] * aj;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] += os[j][e] * aj;
+    }
+    mx = mn;
   }
   const float inv = 1.0f / lsum;
 #pragma unroll
@@ -347,15 +406,27 @@ __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
 // ---------------------------------------------------------------- host side
 static int decode_gp(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8)); }
 
-static int decode_chunk(int B, int Tmax, int H, int Hkv, int W) {
-  // aim for about 2048 busy workgroups; chunk is a power of two in [64, 1024]
+static int decode_kpi(int D, bool bf16) {
+  const int cpr = D / (bf16 ? 8 : 4);
+  return 4 * (64 / cpr) * 4;  // waves * keys per wave step * keys in flight
+}
+
+static int decode_chunk(int B, int Tmax, int H, int Hkv, int D, int W) {
+  // Each workgroup pays a fixed start-up (RoPE of q, first load latency) and
+  // a split range pays a merge pass, so a visible range is split only when
+  // there are fewer (b, K/V head, head group) workgroups than compute units;
+  // then chunks are sized for about 1024 workgroups, at least two workgroup
+  // iterations each so that the double-buffered loads overlap.
   const int G = H / Hkv;
   const int ngh = (G + decode_gp(G) - 1) / decode_gp(G);
+  const int kpi = decode_kpi(D, true);
   const long long span = (long long)(W < Tmax ? W : Tmax);
-  const long long keys = (long long)B * Hkv * ngh * span / 2;  // average visible keys
-  long long c = 64;
-  while (c < 1024 && keys / c > 2048) c <<= 1;
-  return (int)c;
+  const long long whole = (span + kpi - 1) / kpi * kpi;
+  const long long nbg = (long long)B * Hkv * ngh;
+  if (nbg >= 256) return (int)whole;
+  long long c = 2 * kpi;
+  while (c < whole && nbg * ((span + c - 1) / c) > 1024) c <<= 1;
+  return (int)(c < whole ? c : whole);
 }
 
 static int decode_nsplit(int Tmax, int W, int C) {
@@ -364,7 +435,7 @@ static int decode_nsplit(int Tmax, int W, int C) {
 }
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window) {
-  const int C = decode_chunk(B, Tmax, H, Hkv, window);
+  const int C = decode_chunk(B, Tmax, H, Hkv, D, window);
   const int ns = decode_nsplit(Tmax, window, C);
   if (ns <= 1) return 0;
   return (size_t)B * H * ns * (D + 2) * sizeof(float);
@@ -385,8 +456,8 @@ static hipError_t decode_d(DecArgs a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit <= 1) return e;
   const long long waves = (long long)a.B * a.H;
-  const unsigned cgrid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((attn_decode_combine_kernel<D, Elem>), dim3(cgrid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<D, Elem>), dim3((unsigned)((waves + 3) / 4)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -402,16 +473,16 @@ hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_ne
   a.v_cache = v_cache;
   a.seqlens = seqlens;
   a.o = o;
-  a.part = (float*)ws;
   a.B = B;
   a.Tmax = Tmax;
   a.H = H;
   a.Hkv = Hkv;
   a.G = H / Hkv;
   a.W = window;
-  a.C = decode_chunk(B, Tmax, H, Hkv, window);
+  a.C = decode_chunk(B, Tmax, H, Hkv, D, window);
   a.nsplit = decode_nsplit(Tmax, window, a.C);
   a.rope_base = rope_base;
+  a.part = (float*)ws;
   const bool bf = dt == kBF16;
   switch (D) {
     case 32: return bf ? decode_d<32, uint16_t>(a, stream) : decode_d<32, float>(a, stream);
