@@ -4,19 +4,20 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 
 A step is one ``nc_attn_fwd`` call (RoPE + QK-norm + banded attention, the
-prefill path end to end, including its RoPE table build) over the d12 L-layer
-batch: B=8, T=2048, H=Hkv=6, D=128, full causal window, bf16, inputs resident
-in HBM. Four independent input sets are rotated so repeated steps do not run
-out of the 256 MB last-level cache. ``value`` is attention-forward TFLOP/s
-counting 4*D flops per unmasked (query, key) pair.
+prefill path end to end: the k'/table input stage and the attention kernel)
+over the d12 L-layer batch: B=8, T=2048, H=Hkv=6, D=128, full causal window,
+bf16, inputs resident in HBM. Four independent input sets are rotated so
+repeated steps do not run out of the 256 MB last-level cache. ``value`` is
+attention-forward TFLOP/s counting 4*D flops per unmasked (query, key) pair.
 
 The same run also times, with HIP events on the launch stream:
-  * the attention kernel alone (``nc_attn_fwd_tab`` with a prebuilt table),
-    the basis of ``roofline`` (against the 2516.6 TFLOP/s bf16 dense peak);
+  * the attention kernel alone (``nc_attn_core`` on workspaces filled by
+    ``nc_attn_prep``), the basis of ``roofline`` (against the 2516.6 TFLOP/s
+    bf16 dense peak);
   * the split-KV decode over a 2048-slot cache (B=64, H=Hkv=6, D=128) at
     window 512 and 2048, as HBM GB/s of algorithmic bytes;
   * ``nc_rope_qknorm`` on the d12 q and k, as HBM GB/s;
-  * the d12 SSSL and GQA SSSL stacks (4 layer calls sharing one RoPE table);
+  * the d12 SSSL and GQA SSSL stacks (4 ``nc_attn_fwd`` layer calls);
 and, on the host, the fp64 oracle on a bounded sample (``cpu_baseline``).
 
 Only rank 0 of a 1-GPU job exists here: ``--gpus`` above 1 exits.
@@ -122,7 +123,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "fwd_tab", "decode", "rope", "stacks", "copy"],
+                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -160,35 +161,38 @@ def main():
     cfg = wl.CONFIGS[1]
     W = cfg.windows[0]
     flops = wl.prefill_flops(cfg.B, cfg.T, cfg.H, cfg.D, W)
-    if args.only in ("all", "fwd", "fwd_tab"):
+    if args.only in ("all", "fwd", "core"):
         sets = []
         for s in range(args.sets):
             q, k, v = wl.prefill_inputs(cfg, layer=s)  # set s uses layer index s in the seed
             sets.append((q.to(dev), k.to(dev), v.to(dev), torch.empty_like(q, device=dev)))
-        ws = torch.empty(nc.attn_fwd_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Hkv, cfg.D),
-                         dtype=torch.uint8, device=dev)
-        tab = nc.rope_table(cfg.T, cfg.D, device=dev)
+        nws = nc.attn_fwd_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Hkv, cfg.D, 0, cfg.dtype)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
 
         def step(i):
             q, k, v, o = sets[i % len(sets)]
             nc.attn_fwd(q, k, v, window=W, out=o, workspace=ws)
-
-        def kern(i):
-            q, k, v, o = sets[i % len(sets)]
-            nc.attn_fwd_tab(q, k, v, tab, window=W, out=o)
 
         if args.only in ("all", "fwd"):
             for i in range(Wm):
                 step(i)
             ms = event_time_ms(step, K, torch)
             out["step_ms"] = ms
-        if args.only in ("all", "fwd_tab"):
+        if args.only in ("all", "core"):
+            # one prepared workspace (k' and table) per input set
+            wss = [nc.attn_prep(k, workspace=torch.empty_like(ws)) for (q, k, v, o) in sets]
+
+            def kern(i):
+                q, k, v, o = sets[i % len(sets)]
+                nc.attn_core(q, v, wss[i % len(sets)], window=W, out=o)
+
             for i in range(Wm):
                 kern(i)
             out["kern_ms"] = event_time_ms(kern, K, torch)
-        del sets
+            del wss
+        del sets, ws
 
-    if args.only in ("fwd", "fwd_tab"):
+    if args.only in ("fwd", "core"):
         print(json.dumps(out))
         return
 
@@ -254,11 +258,12 @@ def main():
             c = wl.CONFIGS[cidx]
             layers = [tuple(t.to(dev) for t in wl.prefill_inputs(c, layer=l)) for l in range(4)]
             outs = [torch.empty_like(l[0]) for l in layers]
-            tabc = nc.rope_table(c.T, c.D, device=dev)
+            wsc = torch.empty(nc.attn_fwd_workspace_bytes(c.B, c.T, c.H, c.Hkv, c.D, 0, c.dtype),
+                              dtype=torch.uint8, device=dev)
 
-            def sstep(i, layers=layers, outs=outs, tabc=tabc, c=c):
+            def sstep(i, layers=layers, outs=outs, wsc=wsc, c=c):
                 for l, (q, k, v) in enumerate(layers):
-                    nc.attn_fwd_tab(q, k, v, tabc, window=c.windows[l], out=outs[l])
+                    nc.attn_fwd(q, k, v, window=c.windows[l], out=outs[l], workspace=wsc)
 
             for i in range(Wm):
                 sstep(i)
@@ -269,7 +274,7 @@ def main():
                                        f"windows={list(c.windows)}",
                               "us_per_stack": round(ms * 1e3, 2), "TFLOP_per_s": round(tf, 1),
                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-            del layers, outs
+            del layers, outs, wsc
         if args.only == "stacks":
             print(json.dumps(stacks))
             return

@@ -71,7 +71,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 1
+#define NC_ABI_VERSION 2
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -112,38 +112,36 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
  * Requires H % Hkv == 0, window >= 1 (window >= T: full causal), the sizes
  * of nc_rope_qknorm, T * Hkv * D * sizeof(element) < 2^32 (one sequence's K
  * or V is addressed with 32-bit byte offsets), and o not overlapping any input.
+ * Workspace (nc_attn_fwd_workspace_bytes, which depends on B, T, Hkv, D and
+ * dtype): the (cos, sin) table of the T positions and k' = norm(rope(k)).
+ * nc_attn_fwd(...) is exactly nc_attn_prep followed by nc_attn_core on the
+ * same workspace.
  */
-size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset);
+size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset,
+                                   nc_dtype dtype);
 nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
                       int B, int T, int H, int Hkv, int D, int window,
                       double rope_base, int pos_offset, nc_dtype dtype,
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
- * nc_rope_table / nc_attn_fwd_tab -- the same prefill forward split in two
- * calls, for callers that run several layers over the same positions (the
- * SSSL stack of the nanochat pages runs every layer at one T): the RoPE
- * cos/sin table is built once and shared by every layer's nc_attn_fwd_tab.
- * nc_attn_fwd(...) is exactly nc_rope_table into its workspace followed by
- * nc_attn_fwd_tab.
- *
- *   tab  device buffer of nc_rope_table_bytes(T, D) bytes, 16-byte aligned,
- *        caller-owned. nc_rope_table writes, for a_ti =
- *        (pos_offset + t) * rope_base^(-2i/D), t < T, i < D/2, row-major:
- *          part 1 (T*D/2 float pairs): (cos a_ti, sin a_ti) in fp32;
- *          part 2 (T*D/2 pairs of bf16x2 words): (cos, -sin) and (sin, cos),
- *        with a_ti formed and reduced modulo 2*pi in fp64.
- * nc_attn_fwd_tab takes the q/k/v/o arguments of nc_attn_fwd and a table
- * built for at least T positions with the wanted rope_base and pos_offset;
- * the table is only read.
+ * nc_attn_prep / nc_attn_core -- the two stages of nc_attn_fwd, for callers
+ * that schedule them separately (for instance to overlap one layer's prep with
+ * another layer's attention on a second stream).
+ *   nc_attn_prep writes into ws the fp32 (cos, sin) pairs of angles
+ *     (pos_offset + t) * rope_base^(-2i/D), t < T, i < D/2, each formed and
+ *     reduced modulo 2*pi in fp64, and k' = norm(rope(k)) in k's layout and
+ *     element type. Arguments as for nc_attn_fwd.
+ *   nc_attn_core computes o from raw q, the k' and table in ws (only read),
+ *     and v; B, T, Hkv, D and dtype must be those of the nc_attn_prep call
+ *     that filled ws, which must complete (same stream or an event) first.
  */
-size_t nc_rope_table_bytes(int T, int D);
-nc_status nc_rope_table(void* tab, size_t tab_bytes, int T, int D, double rope_base,
-                        int pos_offset, void* stream);
-nc_status nc_attn_fwd_tab(const void* q, const void* k, const void* v, void* o,
-                          int B, int T, int H, int Hkv, int D, int window,
-                          const void* tab, size_t tab_bytes, nc_dtype dtype,
-                          void* stream);
+nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_base,
+                       int pos_offset, nc_dtype dtype, void* ws, size_t ws_bytes,
+                       void* stream);
+nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int H, int Hkv,
+                       int D, int window, nc_dtype dtype, const void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * nc_attn_decode -- one decode step per sequence over a contiguous KV cache

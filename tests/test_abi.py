@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 1
+    assert L.nc_abi_version() == 2
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -75,6 +75,23 @@ def _fwd(**kw):
 def test_attn_fwd_validation(kw, status, frag):
     assert _fwd(**kw) == status
     assert frag in nc.lib().nc_last_error().decode()
+
+
+def test_prep_core_validation():
+    L = nc.lib()
+    need = L.nc_attn_fwd_workspace_bytes(1, 8, 2, 2, 64, 0, 0)
+    assert L.nc_attn_prep(None, 1, 8, 2, 64, 1e4, 0, 0, P, need, None) == 1
+    assert b"k is NULL" in L.nc_last_error()
+    assert L.nc_attn_prep(P, 1, 8, 2, 64, 1e4, 0, 0, P, need - 1, None) == 1
+    assert b"workspace" in L.nc_last_error()
+    assert L.nc_attn_prep(P, 1, 8, 2, 64, -1.0, 0, 0, P, need, None) == 1
+    assert L.nc_attn_core(P, P, P, 1, 8, 2, 2, 64, 0, 0, P, need, None) == 1
+    assert b"window" in L.nc_last_error()
+    assert L.nc_attn_core(P, P, None, 1, 8, 2, 2, 64, 8, 0, P, need, None) == 1
+    assert b"o is NULL" in L.nc_last_error()
+    assert L.nc_attn_core(P, P, P, 1, 8, 2, 2, 64, 8, 0, None, need, None) == 1
+    assert b"ws is NULL" in L.nc_last_error()
+    assert L.nc_attn_core(P, P, P, 1, 8, 3, 2, 64, 8, 0, P, need, None) == 1
 
 
 def test_rope_qknorm_validation():
@@ -118,9 +135,12 @@ def test_workspace_queries():
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
     # fp32 (cos, sin) and bf16 {(cos,-sin),(sin,cos)} per position and
     # frequency (16 bytes), rounded up to 256 bytes
-    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0) == 2048 * 64 * 16
-    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0) == 768  # 3*16*16 = 768
-    assert L.nc_rope_table_bytes(3, 32) == 768
+    # fp32 (cos, sin) per position and frequency, then k' in the element type,
+    # each part rounded up to 256 bytes
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 2
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 1) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 4
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 512 + 512  # 3*16*8 -> 512, 3*2*32*2 -> 512
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 7) == 0
     # few (sequence, head) pairs: the key range is split and needs chunk states
     n = L.nc_attn_decode_workspace_bytes(2, 2048, 6, 6, 128, 2048)
     assert n > 0 and n % 256 == 0

@@ -230,6 +230,18 @@ def _decode_check(q, kn, vn, kc, vc, L, W, dtype, what):
     assert torch.equal(kcd.cpu()[mask], kc[mask]) and torch.equal(vcd.cpu()[mask], vc[mask])
 
 
+
+def test_prep_core_equals_fwd():
+    """attn_prep followed by attn_core is exactly attn_fwd (same kernels, same workspace)."""
+    _say("prep + core == fwd")
+    q, k, v = wl.small_prefill(2, 300, 8, 2, 128, seed=4242)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1 = nc.attn_fwd(q, k, v, window=200, pos_offset=7)
+    ws = nc.attn_prep(k, pos_offset=7)
+    o2 = nc.attn_core(q, v, ws, window=200)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
 DEC_SMALL = [
     # B, Tmax, H, Hkv, D, W, dtype
     (4, 300, 4, 2, 128, 100, torch.bfloat16),

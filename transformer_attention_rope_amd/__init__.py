@@ -8,6 +8,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
 
     rope_qknorm(q, k, rope_base=1e4, pos_offset=0)          -> (q', k')
     attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
+    attn_prep(k, ...) -> workspace;  attn_core(q, v, workspace, window=...) -> o
     attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window=..., rope_base=1e4) -> o
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_decode",
-    "rope_table", "attn_fwd_tab", "decode_workspace",
+    "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes", "rope_qknorm_workspace_bytes",
     "NC_OK", "NC_ERR_INVALID", "NC_ERR_UNSUPPORTED", "NC_ERR_HIP", "NC_BF16", "NC_F32",
 ]
@@ -38,11 +39,10 @@ _SIGS = {
     "nc_last_error": (ctypes.c_char_p, []),
     "nc_rope_qknorm_workspace_bytes": (_sz, [_i, _i, _i]),
     "nc_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
-    "nc_attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
-    "nc_rope_table_bytes": (_sz, [_i, _i]),
-    "nc_rope_table": (_i, [_vp, _sz, _i, _i, _d, _i, _vp]),
-    "nc_attn_fwd_tab": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
+    "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
+    "nc_attn_core": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
                             _vp, _sz, _vp]),
@@ -124,8 +124,9 @@ def rope_qknorm_workspace_bytes(T: int, D: int, pos_offset: int = 0) -> int:
     return int(lib().nc_rope_qknorm_workspace_bytes(T, D, pos_offset))
 
 
-def attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset=0) -> int:
-    return int(lib().nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset))
+def attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset=0, dtype=torch.bfloat16) -> int:
+    dt = NC_F32 if dtype == torch.float32 else NC_BF16
+    return int(lib().nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt))
 
 
 def attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window) -> int:
@@ -180,7 +181,7 @@ def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: in
     o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
     if o.shape != q.shape:
         raise ValueError("out must have q's shape")
-    need = attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset)
+    need = attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, q.dtype)
     ws = _workspace(need, q.device, workspace)
     _call("nc_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
           float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
@@ -188,30 +189,32 @@ def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: in
     return o
 
 
-def rope_table(T: int, D: int, *, rope_base: float = 10000.0, pos_offset: int = 0,
-               device="cuda", out=None):
-    """(cos, sin) fp32 table for positions pos_offset .. pos_offset+T-1, shape (T, D/2, 2)."""
-    n = int(lib().nc_rope_table_bytes(T, D))
-    tab = torch.empty(max(n // 4, 1), dtype=torch.float32, device=device) if out is None else out
-    _gpu(tab, "out", tab.dim(), torch.float32)
-    _call("nc_rope_table", _ptr(tab), tab.numel() * 4, int(T), int(D), float(rope_base),
-          int(pos_offset), _stream(tab))
-    return tab
+def attn_prep(k, *, rope_base: float = 10000.0, pos_offset: int = 0, H=None, workspace=None):
+    """First stage of attn_fwd: k' = norm(rope(k)) and the q-side (cos, sin) table,
+    into a workspace (returned) for attn_core. k (B,T,Hkv,D)."""
+    k = _gpu(k, "k", 4)
+    B, T, Hkv, D = k.shape
+    need = attn_fwd_workspace_bytes(B, T, Hkv if H is None else H, Hkv, D, pos_offset, k.dtype)
+    ws = _workspace(need, k.device, workspace)
+    _call("nc_attn_prep", _ptr(k), B, T, Hkv, D, float(rope_base), int(pos_offset), _dt(k),
+          _ptr(ws), ws.numel() * ws.element_size(), _stream(k))
+    return ws
 
 
-def attn_fwd_tab(q, k, v, tab, *, window: int, out=None):
-    """attn_fwd with a prebuilt rope_table (shared by layers at the same positions)."""
+def attn_core(q, v, workspace, *, window: int, out=None):
+    """Second stage of attn_fwd: attention from raw q (B,T,H,D), v (B,T,Hkv,D) and the
+    workspace filled by attn_prep for the same B, T, Hkv, D and dtype."""
     q = _gpu(q, "q", 4)
-    k = _gpu(k, "k", 4, q.dtype)
     v = _gpu(v, "v", 4, q.dtype)
-    tab = _gpu(tab, "tab", tab.dim(), torch.float32)
     B, T, H, D = q.shape
-    Hkv = k.shape[2]
-    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
-        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    Hkv = v.shape[2]
+    if tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError(f"v {tuple(v.shape)} does not match q {tuple(q.shape)}")
     o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
-    _call("nc_attn_fwd_tab", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
-          _ptr(tab), tab.numel() * 4, _dt(q), _stream(q))
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _call("nc_attn_core", _ptr(q), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window), _dt(q),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     return o
 
 

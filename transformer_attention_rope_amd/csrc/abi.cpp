@@ -120,84 +120,85 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
 }
 
 // ---------------------------------------------------------------- attn_fwd
-size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset) {
-  (void)B;
+// Workspace: the fp32 (cos, sin) table of the T positions, then k'.
+namespace {
+size_t prep_table_bytes(int T, int D) { return round_up(nc::attn_prep_table_bytes(T, D)); }
+size_t prep_k_bytes(int B, int T, int Hkv, int D, nc_dtype dt) {
+  return round_up((size_t)B * T * Hkv * D * (dt == NC_F32 ? 4 : 2));
+}
+nc_status check_fwd_sizes(int B, int T, int H, int Hkv, int D, nc_dtype dt) {
+  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  if (s != NC_OK) return s;
+  if ((long long)T * (D / 2) > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
+  return check_seq_bytes(T, Hkv, D, dt);
+}
+nc_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL");
+  if (!aligned16(ws)) return fail(NC_ERR_INVALID, "ws is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+  return NC_OK;
+}
+}  // namespace
+
+size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_offset,
+                                   nc_dtype dtype) {
   (void)H;
-  (void)Hkv;
   (void)pos_offset;
-  if (T < 1 || D < 2) return 0;
-  return round_up(nc::rope_table_bytes(T, D));
+  if (B < 1 || T < 1 || Hkv < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
+  return prep_table_bytes(T, D) + prep_k_bytes(B, T, Hkv, D, dtype);
+}
+
+nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_base,
+                       int pos_offset, nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, Hkv, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  const char* names[] = {"k"};
+  const void* ptrs[] = {k};
+  if ((s = check_ptrs(names, ptrs, 1)) != NC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, Hkv, Hkv, D, pos_offset, dt))) != NC_OK)
+    return s;
+  hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D), ws, B, T, Hkv, D,
+                                      rope_base, pos_offset, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
+  return ok();
+}
+
+nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int H, int Hkv, int D,
+                       int window, nc_dtype dt, const void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  const char* names[] = {"q", "v", "o"};
+  const void* ptrs[] = {q, v, o};
+  if ((s = check_ptrs(names, ptrs, 3)) != NC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, 0, dt))) != NC_OK)
+    return s;
+  hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D), v, o, B, T, H,
+                                      Hkv, D, window, ws, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_core launch");
+  return ok();
 }
 
 nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T, int H,
                       int Hkv, int D, int window, double rope_base, int pos_offset, nc_dtype dt,
                       void* ws, size_t ws_bytes, void* stream) {
-  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
   if (s != NC_OK) return s;
   if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
   if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
-  if ((long long)T * (D / 2) > 0x7fffffffLL)
-    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
-  if ((s = check_seq_bytes(T, Hkv, D, dt)) != NC_OK) return s;
-  const char* names[] = {"q", "k", "v", "o", "ws"};
-  const void* ptrs[] = {q, k, v, o, ws};
-  if ((s = check_ptrs(names, ptrs, 5)) != NC_OK) return s;
-  const size_t need = nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset);
-  if (ws_bytes < need)
-    return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = nc::launch_rope_table(ws, T, D, rope_base, pos_offset, st);
-  if (e != hipSuccess) return hip_fail(e, "rope table launch");
-  e = nc::launch_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, ws,
-                          dt == NC_BF16 ? nc::kBF16 : nc::kF32, st);
-  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
-  return ok();
-}
-
-// ------------------------------------------------- rope table + attn_fwd_tab
-size_t nc_rope_table_bytes(int T, int D) {
-  if (T < 1 || D < 2) return 0;
-  return round_up(nc::rope_table_bytes(T, D));
-}
-
-nc_status nc_rope_table(void* tab, size_t tab_bytes, int T, int D, double rope_base,
-                        int pos_offset, void* stream) {
-  if (T < 1) return fail(NC_ERR_INVALID, "T must be >= 1 (got %d)", T);
-  if (D != 32 && D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
-  nc_status s = check_rope(rope_base, pos_offset, T);
-  if (s != NC_OK) return s;
-  if ((long long)T * (D / 2) > 0x7fffffffLL)
-    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
-  const char* names[] = {"tab"};
-  const void* ptrs[] = {tab};
-  if ((s = check_ptrs(names, ptrs, 1)) != NC_OK) return s;
-  const size_t need = nc_rope_table_bytes(T, D);
-  if (tab_bytes < need)
-    return fail(NC_ERR_INVALID, "table of %zu bytes is below the required %zu", tab_bytes, need);
-  hipError_t e = nc::launch_rope_table(tab, T, D, rope_base, pos_offset, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "rope table launch");
-  return ok();
-}
-
-nc_status nc_attn_fwd_tab(const void* q, const void* k, const void* v, void* o, int B, int T,
-                          int H, int Hkv, int D, int window, const void* tab, size_t tab_bytes,
-                          nc_dtype dt, void* stream) {
-  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
-  if (s != NC_OK) return s;
-  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
-  if ((long long)T * (D / 2) > 0x7fffffffLL)
-    return fail(NC_ERR_INVALID, "T=%d too long for the RoPE table", T);
-  if ((s = check_seq_bytes(T, Hkv, D, dt)) != NC_OK) return s;
-  const char* names[] = {"q", "k", "v", "o", "tab"};
-  const void* ptrs[] = {q, k, v, o, tab};
-  if ((s = check_ptrs(names, ptrs, 5)) != NC_OK) return s;
-  const size_t need = nc::rope_table_bytes(T, D);
-  if (tab_bytes < need)
-    return fail(NC_ERR_INVALID, "table of %zu bytes is below the %zu needed for T=%d", tab_bytes, need, T);
-  hipError_t e = nc::launch_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, tab,
-                                     dt == NC_BF16 ? nc::kBF16 : nc::kF32, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
-  return ok();
+  const char* names[] = {"q", "k", "v", "o"};
+  const void* ptrs[] = {q, k, v, o};
+  if ((s = check_ptrs(names, ptrs, 4)) != NC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt))) != NC_OK)
+    return s;
+  if ((s = nc_attn_prep(k, B, T, Hkv, D, rope_base, pos_offset, dt, ws, ws_bytes, stream)) != NC_OK)
+    return s;
+  return nc_attn_core(q, v, o, B, T, H, Hkv, D, window, dt, ws, ws_bytes, stream);
 }
 
 // -------------------------------------------------------------- attn_decode

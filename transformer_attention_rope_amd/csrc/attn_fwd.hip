@@ -1,5 +1,6 @@
-// Prefill attention forward for gfx950: RoPE + QK-norm fused into the Q/K
-// loads, GQA, causal sliding-window band, online softmax, bf16 MFMA.
+// Prefill attention forward for gfx950: GQA, causal sliding-window band,
+// softmax, bf16 MFMA; q is rotated and normalised in the kernel, k arrives
+// rotated and normalised from the input stage (attn_prep_kernel).
 //
 // What is computed ("从文本到聊天模型" (onehacker.top) §5.4 score = Q K^T,
 // softmax, weighted sum of V; §5.5 causal mask; §5.6 RoPE;
@@ -10,9 +11,15 @@
 //   q', k'   = RMSNorm(RoPE(q)), RMSNorm(RoPE(k)) at positions pos_offset + t.
 //
 // Design (bf16 path):
-//  * A workgroup of 4 waves owns 128 query columns: hpw query heads of one
-//    K/V group times 128/hpw consecutive positions, so a K/V tile staged in
-//    LDS serves every head of the group. Each wave owns 32 columns.
+//  * k' is formed once per key row by the input stage: every key tile is
+//    visited by several query tiles, and a copy costs the tile loop far less
+//    than re-rotating and re-normalising it on each visit.
+//  * A workgroup of 4 waves (one per SIMD) owns 256 query columns: hpw query
+//    heads of one K/V group times 256/hpw consecutive positions, so a K/V
+//    tile staged in LDS serves every head of the group. Each wave owns 64
+//    columns as two 32-column blocks, so every K or V fragment read from LDS
+//    feeds two MFMAs; with one wave per SIMD the accumulators may use the
+//    whole register file (VGPRs and AGPRs).
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    the K tile is the A operand (LDS), the rotated, normalised, pre-scaled Q
 //    is the B operand (registers, loaded once). In the accumulator layout a
@@ -30,8 +37,16 @@
 //  * V is transposed into LDS (V^T[d][key]) with keys permuted so that each
 //    MFMA A-operand fetch is one 16-byte LDS read matching the key order the
 //    score accumulator hands over.
-//  * Key tiles entirely outside the band are never visited; tiles entirely
-//    inside skip the mask. Heaviest query tiles are dispatched first.
+//  * Staging is double-buffered twice over: tile kt is computed from one LDS
+//    buffer while tile kt+1, loaded into registers during tile kt-1, is
+//    written to the other, and the loads of tile kt+2 go out at the start of
+//    tile kt into the second register set.
+//  * A tile whose keys every column of a wave sees runs a fixed instruction
+//    order in which the exponentials and the staging of the next tile sit
+//    between the MFMAs: a wave issues vector instructions while its own
+//    MFMAs execute, so this work hides under the matrix pipe. Tiles crossing
+//    a wave's band edge are masked in place; tiles outside it are skipped
+//    (the wave only stages). Heaviest query tiles are dispatched first.
 //
 // fp32 path: exact fp32 arithmetic on the vector ALUs (one thread per query
 // column), same band, same softmax without a running maximum.
@@ -39,16 +54,29 @@
 #include "launch.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace nc {
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at
+// compile time (the loop bodies below are too large for the unroller).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
+
 struct FwdArgs {
   const void* q;
-  const void* k;
+  const void* kp;      // k' = RMSNorm(RoPE(k)), layout and type of k
   const void* v;
   void* o;
   const float2* tabq;  // [T][D/2] (cos, sin) fp32 for positions pos_offset + t
-  const uint2* tabk;   // [T][D/2] bf16 pairs {(cos, -sin), (sin, cos)}
   int B, T, H, Hkv, W;
   int G;         // H / Hkv
   int hpw_log2;  // log2(query heads per workgroup)
@@ -63,22 +91,33 @@ struct FwdArgs {
 // =====================================================================
 template <int D>
 struct BfCfg {
-  static constexpr int NW = 8;          // waves per workgroup
-  static constexpr int NT = 64 * NW;    // threads per workgroup
-  static constexpr int NC = 32 * NW;    // query columns per workgroup
-  static constexpr int BN = 64;         // keys per tile
-  static constexpr int KS = D / 16;     // MFMA k-steps of Q.K^T
-  static constexpr int DB = D / 32;     // 32-row blocks of O^T
-  static constexpr int RB = BN / 32;    // 32-key blocks per tile
-  static constexpr int PS = BN / 16;    // MFMA k-steps of P.V
-  static constexpr int KLD = D + 8;     // LDS row stride of K (bf16), +16 B against bank conflicts
-  static constexpr int VLD = BN + 8;    // LDS row stride of V^T (bf16)
-  static constexpr int CPR = D / 8;     // 16-byte chunks per K row
-  static constexpr int KCH = BN * CPR;  // K chunks per tile
+  static constexpr int NW = 4;             // waves per workgroup, one per SIMD
+  static constexpr int NT = 64 * NW;       // threads per workgroup
+  static constexpr int CB = 2;             // 32-column blocks per wave
+  static constexpr int NC = 32 * CB * NW;  // query columns per workgroup
+  static constexpr int BN = 64;            // keys per tile
+  static constexpr int KS = D / 16;        // MFMA k-steps of K Q^T
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int RB = BN / 32;       // 32-key blocks per tile
+  static constexpr int PS = BN / 16;       // MFMA k-steps of V^T P^T
+  static constexpr int KLD = D + 8;        // LDS row stride of K (bf16), +16 B against bank conflicts
+  static constexpr int VLD = BN + 8;       // LDS row stride of V^T (bf16)
+  static constexpr int CPR = D / 8;        // 16-byte chunks per K or V row
+  static constexpr int KCH = BN * CPR;     // K chunks per tile
   static constexpr int NKP = (KCH + NT - 1) / NT;  // K chunks per thread
-  static constexpr int NMB = (BN / 4) * (D / 4);   // 4-key x 4-dim V micro-blocks per tile
-  static constexpr int KBUF = BN * KLD; // bf16 elements per K buffer
-  static constexpr int VBUF = D * VLD;  // bf16 elements per V^T buffer
+  static constexpr int NMB = (BN / 4) * CPR;       // 4-key x 8-dim V micro-blocks per tile
+  static constexpr int NVB = (NMB + NT - 1) / NT;  // V micro-blocks per thread
+  static constexpr int KBUF = BN * KLD;    // bf16 elements per K buffer
+  static constexpr int VBUF = D * VLD;     // bf16 elements per V^T buffer
+  // A tile is NM MFMAs: the score MFMAs (rb, s, cb) for m < NSM, then the
+  // P.V MFMAs (s2, db, cb). Fragment f (K fragments (rb, s) first, then V
+  // fragments (s2, db)) feeds MFMAs f*CB .. f*CB + CB-1.
+  static constexpr int NSM = RB * KS * CB;
+  static constexpr int NPM = PS * DB * CB;
+  static constexpr int NM = NSM + NPM;
+  static constexpr int NKF = RB * KS;
+  static constexpr int NF = NKF + PS * DB;
+  static constexpr int LA = 6;             // LDS fragments read ahead of their MFMA
 };
 
 // Position of key kk (0..BN-1) inside a V^T row. The score accumulator of
@@ -90,45 +129,123 @@ __device__ __forceinline__ int vt_pos(int kk) {
   const int blk16 = kk >> 4, w = kk & 15;
   return (blk16 << 4) | (((w >> 2) & 1) << 3) | ((w >> 3) << 2) | (w & 3);
 }
+// V^T rows hold BN keys in 16-byte chunks; chunk c of row d is stored at
+// chunk position c ^ ((d >> 4) & 7). The transposing writes come from lanes
+// whose rows are 8 apart, the fragment reads from lanes with consecutive
+// rows: with a 72-element row stride and this swizzle both spread over all
+// LDS banks.
+__device__ __forceinline__ int vt_swz(int d, int col) {
+  return ((((col >> 3) ^ (d >> 4)) & 7) << 3) | (col & 7);
+}
 
-// Instruction order of a full tile for D = 128 and D = 64. Step m issues
-// one MFMA -- the score MFMAs S0[0..KS), S1[0..KS) of the two 32-key blocks,
-// then the P.V MFMAs of block 0 and of block 1 -- followed by up to two
-// slices of vector work that do not depend on it:
-//   0..4*NKP-1   RoPE + RMSNorm of the next tile's K chunk id/4, part id%4
-//   100, 101     transposition of the next tile's V micro-block, half 0/1
-//   200+8*rb+i   2^S of score registers 2i, 2i+1 of block rb, packed into
-//                the P operand, and their contribution to the row sum
-// A block's exponentials start two MFMAs after its last score MFMA, and
-// each P.V MFMA comes after the four slices that produce its P operand.
+// Instruction order of a tile in which every key is visible to every column
+// of the wave. After MFMA m come the vector-work entries v[m][..]. Each
+// slice has a first half (id) and a second half (id + 1000) issued one MFMA
+// later, so the instructions between two MFMAs never wait on each other
+// (a wave issues in order; a stalled instruction would hold the next MFMA):
+//   200+8(rb*CB+cb)+i   2^S of score registers 2i, 2i+1 of block (rb, cb);
+//                then packing into the P operand and the row-sum update
+//   100+4vb+m    transposition of the next tile's V micro-block vb, dims
+//                pair m; then its two V^T rows into LDS
+//   j            nothing; then the next tile's K chunk j into LDS
+// Slices start in that order, spread evenly over the MFMAs. An exponential
+// starts two MFMAs after the last score MFMA of its block, and a P.V MFMA
+// comes after the second halves of the four slices that build its P operand.
 template <int D>
-struct FullSched;
-template <>
-struct FullSched<128> {
-  static constexpr int NM = 32;
-  static constexpr short v[NM][2] = {
-      {0, -1},   {1, -1},   {2, -1},   {3, -1},   {4, -1},   {5, -1},   {6, -1},   {7, -1},
-      {100, -1}, {101, -1}, {200, -1}, {201, -1}, {202, -1}, {203, -1}, {204, -1}, {205, -1},
-      {206, -1}, {207, -1}, {208, -1}, {209, -1}, {210, -1}, {211, -1}, {212, -1}, {213, -1},
-      {214, -1}, {215, -1}, {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1},  {-1, -1}};
+struct TileSched {
+  using C = BfCfg<D>;
+  static constexpr int MAXS = 24;
+  short v[C::NM][MAXS];
+  int ok;
+  int nslices;
+  constexpr TileSched() : v{}, ok(1), nslices(0) {
+    short q[160] = {};
+    short early[160] = {};
+    short start[160] = {};
+    bool done[160] = {};
+    int nq = 0;
+    for (int s2 = 0; s2 < C::PS; ++s2)
+      for (int cb = 0; cb < C::CB; ++cb)
+        for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
+          const int rb = s2 / 2;
+          early[nq] = (short)((rb + 1) * C::KS * C::CB + 1);
+          q[nq++] = (short)(200 + 8 * (rb * C::CB + cb) + i);
+        }
+    for (int vb = 0; vb < C::NVB; ++vb)
+      for (int m = 0; m < 4; ++m) q[nq++] = (short)(100 + 4 * vb + m);
+    for (int j = 0; j < C::NKP; ++j) q[nq++] = (short)j;
+    nslices = nq;
+    for (int m = 0; m < C::NM; ++m)
+      for (int k = 0; k < MAXS; ++k) v[m][k] = -1;
+    int cnt[C::NM] = {};
+    auto put = [&](int m, int id) {
+      if (cnt[m] < MAXS) v[m][cnt[m]++] = (short)id; else ok = 0;
+    };
+    // slices started per MFMA: about one when the tile has more MFMAs than slices
+    const int per_slot = (nq + C::NM - 1) / C::NM;
+    int head = 0;
+    for (int m = 0; m < C::NM; ++m) {
+      // second halves of the slices started after MFMA m-1
+      for (int x = 0; x < nq; ++x)
+        if (done[x] && start[x] == m - 1) put(m, q[x] + 1000);
+      int started = 0;
+      auto begin = [&](int x) {
+        put(m, q[x]);
+        done[x] = true;
+        start[x] = (short)m;
+        ++started;
+      };
+      // the P operand of MFMA m+2 must be complete after slot m+1
+      if (m + 2 < C::NM && m + 2 >= C::NSM) {
+        const int mm = m + 2 - C::NSM;
+        const int s2 = mm / (C::DB * C::CB), cb = mm % C::CB, rb = s2 / 2;
+        for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
+          const short id = (short)(200 + 8 * (rb * C::CB + cb) + i);
+          for (int x = 0; x < nq; ++x)
+            if (q[x] == id && !done[x]) {
+              // everything queued before it goes first (keeps the queue order)
+              for (int y = head; y <= x; ++y)
+                if (!done[y]) begin(y);
+            }
+        }
+      }
+      while (head < nq && done[head]) ++head;
+      const bool last = m == C::NM - 1;
+      while ((started < per_slot || last) && head < nq && early[head] <= m) {
+        begin(head);
+        while (head < nq && done[head]) ++head;
+      }
+      if (last)  // slices started after the last MFMA finish right away
+        for (int x = 0; x < nq; ++x)
+          if (done[x] && start[x] == m) put(m, q[x] + 1000);
+    }
+    for (int x = 0; x < nq; ++x)
+      if (!done[x]) ok = 0;
+    // every P.V MFMA comes after the second halves of its exponentials
+    for (int m = C::NSM; m < C::NM; ++m) {
+      const int mm = m - C::NSM;
+      const int s2 = mm / (C::DB * C::CB), cb = mm % C::CB, rb = s2 / 2;
+      for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
+        const int id = 1000 + 200 + 8 * (rb * C::CB + cb) + i;
+        bool seen = false;
+        for (int mp = 0; mp < m; ++mp)
+          for (int k = 0; k < MAXS; ++k)
+            if (v[mp][k] == id) seen = true;
+        if (!seen) ok = 0;
+      }
+    }
+  }
 };
-template <>
-struct FullSched<32> {  // not used: D = 32 tiles run the generic order
-  static constexpr int NM = 8;
-  static constexpr short v[NM][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1},
-                                     {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
-};
-template <>
-struct FullSched<64> {
-  static constexpr int NM = 16;
-  static constexpr short v[NM][2] = {
-      {0, -1},    {1, -1},    {2, -1},    {3, -1},    {100, -1},  {101, -1}, {200, 201}, {202, 203},
-      {204, 205}, {206, 207}, {208, 209}, {210, 211}, {212, 213}, {214, 215}, {-1, -1},  {-1, -1}};
+template <int D>
+struct TileSchedTab {
+  static constexpr TileSched<D> s{};
+  static_assert(s.ok, "tile schedule");
 };
 
 template <int D>
 __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   using C = BfCfg<D>;
+  constexpr int CB = C::CB;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * C::VBUF];
 
@@ -149,18 +266,113 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   const int q_last = min(q0 + (1 << p.bp_log2), p.T) - 1;
   const int g = (grp * hpw) / p.G;
 
-  // ---- this lane's query column
-  const int col = wave * 32 + n;
-  const int t = q0 + (col >> p.hpw_log2);
-  const int h = grp * hpw + (col & (hpw - 1));
-  const bool tvalid = t < p.T;
-  const int tc = tvalid ? t : p.T - 1;
+  // ---- key-tile range of the workgroup's band [max(0, q0 - W + 1), q_last]
+  const int k_first = max(0, q0 - p.W + 1);
+  const int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
+
+  // ---- staging: buffer resources whose ranges end at token T (reads past
+  // ---- the tail return zeros), per-thread byte offsets, per-tile bases
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const size_t kv_base = ((size_t)b * p.T * p.Hkv + g) * D;
+  const uint32_t kv_records = (uint32_t)(((size_t)p.T * p.Hkv - g) * D * 2);
+  const char* kseq = (const char*)((const uint16_t*)p.kp + kv_base);
+  const char* vseq = (const char*)((const uint16_t*)p.v + kv_base);
+
+  uint32_t k_voff[C::NKP], k_lds[C::NKP];
+  bool k_act[C::NKP];
+#pragma unroll
+  for (int j = 0; j < C::NKP; ++j) {
+    const int idx = tid + C::NT * j;
+    const int kr = idx / C::CPR, kc = idx % C::CPR;
+    k_act[j] = idx < C::KCH;
+    k_voff[j] = (uint32_t)kr * row_bytes + kc * 16;
+    k_lds[j] = kr * C::KLD + kc * 8;
+  }
+  // V micro-block mb: dims 8*(mb % CPR) .. +7 of the 4 keys of key group
+  // vgp, so a wave's load of one key slot covers whole rows. Key groups are
+  // taken in the order 0, 2, 1, 3 within each run of four, which (with the
+  // V^T swizzle) keeps the transposing LDS writes free of bank conflicts.
+  uint32_t v_voff[C::NVB];
+  int v_lds[C::NVB];
+  bool v_act[C::NVB];
+#pragma unroll
+  for (int j = 0; j < C::NVB; ++j) {
+    const int mb = tid + C::NT * j;
+    const int vd = mb % C::CPR, grp4 = mb / C::CPR;
+    const int vgp = (grp4 & ~3) | ((grp4 & 1) << 1) | ((grp4 >> 1) & 1);
+    v_act[j] = mb < C::NMB;
+    v_voff[j] = (uint32_t)(4 * vgp) * row_bytes + vd * 16;
+    v_lds[j] = (8 * vd) * C::VLD + vt_swz(8 * vd, vt_pos(4 * vgp));
+  }
+
+  u32x4_t kw[2][C::NKP];
+  u32x4_t vw[2][C::NVB][4];
+
+  // Tile kt into register set S. Resources rebased on the tile's first key:
+  // rows past token T (and only those) fall beyond num_records and read as
+  // zero; a tile past the sequence gets an empty range.
+  auto gload = [&](auto Sc, int kt) {
+    constexpr int S = decltype(Sc)::value;
+    const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq + so, nk);
+#pragma unroll
+    for (int j = 0; j < C::NKP; ++j)
+      if (C::NKP * C::NT == C::KCH || k_act[j]) kw[S][j] = bload16(rk, k_voff[j], 0);
+#pragma unroll
+    for (int j = 0; j < C::NVB; ++j)
+      if (C::NVB * C::NT == C::NMB || v_act[j]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vw[S][j][r] = bload16(rv, v_voff[j] + r * row_bytes, 0);
+      }
+  };
+  // V micro-block j of set S, dims pair m: rows 2m, 2m+1 of its V^T block,
+  // 4 consecutive (permuted) key slots each
+  auto v_pair = [&](auto Sc, int j, int m, uint16_t* vb) {
+    constexpr int S = decltype(Sc)::value;
+    const uint32_t a0 = vw[S][j][0][m], a1 = vw[S][j][1][m], a2 = vw[S][j][2][m], a3 = vw[S][j][3][m];
+    const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+    const u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+    st8(vb + v_lds[j] + (2 * m) * C::VLD, lo);
+    st8(vb + v_lds[j] + (2 * m + 1) * C::VLD, hi);
+  };
+  // register set S into LDS buffer buf
+  auto stage = [&](auto Sc, int buf) {
+    constexpr int S = decltype(Sc)::value;
+    uint16_t* kb = Ks + buf * C::KBUF;
+    uint16_t* vb = Vt + buf * C::VBUF;
+#pragma unroll
+    for (int j = 0; j < C::NKP; ++j)
+      if (C::NKP * C::NT == C::KCH || k_act[j]) st16(kb + k_lds[j], kw[S][j]);
+#pragma unroll
+    for (int j = 0; j < C::NVB; ++j)
+      if (C::NVB * C::NT == C::NMB || v_act[j]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v_pair(Sc, j, m, vb);
+      }
+  };
+
+  // the first two tiles go out before the query prologue
+  gload(ic<0>{}, kt0);
+  gload(ic<1>{}, kt0 + 1);
+
+  // ---- this lane's query columns, one per 32-column block
+  int t[CB], h[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = wave * 32 * CB + cb * 32 + n;
+    t[cb] = q0 + (col >> p.hpw_log2);
+    h[cb] = grp * hpw + (col & (hpw - 1));
+  }
 
   // ---- Q: load, RoPE (fp32 table), RMSNorm, fold log2(e)/sqrt(D), pack as
   // ---- the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7)
-  bf16x8_t bq[C::KS];
-  {
-    const uint16_t* qrow = qg + (((size_t)b * p.T + tc) * p.H + h) * D;
+  bf16x8_t bq[CB][C::KS];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int tc = t[cb] < p.T ? t[cb] : p.T - 1;
+    const uint16_t* qrow = qg + (((size_t)b * p.T + tc) * p.H + h[cb]) * D;
     const float2* trow = p.tabq + (size_t)tc * (D / 2);
     float x[C::KS][8];
     float ss = 0.f;
@@ -188,360 +400,256 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       u32x4_t w;
 #pragma unroll
       for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[s][2 * m] * sc, x[s][2 * m + 1] * sc);
-      bq[s] = __builtin_bit_cast(bf16x8_t, w);
+      bq[cb][s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
-  // ---- key-tile range of the band [max(0, q0 - W + 1), q_last]
-  const int k_first = max(0, q0 - p.W + 1);
-  const int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
-
-  // ---- staging: buffer resources whose ranges end at token T (reads past
-  // ---- the tail return zeros), per-thread byte offsets, per-tile SGPR offsets
-  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
-  const size_t kv_base = ((size_t)b * p.T * p.Hkv + g) * D;
-  const uint32_t kv_records = (uint32_t)(((size_t)p.T * p.Hkv - g) * D * 2);
-  const char* kseq = (const char*)((const uint16_t*)p.k + kv_base);
-  const char* vseq = (const char*)((const uint16_t*)p.v + kv_base);
-  const uint32_t tab_row = (D / 2) * 8;
-  const uint32_t tab_records = (uint32_t)p.T * tab_row;
-
-  uint32_t k_voff[C::NKP], t_voff[C::NKP], k_lds[C::NKP];
-  bool k_act[C::NKP];
-#pragma unroll
-  for (int j = 0; j < C::NKP; ++j) {
-    const int idx = tid + C::NT * j;
-    const int kr = idx / C::CPR, kc = idx % C::CPR;
-    k_act[j] = idx < C::KCH;
-    k_voff[j] = (uint32_t)kr * row_bytes + kc * 16;
-    t_voff[j] = (uint32_t)kr * (D / 2) * 8 + kc * 32;
-    k_lds[j] = kr * C::KLD + kc * 8;
-  }
-  const bool v_act = tid < C::NMB;
-  const int vgp = tid & 15, vd = tid >> 4;  // V micro-block: keys 4*vgp.., dims 4*vd..
-  const uint32_t v_voff = (uint32_t)(4 * vgp) * row_bytes + vd * 8;
-  const int v_lds = (4 * vd) * C::VLD + vt_pos(4 * vgp);
-
-  u32x4_t kw[C::NKP], kt_[C::NKP][2];
-  u32x2_t vw[4];
-
-  // Resources rebased on the tile's first key: rows past token T (and only
-  // those) fall beyond num_records and read as zero.
-  auto gload = [&](int kt) {
-    // a tile past the sequence (staged but never used) gets empty ranges
-    const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
-    const uint32_t st = (uint32_t)kt * C::BN * tab_row;
-    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
-    const uint32_t nt = __builtin_amdgcn_readfirstlane(st < tab_records ? tab_records - st : 0u);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq + so, nk);
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc((const char*)p.tabk + st, nt);
-#pragma unroll
-    for (int j = 0; j < C::NKP; ++j) {
-      if (C::NKP * C::NT == C::KCH || k_act[j]) {
-        kw[j] = bload16(rk, k_voff[j], 0);
-        kt_[j][0] = bload16(rt, t_voff[j], 0);
-        kt_[j][1] = bload16(rt, t_voff[j] + 16, 0);
-      }
-    }
-    if (C::NMB >= C::NT || v_act) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vw[r] = bload8(rv, v_voff + r * row_bytes, 0);
-    }
-  };
-
-  // RoPE + RMSNorm of the staged K chunks (bf16 pair dot products against the
-  // (cos,-sin)/(sin,cos) table), and the V micro-block transposed into V^T.
-  auto stage = [&](int buf) {
-    uint16_t* kb = Ks + buf * C::KBUF;
-    uint16_t* vb = Vt + buf * C::VBUF;
-#pragma unroll
-    for (int j = 0; j < C::NKP; ++j) {
-      if (C::NKP * C::NT == C::KCH || k_act[j]) {
-        float ss = dot2bf(kw[j][0], kw[j][0], 0.f);
-        ss = dot2bf(kw[j][1], kw[j][1], ss);
-        ss = dot2bf(kw[j][2], kw[j][2], ss);
-        ss = dot2bf(kw[j][3], kw[j][3], ss);  // a rotation keeps the sum of squares
-        ss = dpp_group_sum<C::CPR>(ss);
-        const float inv = rsq(ss * (1.0f / D) + kEps);
-        u32x4_t w;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32x4_t& tt = kt_[j][m >> 1];
-          const float xe = dot2bf(kw[j][m], tt[2 * (m & 1)], 0.f);
-          const float xo = dot2bf(kw[j][m], tt[2 * (m & 1) + 1], 0.f);
-          w[m] = pack_bf2(xe * inv, xo * inv);
-        }
-        st16(kb + k_lds[j], w);
-      }
-    }
-    if (C::NMB >= C::NT || v_act) {
-      // rows 4vd..4vd+3 of V^T, 4 consecutive (permuted) key slots each
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint32_t a0 = vw[0][m], a1 = vw[1][m], a2 = vw[2][m], a3 = vw[3][m];
-        const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        st8(vb + v_lds + (2 * m) * C::VLD, lo);
-        st8(vb + v_lds + (2 * m + 1) * C::VLD, hi);
-      }
-    }
-  };
-
-  f32x16_t oacc[C::DB];
+  f32x16_t oacc[C::DB][CB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float lsum = 0.f;
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][cb][r] = 0.f;
+  float lsum[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) lsum[cb] = 0.f;
 
-  // Positions covered by this wave (its 32 columns): [tw0, tw1].
-  const int tw0 = q0 + ((wave * 32) >> p.hpw_log2);
-  const int tw1 = min(q0 + ((wave * 32 + 31) >> p.hpw_log2), p.T - 1);
+  // Positions covered by this wave (its 32*CB columns): [tw0, tw1].
+  const int tw0 = q0 + ((wave * 32 * CB) >> p.hpw_log2);
+  const int tw1 = min(q0 + ((wave * 32 * CB + 32 * CB - 1) >> p.hpw_log2), p.T - 1);
   constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
-  // Scores of one 32-key block: S^T = K Q^T (MFMA, log2 domain).
-  auto scores = [&](const uint16_t* kb, int rb) {
-    f32x16_t acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc, 0, 0, 0);
-    }
-    return acc;
+  auto kfrag = [&](const uint16_t* kb, int rb, int s) {
+    return *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
   };
-  // Softmax numerators 2^S packed as the two bf16 P operands of the block,
-  // their sum accumulated with bf16 pair dot products (the same rounded
-  // values the P.V product uses), then O^T += V^T P^T.
-  auto accumulate = [&](const uint16_t* vb, int rb, const f32x16_t& sc) {
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4_t w;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        w[m] = pack_bf2(fast_exp2(sc[8 * s2 + 2 * m]), fast_exp2(sc[8 * s2 + 2 * m + 1]));
-        lsum = dot2bf(w[m], kOnes, lsum);
-      }
-      pb[s2] = __builtin_bit_cast(bf16x8_t, w);
-    }
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            vb + (db * 32 + n) * C::VLD + 16 * (2 * rb + s2) + 8 * hf);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], oacc[db], 0, 0, 0);
-      }
-    }
+  // V^T fragment (s2, db): row db*32 + n, logical chunk 2*s2 + hf, stored at
+  // chunk (2*s2 + hf) ^ (2*db + n/16) (the swizzle of vt_swz)
+  const int vt_lane = n * C::VLD + 8 * (hf ^ (n >> 4));
+  auto vfrag = [&](const uint16_t* vb, int s2, int db) {
+    return *reinterpret_cast<const bf16x8_t*>(vb + vt_lane + db * 32 * C::VLD + 16 * ((s2 ^ db) & 3));
   };
 
-  // Tile entirely inside the band for every column of the workgroup.
-  auto compute_full = [&](int buf) {
-    const uint16_t* kb = Ks + buf * C::KBUF;
-    const uint16_t* vb = Vt + buf * C::VBUF;
-    f32x16_t sc[C::RB];
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) sc[rb] = scores(kb, rb);
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) accumulate(vb, rb, sc[rb]);
-  };
-
-  // Tile crossing the band edge: per wave and 32-key block, skip blocks the
-  // wave cannot see at all, mask blocks it sees in part.
+  // Tile crossing the band edge for this wave: 32-key blocks the wave cannot
+  // see are skipped, blocks it sees in part are masked in place.
   auto compute_edge = [&](int buf, int kt) {
     const uint16_t* kb = Ks + buf * C::KBUF;
     const uint16_t* vb = Vt + buf * C::VBUF;
-    // key of register r in block rb is kt*BN + rb*32 + 8*(r/4) + 4*hf + r%4
-    const int dl0 = t - kt * C::BN - 4 * hf;
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
       const int kb0 = kt * C::BN + rb * 32;
-      const bool none = kb0 > tw1 || tw0 - (kb0 + 31) >= p.W;
-      if (none) continue;
-      f32x16_t sc = scores(kb, rb);
+      if (kb0 > tw1 || tw0 - (kb0 + 31) >= p.W) continue;
+      f32x16_t sc[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[cb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const bf16x8_t a = kfrag(kb, rb, s);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          sc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[cb][s], sc[cb], 0, 0, 0);
+      }
       const bool all = kb0 + 31 <= tw0 && tw1 - kb0 < p.W;
       if (!all) {
+        // key of register r is kb0 + 8*(r/4) + 4*hf + r%4
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dl = dl0 - (rb * 32 + 8 * (r >> 2) + (r & 3));
-          sc[r] = ((unsigned)dl < (unsigned)p.W) ? sc[r] : -INFINITY;  // 2^-inf = 0
-        }
-      }
-      accumulate(vb, rb, sc);
-    }
-  };
-
-  // Full tile in a fixed instruction order (FullSched): compute tile `buf`
-  // while the next tile's K and V, already in registers, are rotated,
-  // normalised and transposed between the MFMAs, then written to the other
-  // buffer. LDS fragments are read three MFMAs ahead.
-  auto tile_full_sched = [&](int buf) {
-    using SCH = FullSched<D>;
-    constexpr int NS = C::KS, NP = 2 * C::DB, NM = 2 * NS + 2 * NP, LA = 8;
-    static_assert(SCH::NM == NM, "schedule length");
-    const uint16_t* kb = Ks + buf * C::KBUF;
-    const uint16_t* vb = Vt + buf * C::VBUF;
-    f32x16_t sacc[2];
-    u32x4_t pbu[2][2];
-    float kss[C::NKP], kinv[C::NKP];
-    u32x4_t kout[C::NKP];
-    u32x2_t vlo[2], vhi[2];
-    bf16x8_t fr[LA + 1];
+        for (int cb = 0; cb < CB; ++cb) {
+          const int dl0 = t[cb] - kb0 - 4 * hf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sacc[0][r] = 0.f;
-      sacc[1][r] = 0.f;
-    }
-    auto frag = [&](int m) -> bf16x8_t {
-      if (m < 2 * NS) {
-        const int rb = m / NS, s = m % NS;
-        return *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
-      }
-      const int idx = m - 2 * NS, rb = idx / NP, i = idx % NP;
-      const int db = i % C::DB, s2 = i / C::DB;
-      return *reinterpret_cast<const bf16x8_t*>(vb + (db * 32 + n) * C::VLD + 16 * (2 * rb + s2) +
-                                                8 * hf);
-    };
-    auto slice = [&](int id) {
-      if (id < 0) return;
-      if (id < 100) {
-        const int j = id >> 2, part = id & 3;
-        if (part == 0) {
-          float ss = dot2bf(kw[j][0], kw[j][0], 0.f);
-          ss = dot2bf(kw[j][1], kw[j][1], ss);
-          ss = dot2bf(kw[j][2], kw[j][2], ss);
-          kss[j] = dot2bf(kw[j][3], kw[j][3], ss);  // a rotation keeps the sum of squares
-          pin(kss[j]);
-        } else if (part == 1) {
-          kinv[j] = rsq(dpp_group_sum<C::CPR>(kss[j]) * (1.0f / D) + kEps);
-          pin(kinv[j]);
-        } else {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const int m = 2 * (part - 2) + mm;
-            const u32x4_t& tt = kt_[j][m >> 1];
-            const float xe = dot2bf(kw[j][m], tt[2 * (m & 1)], 0.f);
-            const float xo = dot2bf(kw[j][m], tt[2 * (m & 1) + 1], 0.f);
-            uint32_t w = pack_bf2(xe * kinv[j], xo * kinv[j]);
-            pin(w);
-            kout[j][m] = w;
+          for (int r = 0; r < 16; ++r) {
+            const int dl = dl0 - (8 * (r >> 2) + (r & 3));
+            sc[cb][r] = ((unsigned)dl < (unsigned)p.W) ? sc[cb][r] : -INFINITY;  // 2^-inf = 0
           }
         }
-      } else if (id < 200) {
-        const int m = id - 100;
-        const uint32_t a0 = vw[0][m], a1 = vw[1][m], a2 = vw[2][m], a3 = vw[3][m];
-        uint32_t l0 = (a0 & 0xffffu) | (a1 << 16), l1 = (a2 & 0xffffu) | (a3 << 16);
-        uint32_t h0 = (a0 >> 16) | (a1 & 0xffff0000u), h1 = (a2 >> 16) | (a3 & 0xffff0000u);
-        pin(l0);
-        pin(l1);
-        pin(h0);
-        pin(h1);
-        vlo[m] = u32x2_t{l0, l1};
-        vhi[m] = u32x2_t{h0, h1};
-      } else {
-        const int rb = (id - 200) >> 3, i = (id - 200) & 7;
-        const uint32_t w = pack_bf2(fast_exp2(sacc[rb][2 * i]), fast_exp2(sacc[rb][2 * i + 1]));
-        lsum = dot2bf(w, kOnes, lsum);
-        pbu[rb][i >> 2][i & 3] = w;
       }
-    };
+      bf16x8_t pb[CB][2];
 #pragma unroll
-    for (int m = 0; m < LA; ++m) fr[m] = frag(m);
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      if (m + LA < NM) fr[(m + LA) % (LA + 1)] = frag(m + LA);
-      const bf16x8_t a = fr[m % (LA + 1)];
-      if (m < 2 * NS) {
-        const int rb = m / NS, s = m % NS;
-        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc[rb], 0, 0, 0);
-      } else {
-        const int idx = m - 2 * NS, rb = idx / NP, i = idx % NP;
-        const int db = i % C::DB, s2 = i / C::DB;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8_t, pbu[rb][s2]), oacc[db], 0, 0, 0);
-      }
-      slice(SCH::v[m][0]);
-      slice(SCH::v[m][1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the next tile's K' and V^T into the other buffer
-    uint16_t* kbw = Ks + (buf ^ 1) * C::KBUF;
-    uint16_t* vbw = Vt + (buf ^ 1) * C::VBUF;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4_t w;
 #pragma unroll
-    for (int j = 0; j < C::NKP; ++j) st16(kbw + k_lds[j], kout[j]);
-    if (C::NMB >= C::NT || v_act) {
+          for (int m = 0; m < 4; ++m) {
+            w[m] = pack_bf2(fast_exp2(sc[cb][8 * s2 + 2 * m]), fast_exp2(sc[cb][8 * s2 + 2 * m + 1]));
+            lsum[cb] = dot2bf(w[m], kOnes, lsum[cb]);
+          }
+          pb[cb][s2] = __builtin_bit_cast(bf16x8_t, w);
+        }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        st8(vbw + v_lds + (2 * m) * C::VLD, vlo[m]);
-        st8(vbw + v_lds + (2 * m + 1) * C::VLD, vhi[m]);
-      }
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8_t a = vfrag(vb, 2 * rb + s2, db);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            oacc[db][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cb][s2], oacc[db][cb], 0, 0, 0);
+        }
     }
   };
 
-  // ---- double-buffered main loop: tile kt is computed from one LDS buffer
-  // ---- while tile kt+1 is rotated/normalised into the other and tile kt+2
-  // ---- is in flight from memory; one barrier per tile. Staging runs
-  // ---- unconditionally (past kt1 it reads zeros). The band splits into
-  // ---- leading window-edge tiles, full tiles and trailing diagonal tiles;
-  // ---- each range runs its own loop so every loop body is straight-line.
-  gload(kt0);
-  stage(0);
-  gload(kt0 + 1);
-  __syncthreads();
-  auto run = [&](int ka, int kb_, bool edge) {
-    for (int kt = ka; kt <= kb_; ++kt) {
-      const int cur = (kt - kt0) & 1;
-      if constexpr (D >= 64) {
-        if (edge) {
-          compute_edge(cur, kt);
-          stage(cur ^ 1);
+  // Tile kt of parity P (LDS buffer P) for a wave that sees all of it, in a
+  // fixed instruction order (TileSched): the loads of tile kt+2 go out into
+  // register set P first, then the MFMAs of the tile run with the softmax of
+  // its scores and the staging of tile kt+1 (register set P^1, loaded a tile
+  // ago) into LDS buffer P^1 in between.
+  auto tile_full = [&](auto Pc, int kt) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr int LA = C::LA;
+    const uint16_t* kb = Ks + P * C::KBUF;
+    const uint16_t* vb = Vt + P * C::VBUF;
+    uint16_t* kbw = Ks + (P ^ 1) * C::KBUF;
+    uint16_t* vbw = Vt + (P ^ 1) * C::VBUF;
+    gload(ic<P>{}, kt + 2);
+    f32x16_t sacc[C::RB][CB];
+    u32x4_t pbu[CB][C::PS];
+    bf16x8_t fr[LA + 1];
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rb][cb][r] = 0.f;
+    auto frag = [&](int f) -> bf16x8_t {
+      if (f < C::NKF) return kfrag(kb, f / C::KS, f % C::KS);
+      const int fv = f - C::NKF;
+      return vfrag(vb, fv / C::DB, fv % C::DB);
+    };
+    float etmp[C::RB * CB * 8][2];
+    uint32_t vtmp[C::NVB][4][4];
+    auto slice = [&](auto idc) {
+      constexpr int id0 = decltype(idc)::value;
+      constexpr bool second = id0 >= 1000;
+      constexpr int id = second ? id0 - 1000 : id0;
+      if constexpr (id0 < 0) {
+      } else if constexpr (id < 100) {
+        if constexpr (second)
+          if (C::NKP * C::NT == C::KCH || k_act[id]) st16(kbw + k_lds[id], kw[P ^ 1][id]);
+      } else if constexpr (id < 200) {
+        constexpr int j = (id - 100) >> 2, m = (id - 100) & 3;
+        if (!(C::NVB * C::NT == C::NMB || v_act[j])) return;
+        if constexpr (!second) {
+          const uint32_t a0 = vw[P ^ 1][j][0][m], a1 = vw[P ^ 1][j][1][m];
+          const uint32_t a2 = vw[P ^ 1][j][2][m], a3 = vw[P ^ 1][j][3][m];
+          vtmp[j][m][0] = (a0 & 0xffffu) | (a1 << 16);
+          vtmp[j][m][1] = (a2 & 0xffffu) | (a3 << 16);
+          vtmp[j][m][2] = (a0 >> 16) | (a1 & 0xffff0000u);
+          vtmp[j][m][3] = (a2 >> 16) | (a3 & 0xffff0000u);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) pin(vtmp[j][m][x]);
         } else {
-          tile_full_sched(cur);
+          st8(vbw + v_lds[j] + (2 * m) * C::VLD, u32x2_t{vtmp[j][m][0], vtmp[j][m][1]});
+          st8(vbw + v_lds[j] + (2 * m + 1) * C::VLD, u32x2_t{vtmp[j][m][2], vtmp[j][m][3]});
         }
       } else {
-        if (edge) compute_edge(cur, kt); else compute_full(cur);
-        stage(cur ^ 1);
+        constexpr int idx = id - 200;
+        constexpr int rb = idx / (8 * CB), cb = (idx / 8) % CB, i = idx % 8;
+        if constexpr (!second) {
+          etmp[idx][0] = fast_exp2(sacc[rb][cb][2 * i]);
+          etmp[idx][1] = fast_exp2(sacc[rb][cb][2 * i + 1]);
+          pin(etmp[idx][0]);
+          pin(etmp[idx][1]);
+        } else {
+          const uint32_t w = pack_bf2(etmp[idx][0], etmp[idx][1]);
+          lsum[cb] = dot2bf(w, kOnes, lsum[cb]);
+          pbu[cb][rb * 2 + (i >> 2)][i & 3] = w;
+        }
       }
-      gload(kt + 2);
+    };
+    static_for<LA>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      fr[f] = frag(f);
+    });
+    static_for<C::NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int f = m / CB;
+      if constexpr (m % CB == 0 && f + LA < C::NF) fr[(f + LA) % (LA + 1)] = frag(f + LA);
+      const bf16x8_t a = fr[f % (LA + 1)];
+      if constexpr (m < C::NSM) {
+        constexpr int rb = m / (C::KS * CB), s = (m / CB) % C::KS, cb = m % CB;
+        sacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[cb][s], sacc[rb][cb], 0, 0, 0);
+      } else {
+        constexpr int mm = m - C::NSM;
+        constexpr int s2 = mm / (C::DB * CB), db = (mm / CB) % C::DB, cb = mm % CB;
+        oacc[db][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, pbu[cb][s2]), oacc[db][cb], 0, 0, 0);
+      }
+      static_for<TileSched<D>::MAXS>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        slice(ic<TileSchedTab<D>::s.v[m][k]>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // Tile kt of parity P for a wave that sees part or none of it.
+  auto tile_edge = [&](auto Pc, int kt) {
+    constexpr int P = decltype(Pc)::value;
+    gload(ic<P>{}, kt + 2);
+    stage(ic<P ^ 1>{}, P ^ 1);
+    compute_edge(P, kt);
+  };
+
+  // ---- main loop: one barrier per tile. Per wave, the band splits into
+  // ---- leading window-edge tiles, full tiles (every key visible to every
+  // ---- column of the wave: scheduled path) and trailing diagonal tiles;
+  // ---- each range runs its own loop, unrolled by two over the tile parity,
+  // ---- so every loop body is straight-line. Every wave runs kt0..kt1 and
+  // ---- so meets every barrier. Staging runs unconditionally (past kt1 it
+  // ---- reads zeros).
+  stage(ic<0>{}, 0);
+  __syncthreads();
+  auto run = [&](auto body, int ka, int kb_) {
+    int kt = ka;
+    if (kt <= kb_ && ((kt - kt0) & 1)) {
+      body(ic<1>{}, kt);
+      __syncthreads();
+      ++kt;
+    }
+    for (; kt + 1 <= kb_; kt += 2) {
+      body(ic<0>{}, kt);
+      __syncthreads();
+      body(ic<1>{}, kt + 1);
+      __syncthreads();
+    }
+    if (kt <= kb_) {
+      body(ic<0>{}, kt);
       __syncthreads();
     }
   };
-  // full tiles: j0 + BN - 1 <= q0 (every key at or before every query) and
-  // q_last - j0 < W (every key inside every query's window)
-  const int ktA = max(kt0, (q_last - p.W + 1 + C::BN - 1 >= 0) ? (q_last - p.W + C::BN) / C::BN : 0);
-  const int ktB = min(kt1, (q0 + 1) / C::BN - 1);
+  // full tiles for this wave: j0 + BN - 1 <= tw0 and tw1 - j0 < W
+  const int ktA = max(kt0, tw1 - p.W + C::BN > 0 ? (tw1 - p.W + C::BN) / C::BN : 0);
+  const int ktB = min(kt1, (tw0 + 1) / C::BN - 1);
   if (ktA <= ktB) {
-    run(kt0, ktA - 1, true);
-    run(ktA, ktB, false);
-    run(ktB + 1, kt1, true);
+    run(tile_edge, kt0, ktA - 1);
+    run(tile_full, ktA, ktB);
+    run(tile_edge, ktB + 1, kt1);
   } else {
-    run(kt0, kt1, true);
+    run(tile_edge, kt0, kt1);
   }
 
   // ---- epilogue: normalise by the row sum and store bf16 (B, T, H, D)
-  lsum = sum_halves(lsum);
-  const float inv_l = 1.0f / lsum;
-  if (tvalid) {
-    uint16_t* orow = og + (((size_t)b * p.T + t) * p.H + h) * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
+  for (int cb = 0; cb < CB; ++cb) {
+    const float inv_l = 1.0f / sum_halves(lsum[cb]);
+    if (t[cb] < p.T) {
+      uint16_t* orow = og + (((size_t)b * p.T + t[cb]) * p.H + h[cb]) * D;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + 8 * r4 + 4 * hf;
-        const u32x2_t w = {pack_bf2(oacc[db][4 * r4] * inv_l, oacc[db][4 * r4 + 1] * inv_l),
-                           pack_bf2(oacc[db][4 * r4 + 2] * inv_l, oacc[db][4 * r4 + 3] * inv_l)};
-        st8(orow + d, w);
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * hf;
+          const u32x2_t w = {pack_bf2(oacc[db][cb][4 * r4] * inv_l, oacc[db][cb][4 * r4 + 1] * inv_l),
+                             pack_bf2(oacc[db][cb][4 * r4 + 2] * inv_l, oacc[db][cb][4 * r4 + 3] * inv_l)};
+          st8(orow + d, w);
+        }
       }
     }
   }
 }
 
 // =====================================================================
-// fp32 kernel: one thread per query column, fp32 FMAs, K'/V tiles in LDS.
+// fp32 kernel: one thread per query column, fp32 FMAs, k'/V tiles in LDS.
 // =====================================================================
 template <int D>
 __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
@@ -550,7 +658,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   __shared__ float Vf[BN][D + 1];
 
   const float* __restrict__ qg = (const float*)p.q;
-  const float* __restrict__ kg = (const float*)p.k;
+  const float* __restrict__ kg = (const float*)p.kp;
   const float* __restrict__ vg = (const float*)p.v;
   float* __restrict__ og = (float*)p.o;
 
@@ -594,38 +702,24 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   const size_t kv_row = (size_t)p.Hkv * D;
   for (int j0 = (k_first / BN) * BN; j0 <= q_last; j0 += BN) {
     __syncthreads();
-    // stage K' (rotated + normalised) and V: 4 threads per key row
+    // stage K' and V: 4 threads per key row
     {
       const int r = tid >> 2, part = tid & 3;
       const int key = j0 + r;
-      float y[D / 4];
-      float ss = 0.f;
       if (key < p.T) {
         const float* krow = kg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
-        const float2* trow = p.tabq + (size_t)key * (D / 2) + part * (D / 8);
+        const float* vrow = vg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          const float2 cs = trow[i];
-          const float xe = krow[2 * i], xo = krow[2 * i + 1];
-          y[2 * i] = xe * cs.x - xo * cs.y;
-          y[2 * i + 1] = xe * cs.y + xo * cs.x;
-          ss += y[2 * i] * y[2 * i] + y[2 * i + 1] * y[2 * i + 1];
+        for (int i = 0; i < D / 4; ++i) {
+          Kf[r][part * (D / 4) + i] = krow[i];
+          Vf[r][part * (D / 4) + i] = vrow[i];
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < D / 4; ++i) y[i] = 0.f;
-      }
-      ss = group_sum<4>(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
-#pragma unroll
-      for (int i = 0; i < D / 4; ++i) Kf[r][part * (D / 4) + i] = y[i] * inv;
-      if (key < p.T) {
-        const float* vrow = vg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) Vf[r][part * (D / 4) + i] = vrow[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) Vf[r][part * (D / 4) + i] = 0.f;
+        for (int i = 0; i < D / 4; ++i) {
+          Kf[r][part * (D / 4) + i] = 0.f;
+          Vf[r][part * (D / 4) + i] = 0.f;
+        }
       }
     }
     __syncthreads();
@@ -687,16 +781,15 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T,
-                           int H, int Hkv, int D, int window, const void* tab, Dtype dt,
-                           hipStream_t stream) {
+hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
+                            int H, int Hkv, int D, int window, const void* tabq, Dtype dt,
+                            hipStream_t stream) {
   FwdArgs a{};
   a.q = q;
-  a.k = k;
+  a.kp = kp;
   a.v = v;
   a.o = o;
-  a.tabq = (const float2*)tab;
-  a.tabk = (const uint2*)((const char*)tab + rope_table_half_bytes(T, D));
+  a.tabq = (const float2*)tabq;
   a.B = B;
   a.T = T;
   a.H = H;

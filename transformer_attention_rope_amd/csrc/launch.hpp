@@ -10,20 +10,20 @@ namespace nc {
 
 enum Dtype { kBF16 = 0, kF32 = 1 };
 
-// ---- RoPE cos/sin tables for positions pos_offset + t: fp32 (cos, sin) pairs
-// ---- followed by bf16 {(cos,-sin), (sin,cos)} pairs, each [T][D/2].
-size_t rope_table_half_bytes(int T, int D);
-size_t rope_table_bytes(int T, int D);
-hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
-                             hipStream_t stream);
+// ---- prefill input stage: k' = RMSNorm(RoPE(k)) in k's layout and type, and
+// ---- the fp32 (cos, sin) table [T][D/2] of positions pos_offset + t for q
+size_t attn_prep_table_bytes(int T, int D);
+hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
+                            double rope_base, int pos_offset, Dtype dt, hipStream_t stream);
 
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
                               int T, int H, int Hkv, int D, double rope_base, int pos_offset,
                               Dtype dt, hipStream_t stream);
 
-hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int T,
-                           int H, int Hkv, int D, int window, const void* tab, Dtype dt,
-                           hipStream_t stream);
+// attention from raw q (rotated/normalised in the kernel with tabq), k' and v
+hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
+                            int H, int Hkv, int D, int window, const void* tabq, Dtype dt,
+                            hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,

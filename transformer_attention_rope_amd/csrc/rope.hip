@@ -15,46 +15,132 @@
 
 namespace nc {
 
-// ---------------------------------------------------------------- table
-// Two tables over positions p = pos_offset + t, t < T, pairs i < D/2:
-//   tabq[t][i] = (cos, sin)(p * theta_i) in fp32 (for q rows, read once), and
-//   tabk[t][i] = bf16 pairs {(cos, -sin), (sin, cos)} (for k rows, read on every
-//                key-tile visit: each rotated output is one bf16 pair dot product).
-// theta_i = base^(-2i/D); the angle p*theta_i is formed in fp64 and reduced
-// modulo 2*pi with a two-constant Cody-Waite step in fp64, so cos/sin come
-// from an fp32 evaluation on [-pi, pi] whatever the position.
-__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tabq,
-                                                          uint2* __restrict__ tabk, int T,
-                                                          int half, double log2_base,
-                                                          int pos_offset) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= T * half) return;
-  const int t = idx / half, i = idx - t * half;
-  const double theta = exp2(-(double)i / (double)half * log2_base);
-  const double a = (double)(pos_offset + t) * theta;
-  const double kq = rint(a * 0.15915494309189535);        // a / (2 pi)
-  double r = fma(-kq, 6.283185307179586, a);              // 2 pi, high part
-  r = fma(-kq, 2.4492935982947064e-16, r);                // 2 pi, low part
-  float sn, cs;
-  sincosf((float)r, &sn, &cs);
-  tabq[idx] = make_float2(cs, sn);
-  tabk[idx] = make_uint2(pack_bf2(cs, -sn), pack_bf2(sn, cs));
+// ------------------------------------------------------- attention prep
+// Input stage of the prefill forward: k' = RMSNorm(RoPE(k)) for every key row,
+// written once in the layout and type of k (the attention kernel revisits each
+// key tile for several query tiles and only copies it), and the fp32
+// (cos, sin) table of every position for the rotation of q rows:
+//   tabq[t][i] = (cos, sin)(p * theta_i),  p = pos_offset + t,  i < D/2.
+// One workgroup per (position t, block of BB sequences): the D/2 angles of
+// the position are formed once, in fp64 (theta_i = base^(-2i/D) as
+// exp2(-(2i/D) log2 base), then a two-constant Cody-Waite reduction modulo
+// 2*pi), and evaluated with sincosf on [-pi, pi]; the rotation and the norm
+// of the rows run in fp32. The CPR 16-byte chunks of a row sit in
+// consecutive lanes and reduce their sum of squares across lanes.
+template <int D, typename Elem>
+__global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
+                                                         Elem* __restrict__ kp,
+                                                         float2* __restrict__ tabq, int B, int T,
+                                                         int Hkv, double log2_base, int pos_offset,
+                                                         int BB, int nbb) {
+  constexpr bool kBf = sizeof(Elem) == 2;
+  constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;      // chunks per row
+  __shared__ float2 cs[D / 2];
+
+  const int t = (int)blockIdx.x / nbb;
+  const int b0 = ((int)blockIdx.x - t * nbb) * BB;
+  const int nb = min(BB, B - b0);
+  const int tid = threadIdx.x;
+  if (tid < D / 2) {
+    const double theta = exp2(-(double)tid / (D / 2) * log2_base);
+    const double a = (double)(pos_offset + t) * theta;
+    const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
+    double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
+    r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
+    float sn, c;
+    sincosf((float)r, &sn, &c);
+    cs[tid] = make_float2(c, sn);
+    if (b0 == 0) tabq[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
+  }
+  __syncthreads();
+
+  const int total = nb * Hkv * CPR;
+  const int passes = (total + 255) / 256;
+  for (int it = 0; it < passes; ++it) {
+    const int ci = it * 256 + tid;
+    const bool ok = ci < total;
+    const int row = ok ? ci / CPR : 0;
+    const int cc = ci - row * CPR;
+    const int bb = row / Hkv, g = row - bb * Hkv;
+    const size_t off = (((size_t)(b0 + bb) * T + t) * Hkv + g) * D + (size_t)cc * EPC;
+    float x[EPC];
+    if (ok) {
+      const u32x4_t w = ld16(k + off);
+      if constexpr (kBf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          x[2 * m] = bf_lo(w[m]);
+          x[2 * m + 1] = bf_hi(w[m]);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < EPC; ++m) x[m] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < EPC / 2; ++m) {
+      const float2 r = cs[cc * (EPC / 2) + m];
+      const float xe = x[2 * m], xo = x[2 * m + 1];
+      const float ye = xe * r.x - xo * r.y;
+      const float yo = xe * r.y + xo * r.x;
+      x[2 * m] = ye;
+      x[2 * m + 1] = yo;
+      ss += ye * ye + yo * yo;
+    }
+    ss = group_sum<CPR>(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
+    if (ok) {
+      u32x4_t w;
+      if constexpr (kBf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = __float_as_uint(x[m] * inv);
+      }
+      st16(kp + off, w);
+    }
+  }
 }
 
-size_t rope_table_half_bytes(int T, int D) {
-  return (size_t)T * (size_t)(D / 2) * sizeof(float2);
-}
-size_t rope_table_bytes(int T, int D) { return 2 * rope_table_half_bytes(T, D); }
+size_t attn_prep_table_bytes(int T, int D) { return (size_t)T * (size_t)(D / 2) * sizeof(float2); }
 
-hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset,
-                             hipStream_t stream) {
-  const int half = D / 2;
-  const long long n = (long long)T * half;
-  const int grid = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, stream, (float2*)tab,
-                     (uint2*)((char*)tab + rope_table_half_bytes(T, D)), T, half,
-                     std::log2(rope_base), pos_offset);
+template <int D>
+static hipError_t attn_prep_d(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
+                              double rope_base, int pos_offset, Dtype dt, hipStream_t stream) {
+  // sequences per workgroup: about 64 rows, so the angles are amortised
+  int BB = (64 + Hkv - 1) / Hkv;
+  if (BB > B) BB = B;
+  if (BB < 1) BB = 1;
+  const int nbb = (B + BB - 1) / BB;
+  const long long nblk = (long long)T * nbb;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const double lb = std::log2(rope_base);
+  if (dt == kBF16) {
+    hipLaunchKernelGGL((attn_prep_kernel<D, uint16_t>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                       (const uint16_t*)k, (uint16_t*)kp, (float2*)tabq, B, T, Hkv, lb, pos_offset,
+                       BB, nbb);
+  } else {
+    hipLaunchKernelGGL((attn_prep_kernel<D, float>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                       (const float*)k, (float*)kp, (float2*)tabq, B, T, Hkv, lb, pos_offset, BB,
+                       nbb);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
+                            double rope_base, int pos_offset, Dtype dt, hipStream_t stream) {
+  switch (D) {
+    case 32: return attn_prep_d<32>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
+    case 64: return attn_prep_d<64>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
+    case 128: return attn_prep_d<128>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // --------------------------------------------------------- rope + qknorm
