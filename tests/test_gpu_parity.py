@@ -58,6 +58,12 @@ SMALL_BF16 = [
     (1, 512, 1, 1, 128, 512, 0),
     (1, 333, 4, 4, 128, 2048, 0),
     (1, 190, 3, 1, 64, 33, 77),
+    # one query head per K/V head and windows that are multiples of 64:
+    # window-edge and diagonal tiles take the scheduled path
+    (1, 700, 2, 2, 128, 128, 0),
+    (2, 513, 4, 4, 64, 256, 3),
+    (1, 300, 1, 1, 32, 192, 0),
+    (1, 1100, 1, 1, 128, 64, 0),
 ]
 
 

@@ -107,6 +107,7 @@ struct BfCfg {
   static constexpr int NKP = (KCH + NT - 1) / NT;  // K chunks per thread
   static constexpr int NMB = (BN / 4) * CPR;       // 4-key x 8-dim V micro-blocks per tile
   static constexpr int NVB = (NMB + NT - 1) / NT;  // V micro-blocks per thread
+  static constexpr int QLD = D + 8;        // LDS row stride of staged q / o rows (bf16)
   static constexpr int KBUF = BN * KLD;    // bf16 elements per K buffer
   static constexpr int VBUF = D * VLD;     // bf16 elements per V^T buffer
   // A tile is NM MFMAs: the score MFMAs (rb, s, cb) for m < NSM, then the
@@ -117,7 +118,6 @@ struct BfCfg {
   static constexpr int NM = NSM + NPM;
   static constexpr int NKF = RB * KS;
   static constexpr int NF = NKF + PS * DB;
-  static constexpr int LA = 6;             // LDS fragments read ahead of their MFMA
 };
 
 // Position of key kk (0..BN-1) inside a V^T row. The score accumulator of
@@ -138,27 +138,80 @@ __device__ __forceinline__ int vt_swz(int d, int col) {
   return ((((col >> 3) ^ (d >> 4)) & 7) << 3) | (col & 7);
 }
 
-// Instruction order of a tile in which every key is visible to every column
-// of the wave. After MFMA m come the vector-work entries v[m][..]. Each
-// slice has a first half (id) and a second half (id + 1000) issued one MFMA
-// later, so the instructions between two MFMAs never wait on each other
-// (a wave issues in order; a stalled instruction would hold the next MFMA):
+// Kinds of tiles with a fixed instruction order, for a wave whose 64 columns
+// are 64 consecutive positions starting on a tile boundary:
+//   kFull  every key visible to every column;
+//   kDiag  the tile holding the wave's own positions (causal diagonal): the
+//          block of keys 32..63 x queries 0..31 is skipped, the two blocks on
+//          the diagonal are masked (key <= query);
+//   kWin   the first tile of the window (keys q - W ..): the block of keys
+//          0..31 x queries 32..63 is skipped, the diagonal blocks are masked
+//          (key > query - W).
+enum TileKind { kFull = 0, kDiag = 1, kWin = 2 };
+
+// Instruction order of such a tile, as a list of MFMAs: the score MFMAs
+// (rb, s, cb) of the present 32x32 blocks, then their P.V MFMAs (s2, db, cb).
+// Before MFMA m the K/V fragments fl[m][..] are read from LDS (each about
+// LAM MFMAs before its first use); after MFMA m come the vector-work entries
+// v[m][..]. Each slice has a first half (id) and a second half (id + 1000)
+// issued one MFMA later, so the instructions between two MFMAs never wait on
+// each other (a wave issues in order; a stalled instruction would hold the
+// next MFMA):
 //   200+8(rb*CB+cb)+i   2^S of score registers 2i, 2i+1 of block (rb, cb);
-//                then packing into the P operand and the row-sum update
+//                then packing into the P operand (masked on kDiag/kWin
+//                diagonal blocks) and the row-sum update
 //   100+4vb+m    transposition of the next tile's V micro-block vb, dims
-//                pair m; then its two V^T rows into LDS
-//   j            nothing; then the next tile's K chunk j into LDS
+//                pair m; then its two V^T rows into LDS      (if STAGE)
+//   j            nothing; then the next tile's K chunk j into LDS (if STAGE)
 // Slices start in that order, spread evenly over the MFMAs. An exponential
 // starts two MFMAs after the last score MFMA of its block, and a P.V MFMA
 // comes after the second halves of the four slices that build its P operand.
-template <int D>
+template <int D, int KIND, bool STAGE>
 struct TileSched {
   using C = BfCfg<D>;
-  static constexpr int MAXS = 24;
+  static constexpr int MAXS = 24, MAXL = 16, LAM = 12;
+  static constexpr bool present(int rb, int cb) {
+    return !((KIND == kDiag && rb == 1 && cb == 0) || (KIND == kWin && rb == 0 && cb == 1));
+  }
+  short mt[C::NM], ma[C::NM], mb[C::NM], mc[C::NM], mf[C::NM];
+  short fl[C::NM][MAXL];
   short v[C::NM][MAXS];
-  int ok;
-  int nslices;
-  constexpr TileSched() : v{}, ok(1), nslices(0) {
+  int nm, nsm, ok, nslices;
+  constexpr TileSched()
+      : mt{}, ma{}, mb{}, mc{}, mf{}, fl{}, v{}, nm(0), nsm(0), ok(1), nslices(0) {
+    for (int rb = 0; rb < C::RB; ++rb)
+      for (int s = 0; s < C::KS; ++s)
+        for (int cb = 0; cb < C::CB; ++cb)
+          if (present(rb, cb)) {
+            mt[nm] = 0; ma[nm] = (short)rb; mb[nm] = (short)s; mc[nm] = (short)cb;
+            mf[nm] = (short)(rb * C::KS + s);
+            ++nm;
+          }
+    nsm = nm;
+    for (int s2 = 0; s2 < C::PS; ++s2)
+      for (int db = 0; db < C::DB; ++db)
+        for (int cb = 0; cb < C::CB; ++cb)
+          if (present(s2 / 2, cb)) {
+            mt[nm] = 1; ma[nm] = (short)s2; mb[nm] = (short)db; mc[nm] = (short)cb;
+            mf[nm] = (short)(C::NKF + s2 * C::DB + db);
+            ++nm;
+          }
+    for (int m = 0; m < C::NM; ++m) {
+      for (int k = 0; k < MAXL; ++k) fl[m][k] = -1;
+      for (int k = 0; k < MAXS; ++k) v[m][k] = -1;
+    }
+    int nfl[C::NM] = {};
+    for (int f = 0; f < C::NF; ++f) {
+      int first = -1;
+      for (int m = 0; m < nm && first < 0; ++m)
+        if (mf[m] == f) first = m;
+      if (first < 0) continue;
+      const int at = first > LAM ? first - LAM : 0;
+      if (nfl[at] < MAXL) fl[at][nfl[at]++] = (short)f; else ok = 0;
+    }
+    int last[2][2] = {{-1, -1}, {-1, -1}};
+    for (int m = 0; m < nsm; ++m) last[ma[m]][mc[m]] = m;
+
     short q[160] = {};
     short early[160] = {};
     short start[160] = {};
@@ -166,26 +219,25 @@ struct TileSched {
     int nq = 0;
     for (int s2 = 0; s2 < C::PS; ++s2)
       for (int cb = 0; cb < C::CB; ++cb)
-        for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
-          const int rb = s2 / 2;
-          early[nq] = (short)((rb + 1) * C::KS * C::CB + 1);
-          q[nq++] = (short)(200 + 8 * (rb * C::CB + cb) + i);
-        }
-    for (int vb = 0; vb < C::NVB; ++vb)
-      for (int m = 0; m < 4; ++m) q[nq++] = (short)(100 + 4 * vb + m);
-    for (int j = 0; j < C::NKP; ++j) q[nq++] = (short)j;
+        if (present(s2 / 2, cb))
+          for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
+            const int rb = s2 / 2;
+            early[nq] = (short)(last[rb][cb] + 2);
+            q[nq++] = (short)(200 + 8 * (rb * C::CB + cb) + i);
+          }
+    if (STAGE) {
+      for (int vb = 0; vb < C::NVB; ++vb)
+        for (int m = 0; m < 4; ++m) q[nq++] = (short)(100 + 4 * vb + m);
+      for (int j = 0; j < C::NKP; ++j) q[nq++] = (short)j;
+    }
     nslices = nq;
-    for (int m = 0; m < C::NM; ++m)
-      for (int k = 0; k < MAXS; ++k) v[m][k] = -1;
     int cnt[C::NM] = {};
     auto put = [&](int m, int id) {
       if (cnt[m] < MAXS) v[m][cnt[m]++] = (short)id; else ok = 0;
     };
-    // slices started per MFMA: about one when the tile has more MFMAs than slices
-    const int per_slot = (nq + C::NM - 1) / C::NM;
+    const int per_slot = (nq + nm - 1) / nm;
     int head = 0;
-    for (int m = 0; m < C::NM; ++m) {
-      // second halves of the slices started after MFMA m-1
+    for (int m = 0; m < nm; ++m) {
       for (int x = 0; x < nq; ++x)
         if (done[x] && start[x] == m - 1) put(m, q[x] + 1000);
       int started = 0;
@@ -196,35 +248,31 @@ struct TileSched {
         ++started;
       };
       // the P operand of MFMA m+2 must be complete after slot m+1
-      if (m + 2 < C::NM && m + 2 >= C::NSM) {
-        const int mm = m + 2 - C::NSM;
-        const int s2 = mm / (C::DB * C::CB), cb = mm % C::CB, rb = s2 / 2;
+      if (m + 2 < nm && mt[m + 2] == 1) {
+        const int s2 = ma[m + 2], cb = mc[m + 2], rb = s2 / 2;
         for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
           const short id = (short)(200 + 8 * (rb * C::CB + cb) + i);
           for (int x = 0; x < nq; ++x)
             if (q[x] == id && !done[x]) {
-              // everything queued before it goes first (keeps the queue order)
               for (int y = head; y <= x; ++y)
                 if (!done[y]) begin(y);
             }
         }
       }
       while (head < nq && done[head]) ++head;
-      const bool last = m == C::NM - 1;
-      while ((started < per_slot || last) && head < nq && early[head] <= m) {
+      const bool lastm = m == nm - 1;
+      while ((started < per_slot || lastm) && head < nq && early[head] <= m) {
         begin(head);
         while (head < nq && done[head]) ++head;
       }
-      if (last)  // slices started after the last MFMA finish right away
+      if (lastm)
         for (int x = 0; x < nq; ++x)
           if (done[x] && start[x] == m) put(m, q[x] + 1000);
     }
     for (int x = 0; x < nq; ++x)
       if (!done[x]) ok = 0;
-    // every P.V MFMA comes after the second halves of its exponentials
-    for (int m = C::NSM; m < C::NM; ++m) {
-      const int mm = m - C::NSM;
-      const int s2 = mm / (C::DB * C::CB), cb = mm % C::CB, rb = s2 / 2;
+    for (int m = nsm; m < nm; ++m) {
+      const int s2 = ma[m], cb = mc[m], rb = s2 / 2;
       for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
         const int id = 1000 + 200 + 8 * (rb * C::CB + cb) + i;
         bool seen = false;
@@ -236,9 +284,9 @@ struct TileSched {
     }
   }
 };
-template <int D>
+template <int D, int KIND, bool STAGE>
 struct TileSchedTab {
-  static constexpr TileSched<D> s{};
+  static constexpr TileSched<D, KIND, STAGE> s{};
   static_assert(s.ok, "tile schedule");
 };
 
@@ -246,8 +294,15 @@ template <int D>
 __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   using C = BfCfg<D>;
   constexpr int CB = C::CB;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * C::VBUF];
+  // K and V^T double buffers; before the first tile and after the last one
+  // the same memory holds each wave's q rows and output rows (QLD-element
+  // rows, 64 per wave) on their way between row-major global memory and the
+  // MFMA register layouts.
+  constexpr int kSmem = 2 * (C::KBUF + C::VBUF) > 4 * 64 * C::QLD ? 2 * (C::KBUF + C::VBUF)
+                                                                   : 4 * 64 * C::QLD;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+  uint16_t* const Ks = smem;
+  uint16_t* const Vt = smem + 2 * C::KBUF;
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
   uint16_t* __restrict__ og = (uint16_t*)p.o;
@@ -353,10 +408,6 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       }
   };
 
-  // the first two tiles go out before the query prologue
-  gload(ic<0>{}, kt0);
-  gload(ic<1>{}, kt0 + 1);
-
   // ---- this lane's query columns, one per 32-column block
   int t[CB], h[CB];
 #pragma unroll
@@ -366,42 +417,71 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     h[cb] = grp * hpw + (col & (hpw - 1));
   }
 
-  // ---- Q: load, RoPE (fp32 table), RMSNorm, fold log2(e)/sqrt(D), pack as
-  // ---- the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7)
+  // ---- Q: the wave's 64 q rows are read row-major (CPR lanes per row, so
+  // ---- every load covers whole rows), rotated with the fp32 table, RMS-
+  // ---- normalised (sum over the row's lanes), scaled by log2(e)/sqrt(D) and
+  // ---- rounded to bf16 there, written to the wave's LDS rows, and read back
+  // ---- as the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7). The
+  // ---- first two key tiles go out after the q rows.
+  constexpr int RPI = 64 / C::CPR;  // q rows per load
+  uint16_t* const qs = smem + wave * 64 * C::QLD;
+  // row r of the wave: column wave*64 + r
+  auto col_row = [&](int r, int& tr, int& hr) {
+    const int col = wave * 64 + r;
+    tr = q0 + (col >> p.hpw_log2);
+    hr = grp * hpw + (col & (hpw - 1));
+  };
+  const int qc = lane % C::CPR, qr0 = lane / C::CPR;
   bf16x8_t bq[CB][C::KS];
+  {
+    constexpr int NB = C::CPR >= 8 ? 2 : 1;  // batches of rows (register pressure)
+    constexpr int PB = C::CPR / NB;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int tc = t[cb] < p.T ? t[cb] : p.T - 1;
-    const uint16_t* qrow = qg + (((size_t)b * p.T + tc) * p.H + h[cb]) * D;
-    const float2* trow = p.tabq + (size_t)tc * (D / 2);
-    float x[C::KS][8];
-    float ss = 0.f;
+    for (int bt = 0; bt < NB; ++bt) {
+      u32x4_t qw[PB];
+      f32x4_t tq[PB][2];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const int d0 = 16 * s + 8 * hf;
-      const u32x4_t w = ld16(qrow + d0);
-      const f32x4_t c01 = *reinterpret_cast<const f32x4_t*>(trow + d0 / 2);
-      const f32x4_t c23 = *reinterpret_cast<const f32x4_t*>(trow + d0 / 2 + 2);
-      const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+      for (int ii = 0; ii < PB; ++ii) {
+        const int i = bt * PB + ii;
+        int tr, hr;
+        col_row(i * RPI + qr0, tr, hr);
+        const int tc = tr < p.T ? tr : p.T - 1;
+        qw[ii] = ld16(qg + (((size_t)b * p.T + tc) * p.H + hr) * D + qc * 8);
+        const float2* trow = p.tabq + (size_t)tc * (D / 2) + qc * 4;
+        tq[ii][0] = *reinterpret_cast<const f32x4_t*>(trow);
+        tq[ii][1] = *reinterpret_cast<const f32x4_t*>(trow + 2);
+      }
+      if (bt == 0) {
+        gload(ic<0>{}, kt0);
+        gload(ic<1>{}, kt0 + 1);
+      }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float xe = bf_lo(w[m]), xo = bf_hi(w[m]);
-        const float c = cs[2 * m], sn = cs[2 * m + 1];
-        const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
-        x[s][2 * m] = ye;
-        x[s][2 * m + 1] = yo;
-        ss += ye * ye + yo * yo;
+      for (int ii = 0; ii < PB; ++ii) {
+        const int i = bt * PB + ii;
+        float x[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float xe = bf_lo(qw[ii][m]), xo = bf_hi(qw[ii][m]);
+          const float c = tq[ii][m >> 1][2 * (m & 1)], sn = tq[ii][m >> 1][2 * (m & 1) + 1];
+          const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+          x[2 * m] = ye;
+          x[2 * m + 1] = yo;
+          ss += ye * ye + yo * yo;
+        }
+        ss = dpp_group_sum<C::CPR>(ss);
+        const float sc = p.qscale * rsq(ss * (1.0f / D) + kEps);
+        u32x4_t w;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * sc, x[2 * m + 1] * sc);
+        st16(qs + (i * RPI + qr0) * C::QLD + qc * 8, w);
       }
     }
-    ss = sum_halves(ss);
-    const float sc = p.qscale * rsq(ss * (1.0f / D) + kEps);
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4_t w;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[s][2 * m] * sc, x[s][2 * m + 1] * sc);
-      bq[cb][s] = __builtin_bit_cast(bf16x8_t, w);
-    }
+      for (int s = 0; s < C::KS; ++s)
+        bq[cb][s] = *reinterpret_cast<const bf16x8_t*>(qs + (cb * 32 + n) * C::QLD + 16 * s + 8 * hf);
   }
 
   f32x16_t oacc[C::DB][CB];
@@ -489,22 +569,38 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     }
   };
 
-  // Tile kt of parity P (LDS buffer P) for a wave that sees all of it, in a
-  // fixed instruction order (TileSched): the loads of tile kt+2 go out into
-  // register set P first, then the MFMAs of the tile run with the softmax of
-  // its scores and the staging of tile kt+1 (register set P^1, loaded a tile
+  // Diagonal-block masks of kDiag tiles: pair i of a score block holds keys
+  // c(2i), c(2i+1) with c(r) = 8*(r/4) + r%4 + 4*hf against query n; a key is
+  // at or before the query iff c(r) <= n - 4*hf. One bf16 half per key.
+  uint32_t dmask[8];
+  {
+    const int e = n - 4 * hf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c0 = 8 * ((2 * i) >> 2) + ((2 * i) & 3), c1 = 8 * ((2 * i + 1) >> 2) + ((2 * i + 1) & 3);
+      dmask[i] = (c0 <= e ? 0x0000ffffu : 0u) | (c1 <= e ? 0xffff0000u : 0u);
+    }
+  }
+
+  // Tile kt of parity P (LDS buffer P) of kind KIND, in a fixed instruction
+  // order (TileSched): the loads of tile kt+2 go out into register set P
+  // first, then the MFMAs of the tile run with the softmax of its scores and
+  // (if STAGE) the staging of tile kt+1 (register set P^1, loaded a tile
   // ago) into LDS buffer P^1 in between.
-  auto tile_full = [&](auto Pc, int kt) {
+  auto tile_sched = [&](auto Kc, auto Sc, auto Pc, int kt) {
+    constexpr int KIND = decltype(Kc)::value;
+    constexpr bool STAGE = decltype(Sc)::value != 0;
     constexpr int P = decltype(Pc)::value;
-    constexpr int LA = C::LA;
+    using SCH = TileSchedTab<D, KIND, STAGE>;
+    using TS = TileSched<D, KIND, STAGE>;
     const uint16_t* kb = Ks + P * C::KBUF;
     const uint16_t* vb = Vt + P * C::VBUF;
     uint16_t* kbw = Ks + (P ^ 1) * C::KBUF;
     uint16_t* vbw = Vt + (P ^ 1) * C::VBUF;
-    gload(ic<P>{}, kt + 2);
+    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
     f32x16_t sacc[C::RB][CB];
     u32x4_t pbu[CB][C::PS];
-    bf16x8_t fr[LA + 1];
+    bf16x8_t fr[C::NF];
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
@@ -551,52 +647,55 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
           pin(etmp[idx][0]);
           pin(etmp[idx][1]);
         } else {
-          const uint32_t w = pack_bf2(etmp[idx][0], etmp[idx][1]);
+          uint32_t w = pack_bf2(etmp[idx][0], etmp[idx][1]);
+          if constexpr (KIND == kDiag && rb == cb) w &= dmask[i];
+          if constexpr (KIND == kWin && rb == cb) w &= ~dmask[i];
           lsum[cb] = dot2bf(w, kOnes, lsum[cb]);
           pbu[cb][rb * 2 + (i >> 2)][i & 3] = w;
         }
       }
     };
-    static_for<LA>([&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      fr[f] = frag(f);
-    });
-    static_for<C::NM>([&](auto mc) {
+    static_for<SCH::s.nm>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int f = m / CB;
-      if constexpr (m % CB == 0 && f + LA < C::NF) fr[(f + LA) % (LA + 1)] = frag(f + LA);
-      const bf16x8_t a = fr[f % (LA + 1)];
-      if constexpr (m < C::NSM) {
-        constexpr int rb = m / (C::KS * CB), s = (m / CB) % C::KS, cb = m % CB;
-        sacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[cb][s], sacc[rb][cb], 0, 0, 0);
+      static_for<TS::MAXL>([&](auto lc) {
+        constexpr int f = SCH::s.fl[m][decltype(lc)::value];
+        if constexpr (f >= 0) fr[f] = frag(f);
+      });
+      constexpr int f = SCH::s.mf[m];
+      constexpr int ma = SCH::s.ma[m], mb = SCH::s.mb[m], mcb = SCH::s.mc[m];
+      if constexpr (SCH::s.mt[m] == 0) {
+        sacc[ma][mcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], bq[mcb][mb], sacc[ma][mcb], 0, 0, 0);
       } else {
-        constexpr int mm = m - C::NSM;
-        constexpr int s2 = mm / (C::DB * CB), db = (mm / CB) % C::DB, cb = mm % CB;
-        oacc[db][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8_t, pbu[cb][s2]), oacc[db][cb], 0, 0, 0);
+        oacc[mb][mcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fr[f], __builtin_bit_cast(bf16x8_t, pbu[mcb][ma]), oacc[mb][mcb], 0, 0, 0);
       }
-      static_for<TileSched<D>::MAXS>([&](auto kc) {
+      static_for<TS::MAXS>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        slice(ic<TileSchedTab<D>::s.v[m][k]>{});
+        slice(ic<SCH::s.v[m][k]>{});
       });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // Tile kt of parity P for a wave that sees part or none of it.
+  auto tile_full = [&](auto Pc, int kt) { tile_sched(ic<kFull>{}, ic<1>{}, Pc, kt); };
+  // Tile kt of parity P for a wave that sees part of it (generic path).
   auto tile_edge = [&](auto Pc, int kt) {
     constexpr int P = decltype(Pc)::value;
-    gload(ic<P>{}, kt + 2);
-    stage(ic<P ^ 1>{}, P ^ 1);
+    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
+    if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
     compute_edge(P, kt);
   };
+  // Tile kt of parity P that this wave does not see: staging only.
+  auto tile_empty = [&](auto Pc, int kt) {
+    constexpr int P = decltype(Pc)::value;
+    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
+    if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
+  };
 
-  // ---- main loop: one barrier per tile. Per wave, the band splits into
-  // ---- leading window-edge tiles, full tiles (every key visible to every
-  // ---- column of the wave: scheduled path) and trailing diagonal tiles;
-  // ---- each range runs its own loop, unrolled by two over the tile parity,
-  // ---- so every loop body is straight-line. Every wave runs kt0..kt1 and
-  // ---- so meets every barrier. Staging runs unconditionally (past kt1 it
-  // ---- reads zeros).
+  // ---- main loop: one barrier per tile; every wave runs kt0..kt1 and so
+  // ---- meets every barrier. Each range of tiles of one kind runs its own
+  // ---- loop, unrolled by two over the tile parity, so every loop body is
+  // ---- straight-line.
+  __syncthreads();  // every wave has read its q rows back
   stage(ic<0>{}, 0);
   __syncthreads();
   auto run = [&](auto body, int ka, int kb_) {
@@ -617,23 +716,49 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       __syncthreads();
     }
   };
-  // full tiles for this wave: j0 + BN - 1 <= tw0 and tw1 - j0 < W
-  const int ktA = max(kt0, tw1 - p.W + C::BN > 0 ? (tw1 - p.W + C::BN) / C::BN : 0);
-  const int ktB = min(kt1, (tw0 + 1) / C::BN - 1);
-  if (ktA <= ktB) {
-    run(tile_edge, kt0, ktA - 1);
-    run(tile_full, ktA, ktB);
-    run(tile_edge, ktB + 1, kt1);
+  auto one = [&](auto body, int kt) {
+    if ((kt - kt0) & 1) body(ic<1>{}, kt); else body(ic<0>{}, kt);
+    __syncthreads();
+  };
+  // Waves whose 64 columns are 64 consecutive positions on a tile boundary,
+  // with a window that is a multiple of the tile or wider than the wave's
+  // reach, see: nothing, then (if the window bites) one kWin tile, full
+  // tiles, one kDiag tile (its own positions), then nothing.
+  const bool aligned = hpw == 1 && p.W >= C::BN && tw0 <= q_last &&
+                       (p.W % C::BN == 0 || p.W >= tw0 + C::BN);
+  if (aligned) {
+    const int ktD = tw0 / C::BN;
+    const int ktW = tw0 - p.W >= 0 ? (tw0 - p.W) / C::BN : -1;
+    const int kf0 = ktW >= 0 ? ktW + 1 : kt0;
+    run(tile_empty, kt0, kf0 - 1 - (ktW >= 0 ? 1 : 0));
+    if (ktW >= 0) one([&](auto Pc, int kt) { tile_sched(ic<kWin>{}, ic<1>{}, Pc, kt); }, ktW);
+    run(tile_full, kf0, ktD - 1);
+    if (ktD < kt1)
+      one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<1>{}, Pc, kt); }, ktD);
+    else
+      one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<0>{}, Pc, kt); }, ktD);
+    run(tile_empty, ktD + 1, kt1);
   } else {
-    run(tile_edge, kt0, kt1);
+    // full tiles for this wave: j0 + BN - 1 <= tw0 and tw1 - j0 < W
+    const int ktA = max(kt0, tw1 - p.W + C::BN > 0 ? (tw1 - p.W + C::BN) / C::BN : 0);
+    const int ktB = min(kt1, (tw0 + 1) / C::BN - 1);
+    if (ktA <= ktB) {
+      run(tile_edge, kt0, ktA - 1);
+      run(tile_full, ktA, ktB);
+      run(tile_edge, ktB + 1, kt1);
+    } else {
+      run(tile_edge, kt0, kt1);
+    }
   }
 
-  // ---- epilogue: normalise by the row sum and store bf16 (B, T, H, D)
+  // ---- epilogue: normalise by the row sum, write the wave's output rows to
+  // ---- its LDS rows (the last barrier of the tile loop freed the buffers),
+  // ---- and store them row-major, CPR lanes per row, bf16 (B, T, H, D)
+  {
+    uint16_t* const os = qs;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const float inv_l = 1.0f / sum_halves(lsum[cb]);
-    if (t[cb] < p.T) {
-      uint16_t* orow = og + (((size_t)b * p.T + t[cb]) * p.H + h[cb]) * D;
+    for (int cb = 0; cb < CB; ++cb) {
+      const float inv_l = 1.0f / sum_halves(lsum[cb]);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -641,9 +766,17 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
           const int d = db * 32 + 8 * r4 + 4 * hf;
           const u32x2_t w = {pack_bf2(oacc[db][cb][4 * r4] * inv_l, oacc[db][cb][4 * r4 + 1] * inv_l),
                              pack_bf2(oacc[db][cb][4 * r4 + 2] * inv_l, oacc[db][cb][4 * r4 + 3] * inv_l)};
-          st8(orow + d, w);
+          st8(os + (cb * 32 + n) * C::QLD + d, w);
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPR; ++i) {
+      const int r = i * RPI + qr0;
+      int tr, hr;
+      col_row(r, tr, hr);
+      const u32x4_t w = ld16(os + r * C::QLD + qc * 8);
+      if (tr < p.T) st16(og + (((size_t)b * p.T + tr) * p.H + hr) * D + qc * 8, w);
     }
   }
 }
