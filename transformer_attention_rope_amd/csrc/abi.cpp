@@ -124,7 +124,7 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
 namespace {
 size_t prep_table_bytes(int T, int D) { return round_up(nc::attn_prep_table_bytes(T, D)); }
 size_t prep_k_bytes(int B, int T, int Hkv, int D, nc_dtype dt) {
-  return round_up((size_t)B * T * Hkv * D * (dt == NC_F32 ? 4 : 2));
+  return round_up(nc::attn_prep_k_bytes(B, T, Hkv, D, dt == NC_F32 ? nc::kF32 : nc::kBF16));
 }
 nc_status check_fwd_sizes(int B, int T, int H, int Hkv, int D, nc_dtype dt) {
   nc_status s = check_common(B, T, H, Hkv, D, dt, "T");

@@ -100,15 +100,15 @@ struct BfCfg {
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
   static constexpr int RB = BN / 32;       // 32-key blocks per tile
   static constexpr int PS = BN / 16;       // MFMA k-steps of V^T P^T
-  static constexpr int KLD = D + 8;        // LDS row stride of K (bf16), +16 B against bank conflicts
   static constexpr int VLD = BN + 8;       // LDS row stride of V^T (bf16)
-  static constexpr int CPR = D / 8;        // 16-byte chunks per K or V row
-  static constexpr int KCH = BN * CPR;     // K chunks per tile
-  static constexpr int NKP = (KCH + NT - 1) / NT;  // K chunks per thread
+  static constexpr int CPR = D / 8;        // 16-byte chunks per q, o or V row
+  static constexpr int KCP = BN * D * 2 / 1024;    // 1 KB copies per K tile (64*16 bytes each)
+  static constexpr int NKD = (KCP + NW - 1) / NW;  // K copies per wave per tile
+  static constexpr int KSW = 128 / D;      // K rows per 64-bank span (swizzle period)
   static constexpr int NMB = (BN / 4) * CPR;       // 4-key x 8-dim V micro-blocks per tile
   static constexpr int NVB = (NMB + NT - 1) / NT;  // V micro-blocks per thread
   static constexpr int QLD = D + 8;        // LDS row stride of staged q / o rows (bf16)
-  static constexpr int KBUF = BN * KLD;    // bf16 elements per K buffer
+  static constexpr int KBUF = BN * D;      // bf16 elements per K buffer (swizzled rows)
   static constexpr int VBUF = D * VLD;     // bf16 elements per V^T buffer
   // A tile is NM MFMAs: the score MFMAs (rb, s, cb) for m < NSM, then the
   // P.V MFMAs (s2, db, cb). Fragment f (K fragments (rb, s) first, then V
@@ -162,14 +162,13 @@ enum TileKind { kFull = 0, kDiag = 1, kWin = 2 };
 //                diagonal blocks) and the row-sum update
 //   100+4vb+m    transposition of the next tile's V micro-block vb, dims
 //                pair m; then its two V^T rows into LDS      (if STAGE)
-//   j            nothing; then the next tile's K chunk j into LDS (if STAGE)
 // Slices start in that order, spread evenly over the MFMAs. An exponential
 // starts two MFMAs after the last score MFMA of its block, and a P.V MFMA
 // comes after the second halves of the four slices that build its P operand.
 template <int D, int KIND, bool STAGE>
 struct TileSched {
   using C = BfCfg<D>;
-  static constexpr int MAXS = 24, MAXL = 16, LAM = 12;
+  static constexpr int MAXS = 24, MAXL = 16, LAM = 16;
   static constexpr bool present(int rb, int cb) {
     return !((KIND == kDiag && rb == 1 && cb == 0) || (KIND == kWin && rb == 0 && cb == 1));
   }
@@ -225,11 +224,9 @@ struct TileSched {
             early[nq] = (short)(last[rb][cb] + 2);
             q[nq++] = (short)(200 + 8 * (rb * C::CB + cb) + i);
           }
-    if (STAGE) {
+    if (STAGE)
       for (int vb = 0; vb < C::NVB; ++vb)
         for (int m = 0; m < 4; ++m) q[nq++] = (short)(100 + 4 * vb + m);
-      for (int j = 0; j < C::NKP; ++j) q[nq++] = (short)j;
-    }
     nslices = nq;
     int cnt[C::NM] = {};
     auto put = [&](int m, int id) {
@@ -294,13 +291,13 @@ template <int D>
 __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   using C = BfCfg<D>;
   constexpr int CB = C::CB;
-  // K and V^T double buffers; before the first tile and after the last one
-  // the same memory holds each wave's q rows and output rows (QLD-element
-  // rows, 64 per wave) on their way between row-major global memory and the
-  // MFMA register layouts.
-  constexpr int kSmem = 2 * (C::KBUF + C::VBUF) > 4 * 64 * C::QLD ? 2 * (C::KBUF + C::VBUF)
-                                                                   : 4 * 64 * C::QLD;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+  // K and V^T double buffers. Before the first tile and after the last one
+  // the V^T part (enlarged to fit) holds each wave's q rows and output rows
+  // (QLD-element rows, 64 per wave) on their way between row-major global
+  // memory and the MFMA register layouts; the K part is only written by the
+  // tile copies, so the first one can start at once.
+  constexpr int kVpart = 2 * C::VBUF > 4 * 64 * C::QLD ? 2 * C::VBUF : 4 * 64 * C::QLD;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::KBUF + kVpart];
   uint16_t* const Ks = smem;
   uint16_t* const Vt = smem + 2 * C::KBUF;
 
@@ -330,18 +327,18 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
   const size_t kv_base = ((size_t)b * p.T * p.Hkv + g) * D;
   const uint32_t kv_records = (uint32_t)(((size_t)p.T * p.Hkv - g) * D * 2);
-  const char* kseq = (const char*)((const uint16_t*)p.kp + kv_base);
   const char* vseq = (const char*)((const uint16_t*)p.v + kv_base);
-
-  uint32_t k_voff[C::NKP], k_lds[C::NKP];
-  bool k_act[C::NKP];
+  const char* kseq = (const char*)((const uint16_t*)p.kp + kv_base);
+  // the K row that copy j of this wave's lane fills in a tile, and the chunk
+  // of it: LDS row r holds chunk c of global row r at position
+  // c ^ ((r / KSW) % CPR), so the row-strided fragment reads spread over all
+  // banks while every copy still reads whole rows
+  uint32_t k_voff[C::NKD];
 #pragma unroll
-  for (int j = 0; j < C::NKP; ++j) {
-    const int idx = tid + C::NT * j;
-    const int kr = idx / C::CPR, kc = idx % C::CPR;
-    k_act[j] = idx < C::KCH;
-    k_voff[j] = (uint32_t)kr * row_bytes + kc * 16;
-    k_lds[j] = kr * C::KLD + kc * 8;
+  for (int j = 0; j < C::NKD; ++j) {
+    const int slot = (wave * C::NKD + j) * 64 + lane;  // 16-byte slot in the tile
+    const int r = slot / C::CPR, c = slot % C::CPR;
+    k_voff[j] = (uint32_t)r * row_bytes + (uint32_t)((c ^ ((r / C::KSW) % C::CPR)) * 16);
   }
   // V micro-block mb: dims 8*(mb % CPR) .. +7 of the 4 keys of key group
   // vgp, so a wave's load of one key slot covers whole rows. Key groups are
@@ -360,21 +357,16 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     v_lds[j] = (8 * vd) * C::VLD + vt_swz(8 * vd, vt_pos(4 * vgp));
   }
 
-  u32x4_t kw[2][C::NKP];
   u32x4_t vw[2][C::NVB][4];
 
-  // Tile kt into register set S. Resources rebased on the tile's first key:
-  // rows past token T (and only those) fall beyond num_records and read as
-  // zero; a tile past the sequence gets an empty range.
+  // V rows of tile kt into register set S. The resource is rebased on the
+  // tile's first key: rows past token T (and only those) fall beyond
+  // num_records and read as zero; a tile past the sequence gets an empty range.
   auto gload = [&](auto Sc, int kt) {
     constexpr int S = decltype(Sc)::value;
     const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
     const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq + so, nk);
-#pragma unroll
-    for (int j = 0; j < C::NKP; ++j)
-      if (C::NKP * C::NT == C::KCH || k_act[j]) kw[S][j] = bload16(rk, k_voff[j], 0);
 #pragma unroll
     for (int j = 0; j < C::NVB; ++j)
       if (C::NVB * C::NT == C::NMB || v_act[j]) {
@@ -392,14 +384,25 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     st8(vb + v_lds[j] + (2 * m) * C::VLD, lo);
     st8(vb + v_lds[j] + (2 * m + 1) * C::VLD, hi);
   };
-  // register set S into LDS buffer buf
+  // k' tile kt into LDS K buffer buf: each wave makes NKD copies of 1 KB
+  // (16 bytes per lane) straight from memory to LDS. The resource is rebased
+  // on the tile's first key, so rows past token T read as zero. The copies
+  // count as loads (vmcnt): a wait for them precedes the barrier that
+  // publishes the buffer.
+  auto kcopy = [&](int kt, int buf) {
+    const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
+#pragma unroll
+    for (int j = 0; j < C::NKD; ++j) {
+      const int f = wave * C::NKD + j;
+      if (C::NKD * C::NW == C::KCP || f < C::KCP) lds_copy16(rk, Ks + buf * C::KBUF + f * 512, k_voff[j]);
+    }
+  };
+  // V register set S into LDS buffer buf
   auto stage = [&](auto Sc, int buf) {
     constexpr int S = decltype(Sc)::value;
-    uint16_t* kb = Ks + buf * C::KBUF;
     uint16_t* vb = Vt + buf * C::VBUF;
-#pragma unroll
-    for (int j = 0; j < C::NKP; ++j)
-      if (C::NKP * C::NT == C::KCH || k_act[j]) st16(kb + k_lds[j], kw[S][j]);
 #pragma unroll
     for (int j = 0; j < C::NVB; ++j)
       if (C::NVB * C::NT == C::NMB || v_act[j]) {
@@ -424,7 +427,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // ---- as the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7). The
   // ---- first two key tiles go out after the q rows.
   constexpr int RPI = 64 / C::CPR;  // q rows per load
-  uint16_t* const qs = smem + wave * 64 * C::QLD;
+  uint16_t* const qs = Vt + wave * 64 * C::QLD;
   // row r of the wave: column wave*64 + r
   auto col_row = [&](int r, int& tr, int& hr) {
     const int col = wave * 64 + r;
@@ -432,6 +435,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     hr = grp * hpw + (col & (hpw - 1));
   };
   const int qc = lane % C::CPR, qr0 = lane / C::CPR;
+  kcopy(kt0, 0);
   bf16x8_t bq[CB][C::KS];
   {
     constexpr int NB = C::CPR >= 8 ? 2 : 1;  // batches of rows (register pressure)
@@ -500,8 +504,11 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   const int tw1 = min(q0 + ((wave * 32 * CB + 32 * CB - 1) >> p.hpw_log2), p.T - 1);
   constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
+  // K fragment (rb, s): row rb*32 + n, chunk 2s + hf, at its swizzled position
+  const int k_lane = n * D;
+  const int k_swz = (n / C::KSW) % C::CPR;
   auto kfrag = [&](const uint16_t* kb, int rb, int s) {
-    return *reinterpret_cast<const bf16x8_t*>(kb + (rb * 32 + n) * C::KLD + 16 * s + 8 * hf);
+    return *reinterpret_cast<const bf16x8_t*>(kb + rb * 32 * D + k_lane + (((2 * s + hf) ^ k_swz) << 3));
   };
   // V^T fragment (s2, db): row db*32 + n, logical chunk 2*s2 + hf, stored at
   // chunk (2*s2 + hf) ^ (2*db + n/16) (the swizzle of vt_swz)
@@ -582,11 +589,12 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     }
   }
 
-  // Tile kt of parity P (LDS buffer P) of kind KIND, in a fixed instruction
-  // order (TileSched): the loads of tile kt+2 go out into register set P
-  // first, then the MFMAs of the tile run with the softmax of its scores and
-  // (if STAGE) the staging of tile kt+1 (register set P^1, loaded a tile
-  // ago) into LDS buffer P^1 in between.
+  // Tile kt of parity P (LDS buffers P) of kind KIND, in a fixed instruction
+  // order (TileSched): the k' copy of tile kt+1 into K buffer P^1 (if STAGE)
+  // and the V loads of tile kt+2 into register set P go out first, then the
+  // MFMAs of the tile run with the softmax of its scores and (if STAGE) the
+  // transposition of tile kt+1's V (register set P^1, loaded a tile ago)
+  // into V^T buffer P^1 in between.
   auto tile_sched = [&](auto Kc, auto Sc, auto Pc, int kt) {
     constexpr int KIND = decltype(Kc)::value;
     constexpr bool STAGE = decltype(Sc)::value != 0;
@@ -595,8 +603,8 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     using TS = TileSched<D, KIND, STAGE>;
     const uint16_t* kb = Ks + P * C::KBUF;
     const uint16_t* vb = Vt + P * C::VBUF;
-    uint16_t* kbw = Ks + (P ^ 1) * C::KBUF;
     uint16_t* vbw = Vt + (P ^ 1) * C::VBUF;
+    if (STAGE && kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
     if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
     f32x16_t sacc[C::RB][CB];
     u32x4_t pbu[CB][C::PS];
@@ -619,9 +627,6 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       constexpr bool second = id0 >= 1000;
       constexpr int id = second ? id0 - 1000 : id0;
       if constexpr (id0 < 0) {
-      } else if constexpr (id < 100) {
-        if constexpr (second)
-          if (C::NKP * C::NT == C::KCH || k_act[id]) st16(kbw + k_lds[id], kw[P ^ 1][id]);
       } else if constexpr (id < 200) {
         constexpr int j = (id - 100) >> 2, m = (id - 100) & 3;
         if (!(C::NVB * C::NT == C::NMB || v_act[j])) return;
@@ -680,6 +685,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // Tile kt of parity P for a wave that sees part of it (generic path).
   auto tile_edge = [&](auto Pc, int kt) {
     constexpr int P = decltype(Pc)::value;
+    if (kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
     if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
     if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
     compute_edge(P, kt);
@@ -687,8 +693,15 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // Tile kt of parity P that this wave does not see: staging only.
   auto tile_empty = [&](auto Pc, int kt) {
     constexpr int P = decltype(Pc)::value;
+    if (kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
     if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
     if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
+  };
+  // End of a tile: this wave's k' copies have landed (they are loads, so the
+  // barrier's own waits do not cover them), then all waves meet.
+  auto tile_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
   };
 
   // ---- main loop: one barrier per tile; every wave runs kt0..kt1 and so
@@ -697,28 +710,28 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // ---- straight-line.
   __syncthreads();  // every wave has read its q rows back
   stage(ic<0>{}, 0);
-  __syncthreads();
+  tile_sync();
   auto run = [&](auto body, int ka, int kb_) {
     int kt = ka;
     if (kt <= kb_ && ((kt - kt0) & 1)) {
       body(ic<1>{}, kt);
-      __syncthreads();
+      tile_sync();
       ++kt;
     }
     for (; kt + 1 <= kb_; kt += 2) {
       body(ic<0>{}, kt);
-      __syncthreads();
+      tile_sync();
       body(ic<1>{}, kt + 1);
-      __syncthreads();
+      tile_sync();
     }
     if (kt <= kb_) {
       body(ic<0>{}, kt);
-      __syncthreads();
+      tile_sync();
     }
   };
   auto one = [&](auto body, int kt) {
     if ((kt - kt0) & 1) body(ic<1>{}, kt); else body(ic<0>{}, kt);
-    __syncthreads();
+    tile_sync();
   };
   // Waves whose 64 columns are 64 consecutive positions on a tile boundary,
   // with a window that is a multiple of the tile or wider than the wave's

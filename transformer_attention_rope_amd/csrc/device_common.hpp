@@ -102,6 +102,13 @@ __device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS, lane i at
+// lds + 16*i (buffer_load_dwordx4 ... lds; counted by vmcnt, not lgkmcnt).
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           0, 0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
 

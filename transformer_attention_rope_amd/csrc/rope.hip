@@ -17,9 +17,9 @@ namespace nc {
 
 // ------------------------------------------------------- attention prep
 // Input stage of the prefill forward: k' = RMSNorm(RoPE(k)) for every key row,
-// written once in the layout and type of k (the attention kernel revisits each
-// key tile for several query tiles and only copies it), and the fp32
-// (cos, sin) table of every position for the rotation of q rows:
+// written once (the attention kernel revisits each key tile for several query
+// tiles and only copies it), and the fp32 (cos, sin) table of every position
+// for the rotation of q rows:
 //   tabq[t][i] = (cos, sin)(p * theta_i),  p = pos_offset + t,  i < D/2.
 // One workgroup per (position t, block of BB sequences): the D/2 angles of
 // the position are formed once, in fp64 (theta_i = base^(-2i/D) as
@@ -27,6 +27,7 @@ namespace nc {
 // 2*pi), and evaluated with sincosf on [-pi, pi]; the rotation and the norm
 // of the rows run in fp32. The CPR 16-byte chunks of a row sit in
 // consecutive lanes and reduce their sum of squares across lanes.
+// k' keeps k's layout (B, T, Hkv, D) and element type.
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
                                                          Elem* __restrict__ kp,
@@ -109,6 +110,9 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
 }
 
 size_t attn_prep_table_bytes(int T, int D) { return (size_t)T * (size_t)(D / 2) * sizeof(float2); }
+size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt) {
+  return (size_t)B * T * Hkv * D * (dt == kF32 ? 4 : 2);
+}
 
 template <int D>
 static hipError_t attn_prep_d(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
