@@ -133,8 +133,6 @@ def test_decode_validation(kw, status, frag):
 def test_workspace_queries():
     L = nc.lib()
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
-    # fp32 (cos, sin) and bf16 {(cos,-sin),(sin,cos)} per position and
-    # frequency (16 bytes), rounded up to 256 bytes
     # fp32 (cos, sin) per position and frequency, then k', each part rounded
     # up to 256 bytes
     assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 2
