@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention-block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--settle-ms 100]
 
 A step is one ``nc_attn_fwd`` call (RoPE + QK-norm + banded attention, the
 prefill path end to end: the k'/table input stage and the attention kernel)
@@ -19,6 +19,13 @@ The same run also times, with HIP events on the launch stream:
   * ``nc_rope_qknorm`` on the d12 q and k, as HBM GB/s;
   * the d12 SSSL and GQA SSSL stacks (4 ``nc_attn_fwd`` layer calls);
 and, on the host, the fp64 oracle on a bounded sample (``cpu_baseline``).
+
+Every timed part first runs untimed for about ``--settle-ms`` of back-to-back
+GPU work, then ``--warmup`` untimed calls, then exactly ``--steps`` timed calls.
+The settling run is there because the engine clock ramps up over the first
+~30 ms of load after the GPU has been idle (the step runs about 20% slower at
+first); without it the numbers depend on how long the host paused before the
+part started.
 
 Only rank 0 of a 1-GPU job exists here: ``--gpus`` above 1 exits.
 Prints one JSON line.
@@ -83,6 +90,30 @@ def event_time_ms(fn, n, torch):
     return s.elapsed_time(e) / n
 
 
+def settle(fn, ms, torch):
+    """Run fn(i) untimed, keeping the GPU busy, until at least ms of GPU time
+    has passed since the first call; returns the number of calls made."""
+    if ms <= 0:
+        return 0
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record()
+    n, chunk, prev = 0, 8, None
+    while True:
+        for _ in range(chunk):
+            fn(n)
+            n += 1
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        if prev is not None:           # one chunk stays queued while we look
+            prev.synchronize()
+            if start.elapsed_time(prev) >= ms:
+                break
+        prev = ev
+    torch.cuda.synchronize()
+    return n
+
+
 def cpu_baseline(budget_s: float):
     """fp64 oracle on the d12 L-layer workload, one (b, h) head (full T=2048)
     at a time, until every head is done or about budget_s seconds passed."""
@@ -119,8 +150,10 @@ def cpu_baseline(budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed back-to-back GPU work before each timed part (clock ramp)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
                     choices=["all", "fwd", "core", "decode", "rope", "stacks", "copy"],
@@ -146,6 +179,12 @@ def main():
     dev = torch.device("cuda:0")
     K, Wm = args.steps, args.warmup
     out = {}
+    settled = {}   # calls made by the settling run of each part
+
+    def prime(name, fn):
+        settled[name] = settle(fn, args.settle_ms, torch)
+        for i in range(Wm):
+            fn(i)
 
     if args.only == "copy":
         n = 1 << 30
@@ -174,8 +213,7 @@ def main():
             nc.attn_fwd(q, k, v, window=W, out=o, workspace=ws)
 
         if args.only in ("all", "fwd"):
-            for i in range(Wm):
-                step(i)
+            prime("step", step)
             ms = event_time_ms(step, K, torch)
             out["step_ms"] = ms
         if args.only in ("all", "core"):
@@ -186,13 +224,13 @@ def main():
                 q, k, v, o = sets[i % len(sets)]
                 nc.attn_core(q, v, wss[i % len(sets)], window=W, out=o)
 
-            for i in range(Wm):
-                kern(i)
+            prime("core", kern)
             out["kern_ms"] = event_time_ms(kern, K, torch)
             del wss
         del sets, ws
 
     if args.only in ("fwd", "core"):
+        out["settle_calls"] = settled
         print(json.dumps(out))
         return
 
@@ -211,8 +249,7 @@ def main():
                 q, kn, vn, kc, vc, L, o = dsets[i % len(dsets)]
                 nc.attn_decode(q, kn, vn, kc, vc, L, window=Wd, out=o, workspace=wsd)
 
-            for i in range(Wm):
-                dstep(i)
+            prime(f"decode_W{Wd}", dstep)
             ms = event_time_ms(dstep, K, torch)
             nbytes = sum(wl.decode_bytes(ds[5].cpu().tolist(), dcfg.Hkv, dcfg.D, Wd, dcfg.H)
                          for ds in dsets) / len(dsets)
@@ -238,8 +275,7 @@ def main():
             q, k, qo, ko = rsets[i % len(rsets)]
             nc.rope_qknorm(q, k, q_out=qo, k_out=ko)
 
-        for i in range(Wm):
-            rstep(i)
+        prime("rope", rstep)
         ms = event_time_ms(rstep, K, torch)
         nbytes = 2 * (rsets[0][0].numel() + rsets[0][1].numel()) * 2
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -265,8 +301,7 @@ def main():
                 for l, (q, k, v) in enumerate(layers):
                     nc.attn_fwd(q, k, v, window=c.windows[l], out=outs[l], workspace=wsc)
 
-            for i in range(Wm):
-                sstep(i)
+            prime(c.name, sstep)
             ms = event_time_ms(sstep, K, torch)
             fl = sum(wl.prefill_flops(c.B, c.T, c.H, c.D, w) for w in c.windows)
             tf = fl / (ms * 1e-3) / 1e12
@@ -290,6 +325,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
+        "settle_ms": args.settle_ms,
+        "settle_calls": settled,
         "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -21,28 +21,52 @@ namespace nc {
 // tiles and only copies it), and the fp32 (cos, sin) table of every position
 // for the rotation of q rows:
 //   tabq[t][i] = (cos, sin)(p * theta_i),  p = pos_offset + t,  i < D/2.
-// One workgroup per (position t, block of BB sequences): the D/2 angles of
-// the position are formed once, in fp64 (theta_i = base^(-2i/D) as
-// exp2(-(2i/D) log2 base), then a two-constant Cody-Waite reduction modulo
-// 2*pi), and evaluated with sincosf on [-pi, pi]; the rotation and the norm
-// of the rows run in fp32. The CPR 16-byte chunks of a row sit in
-// consecutive lanes and reduce their sum of squares across lanes.
-// k' keeps k's layout (B, T, Hkv, D) and element type.
+// One workgroup per (position t, block of RB key rows of that position), where
+// the rows of a position are its B*Hkv (sequence, head) pairs and RB rows hold
+// 256*PREP_CPT 16-byte chunks. Each thread issues its (up to PREP_CPT) loads
+// first; meanwhile the first D/2 threads form the position's angles in fp64
+// (theta_i = base^(-2i/D) as exp2(-(2i/D) log2 base), then a two-constant
+// Cody-Waite reduction modulo 2*pi) and evaluate them with sincosf on
+// [-pi, pi]. The rotation and the norm of the rows run in fp32; the CPR
+// 16-byte chunks of a row sit in consecutive lanes and reduce their sum of
+// squares across lanes. k' keeps k's layout (B, T, Hkv, D) and element type.
+constexpr int PREP_CPT = 4;  // 16-byte chunks per thread
+
+template <int D, typename Elem>
+constexpr int prep_rows_per_block() {
+  return 256 * PREP_CPT / (D / (sizeof(Elem) == 2 ? 8 : 4));
+}
+
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
                                                          Elem* __restrict__ kp,
-                                                         float2* __restrict__ tabq, int B, int T,
-                                                         int Hkv, double log2_base, int pos_offset,
-                                                         int BB, int nbb) {
+                                                         float2* __restrict__ tabq, int T,
+                                                         int Hkv, int rows, double log2_base,
+                                                         int pos_offset, int nrb) {
   constexpr bool kBf = sizeof(Elem) == 2;
   constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;      // chunks per row
+  constexpr int RB = prep_rows_per_block<D, Elem>();
+  static_assert(64 % CPR == 0, "a row's chunks stay inside one wave");
   __shared__ float2 cs[D / 2];
 
-  const int t = (int)blockIdx.x / nbb;
-  const int b0 = ((int)blockIdx.x - t * nbb) * BB;
-  const int nb = min(BB, B - b0);
+  const int t = (int)blockIdx.x / nrb;
+  const int r0 = ((int)blockIdx.x - t * nrb) * RB;
+  const int total = min(RB, rows - r0) * CPR;  // whole rows only
   const int tid = threadIdx.x;
+
+  u32x4_t w[PREP_CPT];
+  size_t off[PREP_CPT];
+#pragma unroll
+  for (int p = 0; p < PREP_CPT; ++p) {
+    const int ci = p * 256 + tid;
+    const int row = r0 + ci / CPR;
+    const int cc = ci % CPR;
+    const int bb = row / Hkv, g = row - bb * Hkv;
+    off[p] = (((size_t)bb * T + t) * Hkv + g) * D + (size_t)cc * EPC;
+    if (ci < total) w[p] = ld16(k + off[p]);
+  }
+
   if (tid < D / 2) {
     const double theta = exp2(-(double)tid / (D / 2) * log2_base);
     const double a = (double)(pos_offset + t) * theta;
@@ -52,35 +76,26 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     float sn, c;
     sincosf((float)r, &sn, &c);
     cs[tid] = make_float2(c, sn);
-    if (b0 == 0) tabq[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
+    if (r0 == 0) tabq[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
   }
   __syncthreads();
 
-  const int total = nb * Hkv * CPR;
-  const int passes = (total + 255) / 256;
-  for (int it = 0; it < passes; ++it) {
-    const int ci = it * 256 + tid;
-    const bool ok = ci < total;
-    const int row = ok ? ci / CPR : 0;
-    const int cc = ci - row * CPR;
-    const int bb = row / Hkv, g = row - bb * Hkv;
-    const size_t off = (((size_t)(b0 + bb) * T + t) * Hkv + g) * D + (size_t)cc * EPC;
+#pragma unroll
+  for (int p = 0; p < PREP_CPT; ++p) {
+    const int ci = p * 256 + tid;
+    if (p * 256 >= total) break;  // uniform across the workgroup
+    const bool ok = ci < total;   // uniform across the CPR lanes of a row
+    const int cc = ci % CPR;
     float x[EPC];
-    if (ok) {
-      const u32x4_t w = ld16(k + off);
-      if constexpr (kBf) {
+    if constexpr (kBf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          x[2 * m] = bf_lo(w[m]);
-          x[2 * m + 1] = bf_hi(w[m]);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] = ok ? bf_lo(w[p][m]) : 0.f;
+        x[2 * m + 1] = ok ? bf_hi(w[p][m]) : 0.f;
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < EPC; ++m) x[m] = 0.f;
+      for (int m = 0; m < 4; ++m) x[m] = ok ? __uint_as_float(w[p][m]) : 0.f;
     }
     float ss = 0.f;
 #pragma unroll
@@ -96,15 +111,15 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     ss = group_sum<CPR>(ss);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
     if (ok) {
-      u32x4_t w;
+      u32x4_t o;
       if constexpr (kBf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
+        for (int m = 0; m < 4; ++m) o[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
       } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = __float_as_uint(x[m] * inv);
+        for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
-      st16(kp + off, w);
+      st16(kp + off[p], o);
     }
   }
 }
@@ -114,27 +129,27 @@ size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt) {
   return (size_t)B * T * Hkv * D * (dt == kF32 ? 4 : 2);
 }
 
+template <int D, typename Elem>
+static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
+                                   double rope_base, int pos_offset, hipStream_t stream) {
+  constexpr int RB = prep_rows_per_block<D, Elem>();
+  const long long rows = (long long)B * Hkv;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int nrb = (int)((rows + RB - 1) / RB);
+  const long long nblk = (long long)T * nrb;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_prep_kernel<D, Elem>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     (const Elem*)k, (Elem*)kp, (float2*)tabq, T, Hkv, (int)rows,
+                     std::log2(rope_base), pos_offset, nrb);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t attn_prep_d(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
                               double rope_base, int pos_offset, Dtype dt, hipStream_t stream) {
-  // sequences per workgroup: about 64 rows, so the angles are amortised
-  int BB = (64 + Hkv - 1) / Hkv;
-  if (BB > B) BB = B;
-  if (BB < 1) BB = 1;
-  const int nbb = (B + BB - 1) / BB;
-  const long long nblk = (long long)T * nbb;
-  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const double lb = std::log2(rope_base);
-  if (dt == kBF16) {
-    hipLaunchKernelGGL((attn_prep_kernel<D, uint16_t>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                       (const uint16_t*)k, (uint16_t*)kp, (float2*)tabq, B, T, Hkv, lb, pos_offset,
-                       BB, nbb);
-  } else {
-    hipLaunchKernelGGL((attn_prep_kernel<D, float>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                       (const float*)k, (float*)kp, (float2*)tabq, B, T, Hkv, lb, pos_offset, BB,
-                       nbb);
-  }
-  return hipGetLastError();
+  if (dt == kBF16)
+    return attn_prep_launch<D, uint16_t>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, stream);
+  return attn_prep_launch<D, float>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, stream);
 }
 
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
