@@ -14,12 +14,13 @@
 //  * k' is formed once per key row by the input stage: every key tile is
 //    visited by several query tiles, and a copy costs the tile loop far less
 //    than re-rotating and re-normalising it on each visit.
-//  * A workgroup of 4 waves (one per SIMD) owns 256 query columns: hpw query
-//    heads of one K/V group times 256/hpw consecutive positions, so a K/V
-//    tile staged in LDS serves every head of the group. Each wave owns 64
-//    columns as two 32-column blocks, so every K or V fragment read from LDS
-//    feeds two MFMAs; with one wave per SIMD the accumulators may use the
-//    whole register file (VGPRs and AGPRs).
+//  * A workgroup owns 256 query columns: hpw query heads of one K/V group
+//    times 256/hpw consecutive positions, so a K/V tile staged in LDS serves
+//    every head of the group. At D = 128 it is 4 waves (one per SIMD), each
+//    owning 64 columns as two 32-column blocks, so every K or V fragment read
+//    from LDS feeds two MFMAs and the accumulators may use the whole register
+//    file (VGPRs and AGPRs). At D <= 64 it is 8 waves (two per SIMD) of one
+//    32-column block each: one wave's MFMAs run while the other waits.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    the K tile is the A operand (LDS), the rotated, normalised, pre-scaled Q
 //    is the B operand (registers, loaded once). In the accumulator layout a
@@ -89,11 +90,11 @@ struct FwdArgs {
 // =====================================================================
 // bf16 MFMA kernel
 // =====================================================================
-template <int D>
+template <int D, int NW_ = 4>
 struct BfCfg {
-  static constexpr int NW = 4;             // waves per workgroup, one per SIMD
+  static constexpr int NW = NW_;           // waves per workgroup: 4 (one per SIMD) or 8 (two)
   static constexpr int NT = 64 * NW;       // threads per workgroup
-  static constexpr int CB = 2;             // 32-column blocks per wave
+  static constexpr int CB = 8 / NW;        // 32-column blocks per wave (256 columns in all)
   static constexpr int NC = 32 * CB * NW;  // query columns per workgroup
   static constexpr int BN = 64;            // keys per tile
   static constexpr int KS = D / 16;        // MFMA k-steps of K Q^T
@@ -118,6 +119,8 @@ struct BfCfg {
   static constexpr int NM = NSM + NPM;
   static constexpr int NKF = RB * KS;
   static constexpr int NF = NKF + PS * DB;
+  static constexpr int QR = 32 * CB;       // q / o rows per wave
+  static constexpr int NQL = QR * CPR / 64;  // 16-byte row chunks per lane for them
 };
 
 // Position of key kk (0..BN-1) inside a V^T row. The score accumulator of
@@ -138,15 +141,18 @@ __device__ __forceinline__ int vt_swz(int d, int col) {
   return ((((col >> 3) ^ (d >> 4)) & 7) << 3) | (col & 7);
 }
 
-// Kinds of tiles with a fixed instruction order, for a wave whose 64 columns
-// are 64 consecutive positions starting on a tile boundary:
+// Kinds of tiles with a fixed instruction order, for a wave whose columns
+// are consecutive positions starting on a 32-key boundary (64 of them from
+// a tile boundary with two column blocks; 32 from half H of a tile with one):
 //   kFull  every key visible to every column;
-//   kDiag  the tile holding the wave's own positions (causal diagonal): the
-//          block of keys 32..63 x queries 0..31 is skipped, the two blocks on
-//          the diagonal are masked (key <= query);
-//   kWin   the first tile of the window (keys q - W ..): the block of keys
-//          0..31 x queries 32..63 is skipped, the diagonal blocks are masked
-//          (key > query - W).
+//   kDiag  the tile holding the wave's own positions (causal diagonal): key
+//          blocks after the column block's own are skipped, the block on the
+//          diagonal is masked (key <= query);
+//   kWin   the first tile of the window (keys q - W ..): key blocks before
+//          the column block's own are skipped, the block on the diagonal is
+//          masked (key > query - W).
+// A 32-key block rb and a column block cb lie on the diagonal when rb == cb
+// (two column blocks) or rb == H (one).
 enum TileKind { kFull = 0, kDiag = 1, kWin = 2 };
 
 // Instruction order of such a tile, as a list of MFMAs: the score MFMAs
@@ -165,12 +171,14 @@ enum TileKind { kFull = 0, kDiag = 1, kWin = 2 };
 // Slices start in that order, spread evenly over the MFMAs. An exponential
 // starts two MFMAs after the last score MFMA of its block, and a P.V MFMA
 // comes after the second halves of the four slices that build its P operand.
-template <int D, int KIND, bool STAGE>
+template <int D, int NW, int KIND, bool STAGE, int H>
 struct TileSched {
-  using C = BfCfg<D>;
-  static constexpr int MAXS = 24, MAXL = 16, LAM = 16;
+  using C = BfCfg<D, NW>;
+  // fragment look-ahead in MFMAs: 8 fragments either way
+  static constexpr int MAXS = 24, MAXL = 16, LAM = 8 * C::CB;
+  static constexpr int diag(int cb) { return C::CB == 2 ? cb : H; }
   static constexpr bool present(int rb, int cb) {
-    return !((KIND == kDiag && rb == 1 && cb == 0) || (KIND == kWin && rb == 0 && cb == 1));
+    return !((KIND == kDiag && rb > diag(cb)) || (KIND == kWin && rb < diag(cb)));
   }
   short mt[C::NM], ma[C::NM], mb[C::NM], mc[C::NM], mf[C::NM];
   short fl[C::NM][MAXL];
@@ -208,11 +216,12 @@ struct TileSched {
       const int at = first > LAM ? first - LAM : 0;
       if (nfl[at] < MAXL) fl[at][nfl[at]++] = (short)f; else ok = 0;
     }
-    int last[2][2] = {{-1, -1}, {-1, -1}};
+    int last[2][2] = {{-1, -1}, {-1, -1}};  // [rb][cb]
     for (int m = 0; m < nsm; ++m) last[ma[m]][mc[m]] = m;
 
     short q[160] = {};
-    short early[160] = {};
+    short early[160] = {};  // first slot that keeps the exponential off the MFMA's result latency
+    short ready[160] = {};  // first slot after the block's last score MFMA (program order)
     short start[160] = {};
     bool done[160] = {};
     int nq = 0;
@@ -222,6 +231,7 @@ struct TileSched {
           for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
             const int rb = s2 / 2;
             early[nq] = (short)(last[rb][cb] + 2);
+            ready[nq] = (short)last[rb][cb];
             q[nq++] = (short)(200 + 8 * (rb * C::CB + cb) + i);
           }
     if (STAGE)
@@ -244,15 +254,33 @@ struct TileSched {
         start[x] = (short)m;
         ++started;
       };
-      // the P operand of MFMA m+2 must be complete after slot m+1
-      if (m + 2 < nm && mt[m + 2] == 1) {
-        const int s2 = ma[m + 2], cb = mc[m + 2], rb = s2 / 2;
+      // both halves in this slot (the P operand is needed by the next MFMA)
+      auto begin_both = [&](int x) {
+        put(m, q[x]);
+        put(m, q[x] + 1000);
+        done[x] = true;
+        start[x] = -100;
+        ++started;
+      };
+      // The P operand of MFMA m+1 must be complete after slot m, and that of
+      // MFMA m+2 after slot m+1. A slice starts only after its block's last
+      // score MFMA in program order (slot >= ready).
+      for (int ahead = 1; ahead <= 2; ++ahead) {
+        if (m + ahead >= nm || mt[m + ahead] != 1) continue;
+        const int s2 = ma[m + ahead], cb = mc[m + ahead], rb = s2 / 2;
         for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
           const short id = (short)(200 + 8 * (rb * C::CB + cb) + i);
           for (int x = 0; x < nq; ++x)
             if (q[x] == id && !done[x]) {
               for (int y = head; y <= x; ++y)
-                if (!done[y]) begin(y);
+                if (!done[y]) {
+                  if (ahead == 1) {
+                    if (q[y] >= 200 && ready[y] > m) ok = 0;  // P.V follows its scores
+                    begin_both(y);
+                  } else if (q[y] < 200 || ready[y] <= m) {
+                    begin(y);
+                  }
+                }
             }
         }
       }
@@ -268,6 +296,11 @@ struct TileSched {
     }
     for (int x = 0; x < nq; ++x)
       if (!done[x]) ok = 0;
+    for (int x = 0; x < nq; ++x)
+      if (q[x] >= 200)
+        for (int mp = 0; mp < ready[x]; ++mp)
+          for (int k = 0; k < MAXS; ++k)
+            if (v[mp][k] == q[x]) ok = 0;
     for (int m = nsm; m < nm; ++m) {
       const int s2 = ma[m], cb = mc[m], rb = s2 / 2;
       for (int i = 4 * (s2 % 2); i < 4 * (s2 % 2) + 4; ++i) {
@@ -281,22 +314,22 @@ struct TileSched {
     }
   }
 };
-template <int D, int KIND, bool STAGE>
+template <int D, int NW, int KIND, bool STAGE, int H>
 struct TileSchedTab {
-  static constexpr TileSched<D, KIND, STAGE> s{};
+  static constexpr TileSched<D, NW, KIND, STAGE, H> s{};
   static_assert(s.ok, "tile schedule");
 };
 
-template <int D>
-__global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs p) {
-  using C = BfCfg<D>;
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
+  using C = BfCfg<D, NW>;
   constexpr int CB = C::CB;
   // K and V^T double buffers. Before the first tile and after the last one
   // the V^T part (enlarged to fit) holds each wave's q rows and output rows
-  // (QLD-element rows, 64 per wave) on their way between row-major global
+  // (QLD-element rows, QR per wave) on their way between row-major global
   // memory and the MFMA register layouts; the K part is only written by the
   // tile copies, so the first one can start at once.
-  constexpr int kVpart = 2 * C::VBUF > 4 * 64 * C::QLD ? 2 * C::VBUF : 4 * 64 * C::QLD;
+  constexpr int kVpart = 2 * C::VBUF > NW * C::QR * C::QLD ? 2 * C::VBUF : NW * C::QR * C::QLD;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::KBUF + kVpart];
   uint16_t* const Ks = smem;
   uint16_t* const Vt = smem + 2 * C::KBUF;
@@ -353,7 +386,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     const int vd = mb % C::CPR, grp4 = mb / C::CPR;
     const int vgp = (grp4 & ~3) | ((grp4 & 1) << 1) | ((grp4 >> 1) & 1);
     v_act[j] = mb < C::NMB;
-    v_voff[j] = (uint32_t)(4 * vgp) * row_bytes + vd * 16;
+    v_voff[j] = v_act[j] ? (uint32_t)(4 * vgp) * row_bytes + vd * 16 : 0xF0000000u;
     v_lds[j] = (8 * vd) * C::VLD + vt_swz(8 * vd, vt_pos(4 * vgp));
   }
 
@@ -361,18 +394,21 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
 
   // V rows of tile kt into register set S. The resource is rebased on the
   // tile's first key: rows past token T (and only those) fall beyond
-  // num_records and read as zero; a tile past the sequence gets an empty range.
+  // num_records and read as zero. Every wave issues the same 4*NVB loads for
+  // every tile, so the count of loads in flight is the same on every path:
+  // a tile past the workgroup's range (kt > kt1) gets an empty range, and a
+  // lane without a micro-block an offset past any range; both read nothing.
   auto gload = [&](auto Sc, int kt) {
     constexpr int S = decltype(Sc)::value;
     const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
-    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
+    const uint32_t nk =
+        __builtin_amdgcn_readfirstlane(kt <= kt1 && so < kv_records ? kv_records - so : 0u);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq + so, nk);
 #pragma unroll
-    for (int j = 0; j < C::NVB; ++j)
-      if (C::NVB * C::NT == C::NMB || v_act[j]) {
+    for (int j = 0; j < C::NVB; ++j) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vw[S][j][r] = bload16(rv, v_voff[j] + r * row_bytes, 0);
-      }
+      for (int r = 0; r < 4; ++r) vw[S][j][r] = bload16(rv, v_voff[j] + r * row_bytes, 0);
+    }
   };
   // V micro-block j of set S, dims pair m: rows 2m, 2m+1 of its V^T block,
   // 4 consecutive (permuted) key slots each
@@ -386,12 +422,14 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   };
   // k' tile kt into LDS K buffer buf: each wave makes NKD copies of 1 KB
   // (16 bytes per lane) straight from memory to LDS. The resource is rebased
-  // on the tile's first key, so rows past token T read as zero. The copies
-  // count as loads (vmcnt): a wait for them precedes the barrier that
-  // publishes the buffer.
+  // on the tile's first key, so rows past token T read as zero; a tile past
+  // the workgroup's range gets an empty range (it fills the free buffer with
+  // zeros and reads nothing). The copies count as loads (vmcnt): a wait for
+  // them precedes the barrier that publishes the buffer.
   auto kcopy = [&](int kt, int buf) {
     const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
-    const uint32_t nk = __builtin_amdgcn_readfirstlane(so < kv_records ? kv_records - so : 0u);
+    const uint32_t nk =
+        __builtin_amdgcn_readfirstlane(kt <= kt1 && so < kv_records ? kv_records - so : 0u);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq + so, nk);
 #pragma unroll
     for (int j = 0; j < C::NKD; ++j) {
@@ -420,17 +458,17 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     h[cb] = grp * hpw + (col & (hpw - 1));
   }
 
-  // ---- Q: the wave's 64 q rows are read row-major (CPR lanes per row, so
+  // ---- Q: the wave's QR q rows are read row-major (CPR lanes per row, so
   // ---- every load covers whole rows), rotated with the fp32 table, RMS-
   // ---- normalised (sum over the row's lanes), scaled by log2(e)/sqrt(D) and
   // ---- rounded to bf16 there, written to the wave's LDS rows, and read back
   // ---- as the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7). The
   // ---- first two key tiles go out after the q rows.
   constexpr int RPI = 64 / C::CPR;  // q rows per load
-  uint16_t* const qs = Vt + wave * 64 * C::QLD;
-  // row r of the wave: column wave*64 + r
+  uint16_t* const qs = Vt + wave * C::QR * C::QLD;
+  // row r of the wave: column wave*QR + r
   auto col_row = [&](int r, int& tr, int& hr) {
-    const int col = wave * 64 + r;
+    const int col = wave * C::QR + r;
     tr = q0 + (col >> p.hpw_log2);
     hr = grp * hpw + (col & (hpw - 1));
   };
@@ -438,8 +476,8 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   kcopy(kt0, 0);
   bf16x8_t bq[CB][C::KS];
   {
-    constexpr int NB = C::CPR >= 8 ? 2 : 1;  // batches of rows (register pressure)
-    constexpr int PB = C::CPR / NB;
+    constexpr int NB = C::NQL >= 8 ? 2 : 1;  // batches of rows (register pressure)
+    constexpr int PB = C::NQL / NB;
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
       u32x4_t qw[PB];
@@ -595,17 +633,21 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // MFMAs of the tile run with the softmax of its scores and (if STAGE) the
   // transposition of tile kt+1's V (register set P^1, loaded a tile ago)
   // into V^T buffer P^1 in between.
-  auto tile_sched = [&](auto Kc, auto Sc, auto Pc, int kt) {
+  auto tile_sched = [&](auto Kc, auto Sc, auto Pc, auto Hc, int kt) {
     constexpr int KIND = decltype(Kc)::value;
     constexpr bool STAGE = decltype(Sc)::value != 0;
     constexpr int P = decltype(Pc)::value;
-    using SCH = TileSchedTab<D, KIND, STAGE>;
-    using TS = TileSched<D, KIND, STAGE>;
+    constexpr int HALF = decltype(Hc)::value;
+    using SCH = TileSchedTab<D, NW, KIND, STAGE, HALF>;
+    using TS = TileSched<D, NW, KIND, STAGE, HALF>;
     const uint16_t* kb = Ks + P * C::KBUF;
     const uint16_t* vb = Vt + P * C::VBUF;
     uint16_t* vbw = Vt + (P ^ 1) * C::VBUF;
-    if (STAGE && kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
-    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
+    if (STAGE) {
+      kcopy(kt + 1, P ^ 1);
+      __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
+      gload(ic<P>{}, kt + 2);
+    }
     f32x16_t sacc[C::RB][CB];
     u32x4_t pbu[CB][C::PS];
     bf16x8_t fr[C::NF];
@@ -653,8 +695,8 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
           pin(etmp[idx][1]);
         } else {
           uint32_t w = pack_bf2(etmp[idx][0], etmp[idx][1]);
-          if constexpr (KIND == kDiag && rb == cb) w &= dmask[i];
-          if constexpr (KIND == kWin && rb == cb) w &= ~dmask[i];
+          if constexpr (KIND == kDiag && rb == TS::diag(cb)) w &= dmask[i];
+          if constexpr (KIND == kWin && rb == TS::diag(cb)) w &= ~dmask[i];
           lsum[cb] = dot2bf(w, kOnes, lsum[cb]);
           pbu[cb][rb * 2 + (i >> 2)][i & 3] = w;
         }
@@ -681,27 +723,45 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto tile_full = [&](auto Pc, int kt) { tile_sched(ic<kFull>{}, ic<1>{}, Pc, kt); };
+  auto tile_full = [&](auto Pc, int kt) { tile_sched(ic<kFull>{}, ic<1>{}, Pc, ic<0>{}, kt); };
   // Tile kt of parity P for a wave that sees part of it (generic path).
   auto tile_edge = [&](auto Pc, int kt) {
     constexpr int P = decltype(Pc)::value;
-    if (kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
-    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
+    kcopy(kt + 1, P ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
+    gload(ic<P>{}, kt + 2);
     if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
     compute_edge(P, kt);
   };
   // Tile kt of parity P that this wave does not see: staging only.
   auto tile_empty = [&](auto Pc, int kt) {
     constexpr int P = decltype(Pc)::value;
-    if (kt + 1 <= kt1) kcopy(kt + 1, P ^ 1);
-    if (kt + 2 <= kt1) gload(ic<P>{}, kt + 2);
+    kcopy(kt + 1, P ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
+    gload(ic<P>{}, kt + 2);
     if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
   };
-  // End of a tile: this wave's k' copies have landed (they are loads, so the
-  // barrier's own waits do not cover them), then all waves meet.
+  // End of a tile: this wave's LDS writes and k' copies have landed, then all
+  // waves meet. Every tile body issues its NKD copies and then its 4*NVB V
+  // loads (for the tile after next), so "all but the 4*NVB newest loads"
+  // is exactly the copies plus everything older; the V loads keep flying
+  // across the barrier. The barrier is the bare instruction: the wait is
+  // explicit, and the empty asm statements keep the compiler from moving
+  // memory accesses across it.
+  static_assert(C::NVB == 1, "one V micro-block per thread");
+  auto wg_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   auto tile_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    wg_barrier();
+  };
+  // the same after a body that issued no copies or loads (the last tile)
+  auto tile_sync_all = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    wg_barrier();
   };
 
   // ---- main loop: one barrier per tile; every wave runs kt0..kt1 and so
@@ -710,7 +770,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
   // ---- straight-line.
   __syncthreads();  // every wave has read its q rows back
   stage(ic<0>{}, 0);
-  tile_sync();
+  tile_sync_all();
   auto run = [&](auto body, int ka, int kb_) {
     int kt = ka;
     if (kt <= kb_ && ((kt - kt0) & 1)) {
@@ -733,23 +793,40 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
     if ((kt - kt0) & 1) body(ic<1>{}, kt); else body(ic<0>{}, kt);
     tile_sync();
   };
-  // Waves whose 64 columns are 64 consecutive positions on a tile boundary,
+  // Waves whose columns are 32*CB consecutive positions from a 32-key
+  // boundary (a tile boundary when CB = 2; half H of a tile when CB = 1),
   // with a window that is a multiple of the tile or wider than the wave's
   // reach, see: nothing, then (if the window bites) one kWin tile, full
   // tiles, one kDiag tile (its own positions), then nothing.
   const bool aligned = hpw == 1 && p.W >= C::BN && tw0 <= q_last &&
                        (p.W % C::BN == 0 || p.W >= tw0 + C::BN);
+  // calls f(ic<H>) with the half of the tile where the wave's positions start
+  auto with_half = [&](auto f) {
+    if constexpr (C::CB == 1) {
+      if ((tw0 / 32) & 1) f(ic<1>{}); else f(ic<0>{});
+    } else {
+      f(ic<0>{});
+    }
+  };
   if (aligned) {
     const int ktD = tw0 / C::BN;
     const int ktW = tw0 - p.W >= 0 ? (tw0 - p.W) / C::BN : -1;
     const int kf0 = ktW >= 0 ? ktW + 1 : kt0;
     run(tile_empty, kt0, kf0 - 1 - (ktW >= 0 ? 1 : 0));
-    if (ktW >= 0) one([&](auto Pc, int kt) { tile_sched(ic<kWin>{}, ic<1>{}, Pc, kt); }, ktW);
+    if (ktW >= 0)
+      with_half([&](auto Hc) {
+        one([&](auto Pc, int kt) { tile_sched(ic<kWin>{}, ic<1>{}, Pc, Hc, kt); }, ktW);
+      });
     run(tile_full, kf0, ktD - 1);
-    if (ktD < kt1)
-      one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<1>{}, Pc, kt); }, ktD);
-    else
-      one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<0>{}, Pc, kt); }, ktD);
+    with_half([&](auto Hc) {
+      if (ktD < kt1) {
+        one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<1>{}, Pc, Hc, kt); }, ktD);
+      } else {
+        if ((ktD - kt0) & 1) tile_sched(ic<kDiag>{}, ic<0>{}, ic<1>{}, Hc, ktD);
+        else tile_sched(ic<kDiag>{}, ic<0>{}, ic<0>{}, Hc, ktD);
+        tile_sync_all();
+      }
+    });
     run(tile_empty, ktD + 1, kt1);
   } else {
     // full tiles for this wave: j0 + BN - 1 <= tw0 and tw1 - j0 < W
@@ -784,7 +861,7 @@ __global__ void __launch_bounds__(BfCfg<D>::NT, 1) attn_fwd_bf16_kernel(FwdArgs 
       }
     }
 #pragma unroll
-    for (int i = 0; i < C::CPR; ++i) {
+    for (int i = 0; i < C::NQL; ++i) {
       const int r = i * RPI + qr0;
       int tr, hr;
       col_row(r, tr, hr);
@@ -900,6 +977,13 @@ static int ilog2(int x) {
   return r;
 }
 
+// Waves per workgroup of the bf16 kernel: two per SIMD where one column
+// block per wave fits the halved register budget (D <= 64; measured 8-16%
+// faster than one wave per SIMD on the GQA D=64 layers), one per SIMD at
+// D = 128, whose accumulators need more than 256 registers per wave.
+template <int D>
+constexpr int fwd_waves() { return D == 128 ? 4 : 8; }
+
 template <int D>
 static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
   a.qscale = kLog2e / sqrtf((float)D);
@@ -909,12 +993,12 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
     while (hpw < 32 && (a.G % (hpw * 2)) == 0) hpw *= 2;
     a.hpw_log2 = ilog2(hpw);
     a.ngroups = a.H / hpw;
-    a.bp_log2 = ilog2(BfCfg<D>::NC / hpw);
+    a.bp_log2 = ilog2(BfCfg<D, fwd_waves<D>()>::NC / hpw);
     a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
     const long long grid = (long long)a.nqt * a.B * a.ngroups;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(BfCfg<D>::NT), 0, stream,
-                       a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, fwd_waves<D>()>), dim3((unsigned)grid),
+                       dim3(BfCfg<D, fwd_waves<D>()>::NT), 0, stream, a);
   } else {
     a.hpw_log2 = 0;
     a.ngroups = a.H;
