@@ -128,10 +128,13 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * nc_attn_prep / nc_attn_core -- the two stages of nc_attn_fwd, for callers
  * that schedule them separately (for instance to overlap one layer's prep with
  * another layer's attention on a second stream).
- *   nc_attn_prep writes into ws the fp32 (cos, sin) pairs of angles
+ *   nc_attn_prep writes into ws the (cos, sin) pairs of angles
  *     (pos_offset + t) * rope_base^(-2i/D), t < T, i < D/2, each formed and
- *     reduced modulo 2*pi in fp64, and k' = norm(rope(k)) in k's layout and
- *     element type. Arguments as for nc_attn_fwd.
+ *     reduced modulo 2*pi in fp64 and stored as two fp16 (dtype bf16: the
+ *     rounding, at most 2^-11 relative, is a quarter of the bf16 rounding of
+ *     the rotated q that follows) or two fp32 values (dtype fp32), and
+ *     k' = norm(rope(k)) in k's layout and element type. Arguments as for
+ *     nc_attn_fwd.
  *   nc_attn_core computes o from raw q, the k' and table in ws (only read),
  *     and v; B, T, Hkv, D and dtype must be those of the nc_attn_prep call
  *     that filled ws, which must complete (same stream or an event) first.

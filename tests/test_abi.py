@@ -133,12 +133,12 @@ def test_decode_validation(kw, status, frag):
 def test_workspace_queries():
     L = nc.lib()
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
-    # fp32 (cos, sin) per position and frequency, then k', each part rounded
-    # up to 256 bytes
-    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 2
+    # (cos, sin) per position and frequency (two fp16 for bf16, two fp32 for
+    # fp32), then k', each part rounded up to 256 bytes
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 4 + 8 * 2048 * 6 * 128 * 2
     assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 1) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 4
-    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 512 + 512  # 3*16*8, 3*2*32*2
-    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 1) == 512 + 768  # fp32 rows: 3*2*32*4
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 256 + 512  # 3*16*4, 3*2*32*2
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 1) == 512 + 768  # 3*16*8, 3*2*32*4
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 7) == 0
     # few (sequence, head) pairs: the key range is split and needs chunk states
     n = L.nc_attn_decode_workspace_bytes(2, 2048, 6, 6, 128, 2048)

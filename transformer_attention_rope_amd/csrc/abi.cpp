@@ -120,9 +120,13 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
 }
 
 // ---------------------------------------------------------------- attn_fwd
-// Workspace: the fp32 (cos, sin) table of the T positions, then k'.
+// Workspace: the (cos, sin) table of the T positions (fp16 pairs for bf16,
+// fp32 pairs for fp32), then k'.
 namespace {
-size_t prep_table_bytes(int T, int D) { return round_up(nc::attn_prep_table_bytes(T, D)); }
+nc::Dtype to_dt(nc_dtype dt) { return dt == NC_F32 ? nc::kF32 : nc::kBF16; }
+size_t prep_table_bytes(int T, int D, nc_dtype dt) {
+  return round_up(nc::attn_prep_table_bytes(T, D, to_dt(dt)));
+}
 size_t prep_k_bytes(int B, int T, int Hkv, int D, nc_dtype dt) {
   return round_up(nc::attn_prep_k_bytes(B, T, Hkv, D, dt == NC_F32 ? nc::kF32 : nc::kBF16));
 }
@@ -147,7 +151,7 @@ size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_
   (void)H;
   (void)pos_offset;
   if (B < 1 || T < 1 || Hkv < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
-  return prep_table_bytes(T, D) + prep_k_bytes(B, T, Hkv, D, dtype);
+  return prep_table_bytes(T, D, dtype) + prep_k_bytes(B, T, Hkv, D, dtype);
 }
 
 nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_base,
@@ -160,7 +164,7 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
   if ((s = check_ptrs(names, ptrs, 1)) != NC_OK) return s;
   if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, Hkv, Hkv, D, pos_offset, dt))) != NC_OK)
     return s;
-  hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D), ws, B, T, Hkv, D,
+  hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D, dt), ws, B, T, Hkv, D,
                                       rope_base, pos_offset, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
@@ -177,7 +181,7 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
   if ((s = check_ptrs(names, ptrs, 3)) != NC_OK) return s;
   if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, 0, dt))) != NC_OK)
     return s;
-  hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D), v, o, B, T, H,
+  hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D, dt), v, o, B, T, H,
                                       Hkv, D, window, ws, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core launch");

@@ -77,7 +77,8 @@ struct FwdArgs {
   const void* kp;      // k' = RMSNorm(RoPE(k)), layout and type of k
   const void* v;
   void* o;
-  const float2* tabq;  // [T][D/2] (cos, sin) fp32 for positions pos_offset + t
+  const void* tabq;    // [T][D/2] (cos, sin) of positions pos_offset + t: fp16 pairs
+                       // packed in 32 bits (bf16 kernel), float2 (fp32 kernel)
   int B, T, H, Hkv, W;
   int G;         // H / Hkv
   int hpw_log2;  // log2(query heads per workgroup)
@@ -120,6 +121,11 @@ struct BfCfg {
   static constexpr int NKF = RB * KS;
   static constexpr int NF = NKF + PS * DB;
   static constexpr int QR = 32 * CB;       // q / o rows per wave
+  // V register sets: two (tile kt+2 loads while tile kt+1 is transposed)
+  // except with two waves per SIMD at D = 128, where one set (tile kt+1 loads
+  // at the start of tile kt and is transposed at its end) keeps the wave
+  // within 256 registers
+  static constexpr int VS = (NW == 8 && D == 128) ? 1 : 2;
   static constexpr int NQL = QR * CPR / 64;  // 16-byte row chunks per lane for them
 };
 
@@ -175,7 +181,7 @@ template <int D, int NW, int KIND, bool STAGE, int H>
 struct TileSched {
   using C = BfCfg<D, NW>;
   // fragment look-ahead in MFMAs: 8 fragments either way
-  static constexpr int MAXS = 24, MAXL = 16, LAM = 8 * C::CB;
+  static constexpr int MAXS = 24, MAXL = 16, LAM = C::CB == 2 ? 16 : 6;
   static constexpr int diag(int cb) { return C::CB == 2 ? cb : H; }
   static constexpr bool present(int rb, int cb) {
     return !((KIND == kDiag && rb > diag(cb)) || (KIND == kWin && rb < diag(cb)));
@@ -390,7 +396,12 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
     v_lds[j] = (8 * vd) * C::VLD + vt_swz(8 * vd, vt_pos(4 * vgp));
   }
 
-  u32x4_t vw[2][C::NVB][4];
+  u32x4_t vw[C::VS][C::NVB][4];
+  // register set the tile of parity P loads into, the set it transposes from,
+  // and how many tiles ahead it loads
+  constexpr auto lset = [](int P) { return C::VS == 2 ? P : 0; };
+  constexpr auto sset = [](int P) { return C::VS == 2 ? (P ^ 1) : 0; };
+  constexpr int VAHEAD = C::VS;
 
   // V rows of tile kt into register set S. The resource is rebased on the
   // tile's first key: rows past token T (and only those) fall beyond
@@ -398,7 +409,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // every tile, so the count of loads in flight is the same on every path:
   // a tile past the workgroup's range (kt > kt1) gets an empty range, and a
   // lane without a micro-block an offset past any range; both read nothing.
-  auto gload = [&](auto Sc, int kt) {
+  auto gload = [&](auto Sc, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(Sc)::value;
     const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
     const uint32_t nk =
@@ -412,7 +423,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   };
   // V micro-block j of set S, dims pair m: rows 2m, 2m+1 of its V^T block,
   // 4 consecutive (permuted) key slots each
-  auto v_pair = [&](auto Sc, int j, int m, uint16_t* vb) {
+  auto v_pair = [&](auto Sc, int j, int m, uint16_t* vb) __attribute__((always_inline)) {
     constexpr int S = decltype(Sc)::value;
     const uint32_t a0 = vw[S][j][0][m], a1 = vw[S][j][1][m], a2 = vw[S][j][2][m], a3 = vw[S][j][3][m];
     const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
@@ -426,7 +437,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // the workgroup's range gets an empty range (it fills the free buffer with
   // zeros and reads nothing). The copies count as loads (vmcnt): a wait for
   // them precedes the barrier that publishes the buffer.
-  auto kcopy = [&](int kt, int buf) {
+  auto kcopy = [&](int kt, int buf) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)kt * C::BN * row_bytes;
     const uint32_t nk =
         __builtin_amdgcn_readfirstlane(kt <= kt1 && so < kv_records ? kv_records - so : 0u);
@@ -438,7 +449,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
     }
   };
   // V register set S into LDS buffer buf
-  auto stage = [&](auto Sc, int buf) {
+  auto stage = [&](auto Sc, int buf) __attribute__((always_inline)) {
     constexpr int S = decltype(Sc)::value;
     uint16_t* vb = Vt + buf * C::VBUF;
 #pragma unroll
@@ -459,15 +470,15 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   }
 
   // ---- Q: the wave's QR q rows are read row-major (CPR lanes per row, so
-  // ---- every load covers whole rows), rotated with the fp32 table, RMS-
+  // ---- every load covers whole rows), rotated with the table, RMS-
   // ---- normalised (sum over the row's lanes), scaled by log2(e)/sqrt(D) and
   // ---- rounded to bf16 there, written to the wave's LDS rows, and read back
   // ---- as the MFMA B operand (lane-half hf holds dims 16s + 8hf .. +7). The
-  // ---- first two key tiles go out after the q rows.
+  // ---- first V tiles go out after the q rows (the first k' tile before).
   constexpr int RPI = 64 / C::CPR;  // q rows per load
   uint16_t* const qs = Vt + wave * C::QR * C::QLD;
   // row r of the wave: column wave*QR + r
-  auto col_row = [&](int r, int& tr, int& hr) {
+  auto col_row = [&](int r, int& tr, int& hr) __attribute__((always_inline)) {
     const int col = wave * C::QR + r;
     tr = q0 + (col >> p.hpw_log2);
     hr = grp * hpw + (col & (hpw - 1));
@@ -476,12 +487,15 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   kcopy(kt0, 0);
   bf16x8_t bq[CB][C::KS];
   {
-    constexpr int NB = C::NQL >= 8 ? 2 : 1;  // batches of rows (register pressure)
-    constexpr int PB = C::NQL / NB;
+    // all rows and their table entries (one 16-byte load each: four fp16
+    // (cos, sin) pairs) in one round trip
+    constexpr int NB = 1;
+    constexpr int PB = C::NQL;
+    const uint32_t* const tab = reinterpret_cast<const uint32_t*>(p.tabq);
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
       u32x4_t qw[PB];
-      f32x4_t tq[PB][2];
+      u32x4_t tq[PB];
 #pragma unroll
       for (int ii = 0; ii < PB; ++ii) {
         const int i = bt * PB + ii;
@@ -489,13 +503,11 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
         col_row(i * RPI + qr0, tr, hr);
         const int tc = tr < p.T ? tr : p.T - 1;
         qw[ii] = ld16(qg + (((size_t)b * p.T + tc) * p.H + hr) * D + qc * 8);
-        const float2* trow = p.tabq + (size_t)tc * (D / 2) + qc * 4;
-        tq[ii][0] = *reinterpret_cast<const f32x4_t*>(trow);
-        tq[ii][1] = *reinterpret_cast<const f32x4_t*>(trow + 2);
+        tq[ii] = ld16(tab + (size_t)tc * (D / 2) + qc * 4);
       }
       if (bt == 0) {
         gload(ic<0>{}, kt0);
-        gload(ic<1>{}, kt0 + 1);
+        if constexpr (C::VS == 2) gload(ic<1>{}, kt0 + 1);
       }
 #pragma unroll
       for (int ii = 0; ii < PB; ++ii) {
@@ -505,7 +517,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const float xe = bf_lo(qw[ii][m]), xo = bf_hi(qw[ii][m]);
-          const float c = tq[ii][m >> 1][2 * (m & 1)], sn = tq[ii][m >> 1][2 * (m & 1) + 1];
+          const float c = h_lo(tq[ii][m]), sn = h_hi(tq[ii][m]);
           const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
           x[2 * m] = ye;
           x[2 * m + 1] = yo;
@@ -545,19 +557,19 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // K fragment (rb, s): row rb*32 + n, chunk 2s + hf, at its swizzled position
   const int k_lane = n * D;
   const int k_swz = (n / C::KSW) % C::CPR;
-  auto kfrag = [&](const uint16_t* kb, int rb, int s) {
+  auto kfrag = [&](const uint16_t* kb, int rb, int s) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8_t*>(kb + rb * 32 * D + k_lane + (((2 * s + hf) ^ k_swz) << 3));
   };
   // V^T fragment (s2, db): row db*32 + n, logical chunk 2*s2 + hf, stored at
   // chunk (2*s2 + hf) ^ (2*db + n/16) (the swizzle of vt_swz)
   const int vt_lane = n * C::VLD + 8 * (hf ^ (n >> 4));
-  auto vfrag = [&](const uint16_t* vb, int s2, int db) {
+  auto vfrag = [&](const uint16_t* vb, int s2, int db) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8_t*>(vb + vt_lane + db * 32 * C::VLD + 16 * ((s2 ^ db) & 3));
   };
 
   // Tile crossing the band edge for this wave: 32-key blocks the wave cannot
   // see are skipped, blocks it sees in part are masked in place.
-  auto compute_edge = [&](int buf, int kt) {
+  auto compute_edge = [&](int buf, int kt) __attribute__((always_inline)) {
     const uint16_t* kb = Ks + buf * C::KBUF;
     const uint16_t* vb = Vt + buf * C::VBUF;
 #pragma unroll
@@ -617,15 +629,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // Diagonal-block masks of kDiag tiles: pair i of a score block holds keys
   // c(2i), c(2i+1) with c(r) = 8*(r/4) + r%4 + 4*hf against query n; a key is
   // at or before the query iff c(r) <= n - 4*hf. One bf16 half per key.
-  uint32_t dmask[8];
-  {
+  // Formed where used (only diagonal and window tiles), so that no register
+  // holds them across the tile loop.
+  auto dmask = [&](int i) __attribute__((always_inline)) -> uint32_t {
     const int e = n - 4 * hf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c0 = 8 * ((2 * i) >> 2) + ((2 * i) & 3), c1 = 8 * ((2 * i + 1) >> 2) + ((2 * i + 1) & 3);
-      dmask[i] = (c0 <= e ? 0x0000ffffu : 0u) | (c1 <= e ? 0xffff0000u : 0u);
-    }
-  }
+    const int c0 = 8 * ((2 * i) >> 2) + ((2 * i) & 3), c1 = 8 * ((2 * i + 1) >> 2) + ((2 * i + 1) & 3);
+    return (c0 <= e ? 0x0000ffffu : 0u) | (c1 <= e ? 0xffff0000u : 0u);
+  };
 
   // Tile kt of parity P (LDS buffers P) of kind KIND, in a fixed instruction
   // order (TileSched): the k' copy of tile kt+1 into K buffer P^1 (if STAGE)
@@ -633,7 +643,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // MFMAs of the tile run with the softmax of its scores and (if STAGE) the
   // transposition of tile kt+1's V (register set P^1, loaded a tile ago)
   // into V^T buffer P^1 in between.
-  auto tile_sched = [&](auto Kc, auto Sc, auto Pc, auto Hc, int kt) {
+  auto tile_sched = [&](auto Kc, auto Sc, auto Pc, auto Hc, int kt) __attribute__((always_inline)) {
     constexpr int KIND = decltype(Kc)::value;
     constexpr bool STAGE = decltype(Sc)::value != 0;
     constexpr int P = decltype(Pc)::value;
@@ -646,7 +656,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
     if (STAGE) {
       kcopy(kt + 1, P ^ 1);
       __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
-      gload(ic<P>{}, kt + 2);
+      gload(ic<lset(P)>{}, kt + VAHEAD);
     }
     f32x16_t sacc[C::RB][CB];
     u32x4_t pbu[CB][C::PS];
@@ -657,14 +667,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[rb][cb][r] = 0.f;
-    auto frag = [&](int f) -> bf16x8_t {
+    auto frag = [&](int f) __attribute__((always_inline)) -> bf16x8_t {
       if (f < C::NKF) return kfrag(kb, f / C::KS, f % C::KS);
       const int fv = f - C::NKF;
       return vfrag(vb, fv / C::DB, fv % C::DB);
     };
     float etmp[C::RB * CB * 8][2];
     uint32_t vtmp[C::NVB][4][4];
-    auto slice = [&](auto idc) {
+    auto slice = [&](auto idc) __attribute__((always_inline)) {
       constexpr int id0 = decltype(idc)::value;
       constexpr bool second = id0 >= 1000;
       constexpr int id = second ? id0 - 1000 : id0;
@@ -673,8 +683,9 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
         constexpr int j = (id - 100) >> 2, m = (id - 100) & 3;
         if (!(C::NVB * C::NT == C::NMB || v_act[j])) return;
         if constexpr (!second) {
-          const uint32_t a0 = vw[P ^ 1][j][0][m], a1 = vw[P ^ 1][j][1][m];
-          const uint32_t a2 = vw[P ^ 1][j][2][m], a3 = vw[P ^ 1][j][3][m];
+          constexpr int SS = sset(P);
+          const uint32_t a0 = vw[SS][j][0][m], a1 = vw[SS][j][1][m];
+          const uint32_t a2 = vw[SS][j][2][m], a3 = vw[SS][j][3][m];
           vtmp[j][m][0] = (a0 & 0xffffu) | (a1 << 16);
           vtmp[j][m][1] = (a2 & 0xffffu) | (a3 << 16);
           vtmp[j][m][2] = (a0 >> 16) | (a1 & 0xffff0000u);
@@ -695,8 +706,8 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
           pin(etmp[idx][1]);
         } else {
           uint32_t w = pack_bf2(etmp[idx][0], etmp[idx][1]);
-          if constexpr (KIND == kDiag && rb == TS::diag(cb)) w &= dmask[i];
-          if constexpr (KIND == kWin && rb == TS::diag(cb)) w &= ~dmask[i];
+          if constexpr (KIND == kDiag && rb == TS::diag(cb)) w &= dmask(i);
+          if constexpr (KIND == kWin && rb == TS::diag(cb)) w &= ~dmask(i);
           lsum[cb] = dot2bf(w, kOnes, lsum[cb]);
           pbu[cb][rb * 2 + (i >> 2)][i & 3] = w;
         }
@@ -723,43 +734,46 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto tile_full = [&](auto Pc, int kt) { tile_sched(ic<kFull>{}, ic<1>{}, Pc, ic<0>{}, kt); };
+  auto tile_full = [&](auto Pc, int kt) __attribute__((always_inline)) { tile_sched(ic<kFull>{}, ic<1>{}, Pc, ic<0>{}, kt); };
   // Tile kt of parity P for a wave that sees part of it (generic path).
-  auto tile_edge = [&](auto Pc, int kt) {
+  // (With one V register set the transposition comes after the compute, so
+  // the loads issued at the start of the tile have the tile to land.)
+  auto tile_edge = [&](auto Pc, int kt) __attribute__((always_inline)) {
     constexpr int P = decltype(Pc)::value;
     kcopy(kt + 1, P ^ 1);
     __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
-    gload(ic<P>{}, kt + 2);
-    if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
+    gload(ic<lset(P)>{}, kt + VAHEAD);
+    if (C::VS == 2 && kt + 1 <= kt1) stage(ic<sset(P)>{}, P ^ 1);
     compute_edge(P, kt);
+    if (C::VS == 1 && kt + 1 <= kt1) stage(ic<sset(P)>{}, P ^ 1);
   };
   // Tile kt of parity P that this wave does not see: staging only.
-  auto tile_empty = [&](auto Pc, int kt) {
+  auto tile_empty = [&](auto Pc, int kt) __attribute__((always_inline)) {
     constexpr int P = decltype(Pc)::value;
     kcopy(kt + 1, P ^ 1);
     __builtin_amdgcn_sched_barrier(0);  // the copies go out before the V loads
-    gload(ic<P>{}, kt + 2);
-    if (kt + 1 <= kt1) stage(ic<P ^ 1>{}, P ^ 1);
+    gload(ic<lset(P)>{}, kt + VAHEAD);
+    if (kt + 1 <= kt1) stage(ic<sset(P)>{}, P ^ 1);
   };
   // End of a tile: this wave's LDS writes and k' copies have landed, then all
   // waves meet. Every tile body issues its NKD copies and then its 4*NVB V
-  // loads (for the tile after next), so "all but the 4*NVB newest loads"
+  // loads (for a later tile), so "all but the 4*NVB newest loads"
   // is exactly the copies plus everything older; the V loads keep flying
   // across the barrier. The barrier is the bare instruction: the wait is
   // explicit, and the empty asm statements keep the compiler from moving
   // memory accesses across it.
   static_assert(C::NVB == 1, "one V micro-block per thread");
-  auto wg_barrier = [&]() {
+  auto wg_barrier = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto tile_sync = [&]() {
+  auto tile_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
     wg_barrier();
   };
   // the same after a body that issued no copies or loads (the last tile)
-  auto tile_sync_all = [&]() {
+  auto tile_sync_all = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     wg_barrier();
   };
@@ -771,7 +785,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   __syncthreads();  // every wave has read its q rows back
   stage(ic<0>{}, 0);
   tile_sync_all();
-  auto run = [&](auto body, int ka, int kb_) {
+  auto run = [&](auto body, int ka, int kb_) __attribute__((always_inline)) {
     int kt = ka;
     if (kt <= kb_ && ((kt - kt0) & 1)) {
       body(ic<1>{}, kt);
@@ -789,7 +803,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       tile_sync();
     }
   };
-  auto one = [&](auto body, int kt) {
+  auto one = [&](auto body, int kt) __attribute__((always_inline)) {
     if ((kt - kt0) & 1) body(ic<1>{}, kt); else body(ic<0>{}, kt);
     tile_sync();
   };
@@ -801,7 +815,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   const bool aligned = hpw == 1 && p.W >= C::BN && tw0 <= q_last &&
                        (p.W % C::BN == 0 || p.W >= tw0 + C::BN);
   // calls f(ic<H>) with the half of the tile where the wave's positions start
-  auto with_half = [&](auto f) {
+  auto with_half = [&](auto f) __attribute__((always_inline)) {
     if constexpr (C::CB == 1) {
       if ((tw0 / 32) & 1) f(ic<1>{}); else f(ic<0>{});
     } else {
@@ -900,7 +914,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   float qv[D];
   {
     const float* qrow = qg + (((size_t)b * p.T + tc) * p.H + h) * D;
-    const float2* trow = p.tabq + (size_t)tc * (D / 2);
+    const float2* trow = reinterpret_cast<const float2*>(p.tabq) + (size_t)tc * (D / 2);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
@@ -1019,7 +1033,7 @@ hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* 
   a.kp = kp;
   a.v = v;
   a.o = o;
-  a.tabq = (const float2*)tabq;
+  a.tabq = tabq;
   a.B = B;
   a.T = T;
   a.H = H;

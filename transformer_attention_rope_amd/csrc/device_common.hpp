@@ -27,6 +27,19 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Round-to-nearest-even pack of two floats into fp16x2, and its widenings.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  f16x2_t r = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float h_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[0];
+}
+__device__ __forceinline__ float h_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[1];
+}
+
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

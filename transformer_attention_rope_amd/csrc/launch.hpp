@@ -12,7 +12,7 @@ enum Dtype { kBF16 = 0, kF32 = 1 };
 
 // ---- prefill input stage: k' = RMSNorm(RoPE(k)) in k's layout and type, and
 // ---- the fp32 (cos, sin) table [T][D/2] of positions pos_offset + t for q
-size_t attn_prep_table_bytes(int T, int D);
+size_t attn_prep_table_bytes(int T, int D, Dtype dt);
 size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt);
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
                             double rope_base, int pos_offset, Dtype dt, hipStream_t stream);

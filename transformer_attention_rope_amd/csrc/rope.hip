@@ -18,9 +18,12 @@ namespace nc {
 // ------------------------------------------------------- attention prep
 // Input stage of the prefill forward: k' = RMSNorm(RoPE(k)) for every key row,
 // written once (the attention kernel revisits each key tile for several query
-// tiles and only copies it), and the fp32 (cos, sin) table of every position
-// for the rotation of q rows:
-//   tabq[t][i] = (cos, sin)(p * theta_i),  p = pos_offset + t,  i < D/2.
+// tiles and only copies it), and the (cos, sin) table of every position for
+// the rotation of q rows:
+//   tabq[t][i] = (cos, sin)(p * theta_i),  p = pos_offset + t,  i < D/2,
+// as two fp16 halves of one 32-bit word for bf16 rows (round to nearest:
+// at most 2^-11 relative, a quarter of the bf16 rounding of the rotated q),
+// as two fp32 values for fp32 rows.
 // One workgroup per (position t, block of RB key rows of that position), where
 // the rows of a position are its B*Hkv (sequence, head) pairs and RB rows hold
 // 256*PREP_CPT 16-byte chunks. Each thread issues its (up to PREP_CPT) loads
@@ -40,7 +43,7 @@ constexpr int prep_rows_per_block() {
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
                                                          Elem* __restrict__ kp,
-                                                         float2* __restrict__ tabq, int T,
+                                                         void* __restrict__ tabq, int T,
                                                          int Hkv, int rows, double log2_base,
                                                          int pos_offset, int nrb) {
   constexpr bool kBf = sizeof(Elem) == 2;
@@ -76,7 +79,12 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     float sn, c;
     sincosf((float)r, &sn, &c);
     cs[tid] = make_float2(c, sn);
-    if (r0 == 0) tabq[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
+    if (r0 == 0) {
+      if constexpr (kBf)
+        reinterpret_cast<uint32_t*>(tabq)[(size_t)t * (D / 2) + tid] = pack_h2(c, sn);
+      else
+        reinterpret_cast<float2*>(tabq)[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
+    }
   }
   __syncthreads();
 
@@ -124,7 +132,9 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
   }
 }
 
-size_t attn_prep_table_bytes(int T, int D) { return (size_t)T * (size_t)(D / 2) * sizeof(float2); }
+size_t attn_prep_table_bytes(int T, int D, Dtype dt) {
+  return (size_t)T * (size_t)(D / 2) * (dt == kF32 ? sizeof(float2) : sizeof(uint32_t));
+}
 size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt) {
   return (size_t)B * T * Hkv * D * (dt == kF32 ? 4 : 2);
 }
@@ -139,7 +149,7 @@ static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, i
   const long long nblk = (long long)T * nrb;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_prep_kernel<D, Elem>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                     (const Elem*)k, (Elem*)kp, (float2*)tabq, T, Hkv, (int)rows,
+                     (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
                      std::log2(rope_base), pos_offset, nrb);
   return hipGetLastError();
 }
