@@ -285,6 +285,25 @@ def test_config4_decode_full_size(W):
     _decode_check(q, kn, vn, kc, vc, L, W, torch.bfloat16, f"config 4 W={W}")
 
 
+def test_decode_ranked_placement_with_ties():
+    """Unsplit decode over a long span (workgroups pick their (sequence, head,
+    head group) by visible length): many equal lengths, lengths beyond the
+    window, L = 1, and two query heads per K/V head; every output and the
+    appended rows against the oracle."""
+    _say("decode ranked placement")
+    B, Tmax, H, Hkv, D, W = 64, 1100, 8, 4, 64, 1024  # 256 (b, g) workgroups: no split
+    g = torch.Generator().manual_seed(2024)
+    q = torch.randn(B, H, D, generator=g).bfloat16()
+    kn = torch.randn(B, Hkv, D, generator=g).bfloat16()
+    vn = torch.randn(B, Hkv, D, generator=g).bfloat16()
+    kc = torch.randn(B, Tmax, Hkv, D, generator=g).bfloat16()
+    vc = torch.randn(B, Tmax, Hkv, D, generator=g).bfloat16()
+    pattern = [1, 1100, 700, 700, 64, 1024, 1025, 700, 3, 1100]
+    L = torch.tensor([pattern[i % len(pattern)] for i in range(B)], dtype=torch.int32)
+    assert nc.attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, W) == 0
+    _decode_check(q, kn, vn, kc, vc, L, W, torch.bfloat16, "ranked placement")
+
+
 def test_decode_matches_prefill_gpu():
     """Decode of token L-1 over the prefill's k' and v equals prefill row L-1."""
     _say("decode vs prefill")

@@ -44,8 +44,13 @@ struct DecArgs {
   int C;        // keys per chunk (multiple of the keys per workgroup step)
   int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
   int ngh;      // head groups per K/V head = ceil(G / GP)
+  int ncu;      // compute units of the device
+  int order;    // 1: workgroups take (b, g, head group) items by visible length (below)
   double rope_base;
 };
+
+// Largest batch for which workgroups rank the sequences by length themselves.
+constexpr int kDecRankMaxB = 512;
 
 template <typename Elem>
 struct ElemTraits;
@@ -93,13 +98,20 @@ __device__ __forceinline__ float merge_scale(float m, float mn) {
   return m == -INFINITY ? 0.f : fast_exp2(m - mn);
 }
 
+// Keys per lane group per iteration, and register sets of K/V rows in flight
+// (the loads of iteration it + kDecBufs - 1 go out while iteration it is
+// consumed).
+constexpr int kDecU = 4;
+constexpr int kDecBufs = 2;
+
 template <int D, int GP, typename Elem>
 __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   using TR = ElemTraits<Elem>;
   constexpr int EPC = TR::EPC;
   constexpr int CPR = D / EPC;        // lanes per key row
   constexpr int KPW = 64 / CPR;       // keys per wave per step
-  constexpr int U = 4;                // keys in flight per lane group
+  constexpr int U = kDecU;            // keys per lane group per iteration
+  constexpr int NBUF = kDecBufs;      // register sets: loads run NBUF-1 iterations ahead
   constexpr int KPI = 4 * KPW * U;    // keys per workgroup iteration
 
   __shared__ float qs[GP][D];         // q' * log2(e)/sqrt(D)
@@ -113,8 +125,41 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = (int)blockIdx.x % a.nsplit;
   const int rest = (int)blockIdx.x / a.nsplit;
-  const int hg = rest % a.ngh;
-  const int bg = rest / a.ngh;
+  int hg = rest % a.ngh;
+  int bg = rest / a.ngh;
+  if (a.order) {
+    // Unsplit ranges (nsplit == 1): workgroup i takes the item of rank i (by
+    // the sequence's visible length, longest first, ties by index) while
+    // i < ncu, then rank nitems-1-(i-ncu). Workgroups i and i+ncu are placed
+    // on the same compute unit, which caps the pair's streaming rate, so the
+    // longest ranges share a unit with the shortest and every unit gets a
+    // similar number of bytes.
+    __shared__ int s_len[kDecRankMaxB];
+    __shared__ int s_b;
+    const int per_b = a.Hkv * a.ngh;
+    const int nitems = a.B * per_b;
+    const int i = (int)blockIdx.x;
+    const int r = i < a.ncu ? i : nitems - 1 - (i - a.ncu);
+    const int br = r / per_b;
+    for (int t = tid; t < a.B; t += 256) {
+      const int Lt = clamp_len(a.seqlens[t], a.Tmax);
+      s_len[t] = Lt < a.W ? Lt : a.W;
+    }
+    __syncthreads();
+    for (int t = tid; t < a.B; t += 256) {
+      const int lt = s_len[t];
+      int rk = 0;
+      for (int u = 0; u < a.B; ++u) {
+        const int lu = s_len[u];
+        rk += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+      }
+      if (rk == br) s_b = t;
+    }
+    __syncthreads();
+    const int within = r - br * per_b;
+    hg = within % a.ngh;
+    bg = s_b * a.Hkv + within / a.ngh;
+  }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
 
   const int L = clamp_len(a.seqlens[b], a.Tmax);
@@ -146,8 +191,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base_el, nrec);
   const int slot = wave * KPW + kl;   // key slot within a workgroup step
   const int nkeys = ks1 - ks0;
-  u32x4_t kw[2][U], vw[2][U];
-  auto issue = [&](int it, int set) {
+  u32x4_t kw[NBUF][U], vw[NBUF][U];
+  auto issue = [&](int it, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t off = (uint32_t)(it * KPI + u * 4 * KPW + slot) * row_bytes + cc * 16;
@@ -156,6 +201,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     }
   };
   issue(0, 0);
+  if constexpr (NBUF == 3) issue(1, 1);  // rows past the chunk read as zero
 
   // ---- cos/sin at position pos: the angle is formed and reduced modulo
   // ---- 2*pi in fp64, then evaluated in fp32 on [-pi, pi]
@@ -227,7 +273,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     for (int e = 0; e < EPC; ++e) acc[i][e] = 0.f;
   }
 
-  auto consume = [&](int it, int set) {
+  auto consume = [&](int it, int set) __attribute__((always_inline)) {
     float kx[U][EPC], vx[U][EPC];
     bool live[U];
 #pragma unroll
@@ -279,13 +325,107 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     }
   };
 
+  // bf16 rows: packed math. q' as bf16 pairs (the rounding the prefill MFMAs
+  // use too): a key's score is four v_dot2_f32_bf16 per lane on the raw
+  // 16-byte piece; the weights of two keys are packed as a bf16 pair, and
+  // one v_perm_b32 plus one dot2 per dimension adds both keys' V to the fp32
+  // accumulator; the row sum takes the same rounded weights. Half the vector
+  // instructions of the widening path, which bounds the loop.
+  constexpr bool kPacked = EPC == 8;
+  uint32_t qv2[GP][kPacked ? 4 : 1];
+  if constexpr (kPacked) {
+#pragma unroll
+    for (int i = 0; i < GP; ++i)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) qv2[i][mm] = pack_bf2(qv[i][2 * mm], qv[i][2 * mm + 1]);
+  }
+  // the iteration that holds key pos (only in the chunk that owns it)
+  const int it_pos = owns_new ? (pos - ks0) / KPI : -1;
+  auto consume_packed = [&](int it, int set, auto) __attribute__((always_inline)) {  // generic: only built for bf16
+    static_assert(U % 2 == 0, "keys are paired");
+    u32x4_t kq[U], vq[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      live[u] = ks0 + it * KPI + u * 4 * KPW + slot < ks1;
+      kq[u] = kw[set][u];
+      vq[u] = vw[set][u];
+    }
+    if (it == it_pos) {  // the appended row, from LDS (its cache row may not be written yet)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ks0 + it * KPI + u * 4 * KPW + slot == pos) {
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            kq[u][mm] = pack_bf2(knew_s[cc * 8 + 2 * mm], knew_s[cc * 8 + 2 * mm + 1]);
+            vq[u][mm] = pack_bf2(vnew_s[cc * 8 + 2 * mm], vnew_s[cc * 8 + 2 * mm + 1]);
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      if (i >= nh) break;
+      float sc[U];
+      float mx = m[i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float sd = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) sd = dot2bf(kq[u][mm], qv2[i][mm], sd);
+        sd = lane_group_sum<CPR>(sd);
+        sc[u] = live[u] ? sd : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      if (mx == -INFINITY) continue;  // no live key for this lane group yet
+      const float alpha = merge_scale(m[i], mx);
+      uint32_t pp[U / 2];
+#pragma unroll
+      for (int u2 = 0; u2 < U / 2; ++u2)  // 2^-inf = 0 for dead slots
+        pp[u2] = pack_bf2(fast_exp2(sc[2 * u2] - mx), fast_exp2(sc[2 * u2 + 1] - mx));
+      float li = l[i] * alpha;
+#pragma unroll
+      for (int u2 = 0; u2 < U / 2; ++u2) li = dot2bf(pp[u2], 0x3F803F80u, li);  // (1, 1)
+      l[i] = li;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[i][e] *= alpha;
+#pragma unroll
+      for (int u2 = 0; u2 < U / 2; ++u2)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const uint32_t va = vq[2 * u2][mm], vb = vq[2 * u2 + 1][mm];
+          // (key 2u2, key 2u2+1) of dims 2mm and 2mm+1
+          const uint32_t lo = __builtin_amdgcn_perm(vb, va, 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(vb, va, 0x07060302u);
+          acc[i][2 * mm] = dot2bf(lo, pp[u2], acc[i][2 * mm]);
+          acc[i][2 * mm + 1] = dot2bf(hi, pp[u2], acc[i][2 * mm + 1]);
+        }
+      m[i] = mx;
+    }
+  };
+  auto step = [&](int it, int set) __attribute__((always_inline)) {
+    if constexpr (kPacked) consume_packed(it, set, 0); else consume(it, set);
+  };
+
   const int niter = (nkeys + KPI - 1) / KPI;
-  for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) issue(it + 1, 1);
-    consume(it, 0);
-    if (it + 1 >= niter) break;
-    if (it + 2 < niter) issue(it + 2, 0);
-    consume(it + 1, 1);
+  if constexpr (NBUF == 2) {
+    for (int it = 0; it < niter; it += 2) {
+      if (it + 1 < niter) issue(it + 1, 1);
+      step(it, 0);
+      if (it + 1 >= niter) break;
+      if (it + 2 < niter) issue(it + 2, 0);
+      step(it + 1, 1);
+    }
+  } else {
+    for (int it = 0; it < niter; it += 3) {
+      if (it + 2 < niter) issue(it + 2, 2);
+      step(it, 0);
+      if (it + 1 >= niter) break;
+      if (it + 3 < niter) issue(it + 3, 0);
+      step(it + 1, 1);
+      if (it + 2 >= niter) break;
+      if (it + 4 < niter) issue(it + 4, 1);
+      step(it + 2, 2);
+    }
   }
 
   // ---- merge the key slots of a wave (lanes kl differ by multiples of CPR)
@@ -408,7 +548,7 @@ static int decode_gp(int G) { return G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8)
 
 static int decode_kpi(int D, bool bf16) {
   const int cpr = D / (bf16 ? 8 : 4);
-  return 4 * (64 / cpr) * 4;  // waves * keys per wave step * keys in flight
+  return 4 * (64 / cpr) * kDecU;  // waves * keys per wave step * keys per lane group
 }
 
 static int decode_chunk(int B, int Tmax, int H, int Hkv, int D, int W) {
@@ -427,6 +567,19 @@ static int decode_chunk(int B, int Tmax, int H, int Hkv, int D, int W) {
   long long c = 2 * kpi;
   while (c < whole && nbg * ((span + c - 1) / c) > 1024) c <<= 1;
   return (int)(c < whole ? c : whole);
+}
+
+// Compute units of the current device, queried once per device.
+static int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 static int decode_nsplit(int Tmax, int W, int C) {
@@ -483,6 +636,11 @@ hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_ne
   a.nsplit = decode_nsplit(Tmax, window, a.C);
   a.rope_base = rope_base;
   a.part = (float*)ws;
+  a.ncu = device_cu_count();
+  // Ranking costs each workgroup one more dependent round trip; it pays where
+  // visible lengths can differ by more than a few hundred keys.
+  const int span = window < Tmax ? window : Tmax;
+  a.order = (a.nsplit == 1 && B <= kDecRankMaxB && a.ncu > 0 && span >= 1024) ? 1 : 0;
   const bool bf = dt == kBF16;
   switch (D) {
     case 32: return bf ? decode_d<32, uint16_t>(a, stream) : decode_d<32, float>(a, stream);
