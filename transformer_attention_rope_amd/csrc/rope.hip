@@ -35,10 +35,11 @@ namespace nc {
 // squares across lanes. k' keeps k's layout (B, T, Hkv, D) and element type.
 constexpr int PREP_CPT = 4;  // 16-byte chunks per thread
 
-template <int D, typename Elem>
+template <int D, typename Elem, int CPT = PREP_CPT>
 constexpr int prep_rows_per_block() {
-  return 256 * PREP_CPT / (D / (sizeof(Elem) == 2 ? 8 : 4));
+  return 256 * CPT / (D / (sizeof(Elem) == 2 ? 8 : 4));
 }
+constexpr int ROPE_CPT = 8;  // chunks per thread of rope_qknorm_kernel
 
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
@@ -173,72 +174,76 @@ hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, i
 }
 
 // --------------------------------------------------------- rope + qknorm
-// One workgroup per (position t, block of up to BB batch rows). Every (b, t)
-// has H + Hkv rows of D elements; each thread owns 16-byte chunks, the CPR
-// chunks of one row sit in consecutive lanes and reduce their sum of squares
-// with cross-lane adds. The D/2 (cos, sin) pairs of the position are formed
-// once per workgroup in LDS. In-place use (out == in) is safe: each thread
-// writes back exactly the chunk it read.
+// Same structure as the input stage above. One workgroup per (position t,
+// block of RB rows of that position), where the rows of a position are its
+// B*(H + Hkv) (sequence, q head or k head) pairs. Each thread issues its (up
+// to ROPE_CPT) 16-byte loads first; meanwhile the first D/2 threads form the
+// angles (fp64, exp2 of the scaled log2 base, two-constant Cody-Waite
+// reduction modulo 2*pi, sincosf on [-pi, pi]). The CPR chunks of a row sit
+// in consecutive lanes and reduce their sum of squares across lanes.
+// In-place use (out == in) is safe: each thread writes back exactly the
+// chunks it read.
 template <int D, typename Elem>
-__global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* __restrict__ q,
-                                                           const Elem* __restrict__ k,
-                                                           Elem* q_out, Elem* k_out, int B, int T,
-                                                           int H, int Hkv, double rope_base,
-                                                           int pos_offset, int BB, int nbb) {
+__global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* q, const Elem* k,  // may alias
+                                                           Elem* q_out, Elem* k_out, int T, int H,
+                                                           int Hkv, int rows, double log2_base,
+                                                           int pos_offset, int nrb) {
   constexpr bool kBf = sizeof(Elem) == 2;
   constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;      // chunks per row
+  constexpr int RB = prep_rows_per_block<D, Elem, ROPE_CPT>();
+  static_assert(64 % CPR == 0, "a row's chunks stay inside one wave");
   __shared__ float2 cs[D / 2];
 
-  const int t = (int)blockIdx.x / nbb;
-  const int b0 = ((int)blockIdx.x - t * nbb) * BB;
-  const int nb = min(BB, B - b0);
+  const int t = (int)blockIdx.x / nrb;
+  const int r0 = ((int)blockIdx.x - t * nrb) * RB;
+  const int total = min(RB, rows - r0) * CPR;  // whole rows only
   const int tid = threadIdx.x;
+  const int R = H + Hkv;
+
+  u32x4_t w[ROPE_CPT];
+  size_t off[ROPE_CPT];
+  bool isq[ROPE_CPT];
+#pragma unroll
+  for (int p = 0; p < ROPE_CPT; ++p) {
+    const int ci = p * 256 + tid;
+    const int row = r0 + ci / CPR;
+    const int cc = ci % CPR;
+    const int bb = row / R, rr = row - bb * R;
+    isq[p] = rr < H;
+    off[p] = isq[p] ? (((size_t)bb * T + t) * H + rr) * D + (size_t)cc * EPC
+                    : (((size_t)bb * T + t) * Hkv + (rr - H)) * D + (size_t)cc * EPC;
+    if (ci < total) w[p] = ld16(isq[p] ? q + off[p] : k + off[p]);
+  }
+
   if (tid < D / 2) {
-    const double theta = pow(rope_base, -2.0 * (double)tid / D);
-    double s, c;
-    sincos((double)(pos_offset + t) * theta, &s, &c);
-    cs[tid] = make_float2((float)c, (float)s);
+    const double theta = exp2(-(double)tid / (D / 2) * log2_base);
+    const double a = (double)(pos_offset + t) * theta;
+    const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
+    double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
+    r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
+    float sn, c;
+    sincosf((float)r, &sn, &c);
+    cs[tid] = make_float2(c, sn);
   }
   __syncthreads();
 
-  const int R = H + Hkv;
-  const int total = nb * R * CPR;
-  const int passes = (total + 255) / 256;
-  for (int it = 0; it < passes; ++it) {
-    const int ci = it * 256 + tid;
-    const bool ok = ci < total;
-    const int row = ok ? ci / CPR : 0;
-    const int cc = ci - row * CPR;
-    const int bb = row / R, rr = row - bb * R;
-    const int b = b0 + bb;
-    const Elem* src;
-    Elem* dst;
-    if (rr < H) {
-      const size_t off = (((size_t)b * T + t) * H + rr) * D + (size_t)cc * EPC;
-      src = q + off;
-      dst = q_out + off;
-    } else {
-      const size_t off = (((size_t)b * T + t) * Hkv + (rr - H)) * D + (size_t)cc * EPC;
-      src = k + off;
-      dst = k_out + off;
-    }
+#pragma unroll
+  for (int p = 0; p < ROPE_CPT; ++p) {
+    const int ci = p * 256 + tid;
+    if (p * 256 >= total) break;  // uniform across the workgroup
+    const bool ok = ci < total;   // uniform across the CPR lanes of a row
+    const int cc = ci % CPR;
     float x[EPC];
-    if (ok) {
-      const u32x4_t w = ld16(src);
-      if constexpr (kBf) {
+    if constexpr (kBf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          x[2 * m] = bf_lo(w[m]);
-          x[2 * m + 1] = bf_hi(w[m]);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) x[m] = __uint_as_float(w[m]);
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] = ok ? bf_lo(w[p][m]) : 0.f;
+        x[2 * m + 1] = ok ? bf_hi(w[p][m]) : 0.f;
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < EPC; ++m) x[m] = 0.f;
+      for (int m = 0; m < 4; ++m) x[m] = ok ? __uint_as_float(w[p][m]) : 0.f;
     }
     float ss = 0.f;
 #pragma unroll
@@ -254,43 +259,44 @@ __global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* __restrict
     ss = group_sum<CPR>(ss);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kEps);
     if (ok) {
-      u32x4_t w;
+      u32x4_t o;
       if constexpr (kBf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
+        for (int m = 0; m < 4; ++m) o[m] = pack_bf2(x[2 * m] * inv, x[2 * m + 1] * inv);
       } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = __float_as_uint(x[m] * inv);
+        for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
-      st16(dst, w);
+      st16(isq[p] ? q_out + off[p] : k_out + off[p], o);
     }
   }
+}
+
+template <int D, typename Elem>
+static hipError_t rope_qknorm_launch(const void* q, const void* k, void* q_out, void* k_out, int B,
+                                     int T, int H, int Hkv, double rope_base, int pos_offset,
+                                     hipStream_t stream) {
+  constexpr int RB = prep_rows_per_block<D, Elem, ROPE_CPT>();
+  const long long rows = (long long)B * (H + Hkv);
+  if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int nrb = (int)((rows + RB - 1) / RB);
+  const long long nblk = (long long)T * nrb;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((rope_qknorm_kernel<D, Elem>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, T, H, Hkv,
+                     (int)rows, std::log2(rope_base), pos_offset, nrb);
+  return hipGetLastError();
 }
 
 template <int D>
 static hipError_t rope_qknorm_d(const void* q, const void* k, void* q_out, void* k_out, int B,
                                 int T, int H, int Hkv, double rope_base, int pos_offset, Dtype dt,
                                 hipStream_t stream) {
-  // Enough rows per workgroup to amortise the per-position angles, while
-  // keeping at least T * ceil(B / BB) workgroups.
-  const int rows_per_b = H + Hkv;
-  int BB = (64 + rows_per_b - 1) / rows_per_b;
-  if (BB > B) BB = B;
-  if (BB < 1) BB = 1;
-  const int nbb = (B + BB - 1) / BB;
-  const long long nblk = (long long)T * nbb;
-  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)nblk);
-  if (dt == kBF16) {
-    hipLaunchKernelGGL((rope_qknorm_kernel<D, uint16_t>), grid, dim3(256), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (uint16_t*)q_out,
-                       (uint16_t*)k_out, B, T, H, Hkv, rope_base, pos_offset, BB, nbb);
-  } else {
-    hipLaunchKernelGGL((rope_qknorm_kernel<D, float>), grid, dim3(256), 0, stream,
-                       (const float*)q, (const float*)k, (float*)q_out, (float*)k_out, B, T, H,
-                       Hkv, rope_base, pos_offset, BB, nbb);
-  }
-  return hipGetLastError();
+  if (dt == kBF16)
+    return rope_qknorm_launch<D, uint16_t>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset,
+                                           stream);
+  return rope_qknorm_launch<D, float>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset,
+                                      stream);
 }
 
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
