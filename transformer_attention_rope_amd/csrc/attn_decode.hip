@@ -29,6 +29,8 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <cmath>
+
 namespace nc {
 
 struct DecArgs {
@@ -46,7 +48,7 @@ struct DecArgs {
   int ngh;      // head groups per K/V head = ceil(G / GP)
   int ncu;      // compute units of the device
   int order;    // 1: workgroups take (b, g, head group) items by visible length (below)
-  double rope_base;
+  double log2_base;  // log2(rope_base)
 };
 
 // Largest batch for which workgroups rank the sequences by length themselves.
@@ -127,6 +129,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int rest = (int)blockIdx.x / a.nsplit;
   int hg = rest % a.ngh;
   int bg = rest / a.ngh;
+  __shared__ int s_len[kDecRankMaxB];  // clamped lengths (ranked placement only)
   if (a.order) {
     // Unsplit ranges (nsplit == 1): workgroup i takes the item of rank i (by
     // the sequence's visible length, longest first, ties by index) while
@@ -134,23 +137,19 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     // on the same compute unit, which caps the pair's streaming rate, so the
     // longest ranges share a unit with the shortest and every unit gets a
     // similar number of bytes.
-    __shared__ int s_len[kDecRankMaxB];
     __shared__ int s_b;
     const int per_b = a.Hkv * a.ngh;
     const int nitems = a.B * per_b;
     const int i = (int)blockIdx.x;
     const int r = i < a.ncu ? i : nitems - 1 - (i - a.ncu);
     const int br = r / per_b;
-    for (int t = tid; t < a.B; t += 256) {
-      const int Lt = clamp_len(a.seqlens[t], a.Tmax);
-      s_len[t] = Lt < a.W ? Lt : a.W;
-    }
+    for (int t = tid; t < a.B; t += 256) s_len[t] = clamp_len(a.seqlens[t], a.Tmax);
     __syncthreads();
     for (int t = tid; t < a.B; t += 256) {
-      const int lt = s_len[t];
+      const int lt = min(s_len[t], a.W);  // visible keys
       int rk = 0;
       for (int u = 0; u < a.B; ++u) {
-        const int lu = s_len[u];
+        const int lu = min(s_len[u], a.W);
         rk += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
       }
       if (rk == br) s_b = t;
@@ -162,7 +161,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
 
-  const int L = clamp_len(a.seqlens[b], a.Tmax);
+  const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], a.Tmax);
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
   const int nch = (L - lo + a.C - 1) / a.C;
@@ -203,10 +202,36 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   issue(0, 0);
   if constexpr (NBUF == 3) issue(1, 1);  // rows past the chunk read as zero
 
+  // ---- the rows this wave rotates (q heads, then the appended k row, one
+  // ---- wave per row, one (even, odd) pair per lane; D/2 <= 64) and v_new:
+  // ---- loaded now, so that their latency overlaps the K/V loads and the angles
+  const float qscale = kLog2e / sqrtf((float)D);
+  const int nrows = nh + (owns_new ? 1 : 0);
+  constexpr int MAXR = (GP + 1 + 3) / 4;  // rows per wave
+  float rx[MAXR][2];
+  Elem vn0 = Elem(0), vn1 = Elem(0);
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int r = wave + 4 * j;
+    rx[j][0] = rx[j][1] = 0.f;
+    if (r < nrows && lane < D / 2) {
+      const bool is_k = r == nh;
+      const Elem* src = is_k ? (const Elem*)a.k_new + ((size_t)b * a.Hkv + g) * D
+                             : qg + ((size_t)b * a.H + h0 + r) * D;
+      rx[j][0] = TR::to_f(src[2 * lane]);
+      rx[j][1] = TR::to_f(src[2 * lane + 1]);
+      if (is_k) {
+        const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
+        vn0 = vsrc[2 * lane];
+        vn1 = vsrc[2 * lane + 1];
+      }
+    }
+  }
+
   // ---- cos/sin at position pos: the angle is formed and reduced modulo
   // ---- 2*pi in fp64, then evaluated in fp32 on [-pi, pi]
   if (tid < D / 2) {
-    const double theta = exp2(-(double)tid / (D / 2) * log2(a.rope_base));
+    const double theta = exp2(-(double)tid / (D / 2) * a.log2_base);
     const double ang = (double)pos * theta;
     const double kq = rint(ang * 0.15915494309189535);
     double r = fma(-kq, 6.283185307179586, ang);
@@ -217,18 +242,16 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   __syncthreads();
 
-  // ---- q' for the nh heads, and the appended row if this chunk owns it:
-  // one wave per row, one (even, odd) pair per lane (D/2 <= 64)
-  const float qscale = kLog2e / sqrtf((float)D);
-  const int nrows = nh + (owns_new ? 1 : 0);
-  for (int r = wave; r < nrows; r += 4) {
+  // ---- q' for the nh heads, and the appended row if this chunk owns it
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int r = wave + 4 * j;
+    if (r >= nrows) break;  // uniform across the wave
     const bool is_k = r == nh;
-    const Elem* src = is_k ? (const Elem*)a.k_new + ((size_t)b * a.Hkv + g) * D
-                           : qg + ((size_t)b * a.H + h0 + r) * D;
     const int i = lane;  // pair index
     float ye = 0.f, yo = 0.f;
     if (i < D / 2) {
-      const float xe = TR::to_f(src[2 * i]), xo = TR::to_f(src[2 * i + 1]);
+      const float xe = rx[j][0], xo = rx[j][1];
       const float2 c = cs[i];
       ye = xe * c.x - xo * c.y;
       yo = xe * c.y + xo * c.x;
@@ -243,9 +266,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
         Elem* dst = kc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
         dst[2 * i] = ke;
         dst[2 * i + 1] = ko;
-        const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
         Elem* vdst = vc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
-        const Elem v0 = vsrc[2 * i], v1 = vsrc[2 * i + 1];
+        const Elem v0 = vn0, v1 = vn1;
         vdst[2 * i] = v0;
         vdst[2 * i + 1] = v1;
         vnew_s[2 * i] = TR::to_f(v0);
@@ -634,7 +656,7 @@ hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_ne
   a.W = window;
   a.C = decode_chunk(B, Tmax, H, Hkv, D, window);
   a.nsplit = decode_nsplit(Tmax, window, a.C);
-  a.rope_base = rope_base;
+  a.log2_base = std::log2(rope_base);
   a.part = (float*)ws;
   a.ncu = device_cu_count();
   // Ranking costs each workgroup one more dependent round trip; it pays where
