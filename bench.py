@@ -17,6 +17,8 @@ The same run also times, with HIP events on the launch stream:
   * the split-KV decode over a 2048-slot cache (B=64, H=Hkv=6, D=128) at
     window 512 and 2048, as HBM GB/s of algorithmic bytes;
   * ``nc_rope_qknorm`` on the d12 q and k, as HBM GB/s;
+  * a 1 GiB device-to-device copy (torch), the practical HBM reference that the
+    decode and rope figures are also given against (``frac_copy``);
   * the d12 SSSL and GQA SSSL stacks (4 ``nc_attn_fwd`` layer calls);
 and, on the host, the fp64 oracle on a bounded sample (``cpu_baseline``).
 
@@ -234,6 +236,21 @@ def main():
         print(json.dumps(out))
         return
 
+    # --------------------------------------- device copy (HBM reference)
+    copy_gbs = None
+    if args.only in ("all", "decode", "rope"):
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+
+        def cstep(i):
+            dst.copy_(src)
+
+        settle(cstep, args.settle_ms, torch)
+        cms = event_time_ms(cstep, 20, torch)
+        copy_gbs = 2 * n / (cms * 1e-3) / 1e9  # bytes read + written
+        del src, dst
+
     # ------------------------------------------------------------ decode
     dec = {}
     if args.only in ("all", "decode"):
@@ -256,6 +273,7 @@ def main():
             gbs = nbytes / (ms * 1e-3) / 1e9
             dec[f"W{Wd}"] = {"us_per_call": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
                              "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                             "frac_copy": round(gbs / copy_gbs, 4),
                              "algorithmic_bytes": int(nbytes)}
         del dsets
         if args.only == "decode":
@@ -281,7 +299,8 @@ def main():
         gbs = nbytes / (ms * 1e-3) / 1e9
         rope = {"workload": "q,k of the d12 layer (8x2048x6x128 each), bf16, read + write",
                 "us_per_call": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
-                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "frac_copy": round(gbs / copy_gbs, 4)}
         del rsets
         if args.only == "rope":
             print(json.dumps(rope))
@@ -344,6 +363,7 @@ def main():
                      "kernel": "attn_fwd_bf16_kernel<128, 4>",
                      "kernel_us": round(out["kern_ms"] * 1e3, 2),
                      "flops_per_launch": flops},
+        "device_copy_GB_per_s": round(copy_gbs, 1) if copy_gbs else None,
         "decode": dec,
         "rope_qknorm": rope,
         "stacks": stacks,
