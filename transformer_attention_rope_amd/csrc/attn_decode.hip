@@ -195,8 +195,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t off = (uint32_t)(it * KPI + u * 4 * KPW + slot) * row_bytes + cc * 16;
-      kw[set][u] = bload16(rk, off, 0);
-      vw[set][u] = bload16(rv, off, 0);
+      kw[set][u] = bload16_nt(rk, off, 0);
+      vw[set][u] = bload16_nt(rv, off, 0);
     }
   };
   issue(0, 0);

@@ -426,8 +426,8 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   auto v_pair = [&](auto Sc, int j, int m, uint16_t* vb) __attribute__((always_inline)) {
     constexpr int S = decltype(Sc)::value;
     const uint32_t a0 = vw[S][j][0][m], a1 = vw[S][j][1][m], a2 = vw[S][j][2][m], a3 = vw[S][j][3][m];
-    const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-    const u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+    const u32x2_t lo = {lo_halves(a0, a1), lo_halves(a2, a3)};
+    const u32x2_t hi = {hi_halves(a0, a1), hi_halves(a2, a3)};
     st8(vb + v_lds[j] + (2 * m) * C::VLD, lo);
     st8(vb + v_lds[j] + (2 * m + 1) * C::VLD, hi);
   };
@@ -686,10 +686,10 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
           constexpr int SS = sset(P);
           const uint32_t a0 = vw[SS][j][0][m], a1 = vw[SS][j][1][m];
           const uint32_t a2 = vw[SS][j][2][m], a3 = vw[SS][j][3][m];
-          vtmp[j][m][0] = (a0 & 0xffffu) | (a1 << 16);
-          vtmp[j][m][1] = (a2 & 0xffffu) | (a3 << 16);
-          vtmp[j][m][2] = (a0 >> 16) | (a1 & 0xffff0000u);
-          vtmp[j][m][3] = (a2 >> 16) | (a3 & 0xffff0000u);
+          vtmp[j][m][0] = lo_halves(a0, a1);
+          vtmp[j][m][1] = lo_halves(a2, a3);
+          vtmp[j][m][2] = hi_halves(a0, a1);
+          vtmp[j][m][3] = hi_halves(a2, a3);
 #pragma unroll
           for (int x = 0; x < 4; ++x) pin(vtmp[j][m][x]);
         } else {
@@ -880,7 +880,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       int tr, hr;
       col_row(r, tr, hr);
       const u32x4_t w = ld16(os + r * C::QLD + qc * 8);
-      if (tr < p.T) st16(og + (((size_t)b * p.T + tr) * p.H + hr) * D + qc * 8, w);
+      if (tr < p.T) st16_nt(og + (((size_t)b * p.T + tr) * p.H + hr) * D + qc * 8, w);
     }
   }
 }

@@ -27,6 +27,15 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// The low 16-bit halves of a and b as one word (a's in the low half), and
+// the high halves likewise: one v_perm_b32 each.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 // Round-to-nearest-even pack of two floats into fp16x2, and its widenings.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
@@ -45,6 +54,12 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
+}
+// Store with the non-temporal hint: for results nothing in the same kernel
+// reads back, so they leave the cache promptly instead of being written back
+// when the kernel ends.
+__device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }
 __device__ __forceinline__ void st8(void* p, u32x2_t v) {
   *reinterpret_cast<u32x2_t*>(p) = v;
@@ -110,6 +125,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// The same with the non-temporal hint (cache policy bit 1), for data read
+// once: it does not push reused lines out of the caches.
+__device__ __forceinline__ u32x4_t bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
 }
 __device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));

@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* q, const E
 #pragma unroll
         for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
-      st16(isq[p] ? q_out + off[p] : k_out + off[p], o);
+      st16_nt(isq[p] ? q_out + off[p] : k_out + off[p], o);
     }
   }
 }
