@@ -52,6 +52,10 @@ __device__ __forceinline__ float h_hi(uint32_t w) {
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+// The same with the non-temporal hint, for rows read once.
+__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }

@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     const int cc = ci % CPR;
     const int bb = row / Hkv, g = row - bb * Hkv;
     off[p] = (((size_t)bb * T + t) * Hkv + g) * D + (size_t)cc * EPC;
-    if (ci < total) w[p] = ld16(k + off[p]);
+    if (ci < total) w[p] = ld16_nt(k + off[p]);
   }
 
   if (tid < D / 2) {
