@@ -64,6 +64,12 @@ SMALL_BF16 = [
     (2, 513, 4, 4, 64, 256, 3),
     (1, 300, 1, 1, 32, 192, 0),
     (1, 1100, 1, 1, 128, 64, 0),
+    # eight query heads per K/V head at D = 128 (32 positions x 8 heads per
+    # workgroup, generic masked path), and a long sequence whose window is a
+    # multiple of 64 but shorter than T (window-edge tiles on every wave)
+    (2, 400, 8, 1, 128, 200, 0),
+    (1, 2048, 2, 2, 128, 1024, 0),
+    (1, 1000, 4, 4, 64, 320, 0),
 ]
 
 
