@@ -101,10 +101,13 @@ __device__ __forceinline__ float merge_scale(float m, float mn) {
 }
 
 // Keys per lane group per iteration, and register sets of K/V rows in flight
-// (the loads of iteration it + kDecBufs - 1 go out while iteration it is
-// consumed).
+// (the loads of iteration it + NBUF - 1 go out while iteration it is
+// consumed; the loop below is written for 2 and 3 sets): three, except with
+// 8 query heads per workgroup, where the third set would take the kernel past
+// 256 registers and so to one wave per SIMD.
 constexpr int kDecU = 4;
-constexpr int kDecBufs = 2;
+template <int GP>
+constexpr int dec_bufs() { return GP <= 4 ? 3 : 2; }
 
 template <int D, int GP, typename Elem>
 __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
@@ -113,7 +116,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   constexpr int CPR = D / EPC;        // lanes per key row
   constexpr int KPW = 64 / CPR;       // keys per wave per step
   constexpr int U = kDecU;            // keys per lane group per iteration
-  constexpr int NBUF = kDecBufs;      // register sets: loads run NBUF-1 iterations ahead
+  constexpr int NBUF = dec_bufs<GP>();  // register sets: loads run NBUF-1 iterations ahead
+  static_assert(NBUF == 2 || NBUF == 3, "register sets in flight");
   constexpr int KPI = 4 * KPW * U;    // keys per workgroup iteration
 
   __shared__ float qs[GP][D];         // q' * log2(e)/sqrt(D)
