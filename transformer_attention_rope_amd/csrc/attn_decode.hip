@@ -14,8 +14,9 @@
 // Design: decode reads every visible K/V row once, so it is bound by HBM.
 // A workgroup owns (sequence b, K/V head g, up to GP query heads of g, a chunk
 // of C consecutive keys). CPR lanes stream one 16-byte piece of a K row and of
-// a V row per key, so a wave reads whole rows with unit-stride loads; each
-// lane group keeps U keys in flight per iteration and rescales its running
+// a V row per key, so a wave reads whole rows with unit-stride loads (with the
+// non-temporal hint: each row is read once); each lane group takes U keys per
+// iteration, with loads up to two iterations ahead, and rescales its running
 // softmax state once per U keys (the scores of cache rows are not assumed
 // bounded, so this path keeps a running maximum). Partial (max, sum,
 // unnormalised output) states are merged across lanes with DPP/shuffles and
@@ -183,8 +184,9 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
 
   // ---- the chunk's K/V rows as buffer loads relative to key ks0; rows past
   // ---- ks1 (the chunk end) read as zero and are masked out of the softmax.
-  // ---- The first iteration's loads are issued before the RoPE prologue so
-  // ---- that their latency overlaps it; later iterations are double-buffered.
+  // ---- The first iterations' loads are issued before the RoPE prologue so
+  // ---- that their latency overlaps it; later ones run NBUF-1 iterations
+  // ---- ahead of their use, in NBUF register sets.
   const int cc = lane % CPR;        // 16-byte piece within the row
   const int kl = lane / CPR;        // key slot within the wave
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * sizeof(Elem);
@@ -582,7 +584,7 @@ static int decode_chunk(int B, int Tmax, int H, int Hkv, int D, int W) {
   // a split range pays a merge pass, so a visible range is split only when
   // there are fewer (b, K/V head, head group) workgroups than compute units;
   // then chunks are sized for about 1024 workgroups, at least two workgroup
-  // iterations each so that the double-buffered loads overlap.
+  // iterations each so that the loads run ahead of their use.
   const int G = H / Hkv;
   const int ngh = (G + decode_gp(G) - 1) / decode_gp(G);
   const int kpi = decode_kpi(D, true);
