@@ -93,10 +93,12 @@ struct FwdArgs {
 // =====================================================================
 template <int D, int NW_ = 4>
 struct BfCfg {
-  static constexpr int NW = NW_;           // waves per workgroup: 4 (one per SIMD) or 8 (two)
+  // waves per workgroup: 4 (one per SIMD), 2 (one per SIMD, two workgroups
+  // per compute unit) or 8 (two per SIMD)
+  static constexpr int NW = NW_;
   static constexpr int NT = 64 * NW;       // threads per workgroup
-  static constexpr int CB = 8 / NW;        // 32-column blocks per wave (256 columns in all)
-  static constexpr int NC = 32 * CB * NW;  // query columns per workgroup
+  static constexpr int CB = NW == 8 ? 1 : 2;  // 32-column blocks per wave
+  static constexpr int NC = 32 * CB * NW;  // query columns per workgroup: 256, or 128 with 2 waves
   static constexpr int BN = 64;            // keys per tile
   static constexpr int KS = D / 16;        // MFMA k-steps of K Q^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -121,11 +123,12 @@ struct BfCfg {
   static constexpr int NKF = RB * KS;
   static constexpr int NF = NKF + PS * DB;
   static constexpr int QR = 32 * CB;       // q / o rows per wave
-  // V register sets: two (tile kt+2 loads while tile kt+1 is transposed)
-  // except with two waves per SIMD at D = 128, where one set (tile kt+1 loads
-  // at the start of tile kt and is transposed at its end) keeps the wave
-  // within 256 registers
-  static constexpr int VS = (NW == 8 && D == 128) ? 1 : 2;
+  // V register sets: two (tile kt+2 loads while tile kt+1 is transposed),
+  // except at D = 128 with two waves per SIMD, or with two waves per
+  // workgroup (two V micro-blocks per thread): there one set (tile kt+1
+  // loads at the start of tile kt and is transposed at its end) keeps the
+  // kernel within its registers without spills
+  static constexpr int VS = ((NW == 8 || NW == 2) && D == 128) ? 1 : 2;
   static constexpr int NQL = QR * CPR / 64;  // 16-byte row chunks per lane for them
 };
 
@@ -762,14 +765,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // across the barrier. The barrier is the bare instruction: the wait is
   // explicit, and the empty asm statements keep the compiler from moving
   // memory accesses across it.
-  static_assert(C::NVB == 1, "one V micro-block per thread");
+  static_assert(4 * C::NVB <= 15, "the V loads of a tile fit the wait count");
   auto wg_barrier = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   auto tile_sync = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (4 * C::NVB));  // vmcnt(4*NVB) lgkmcnt(0)
     wg_barrier();
   };
   // the same after a body that issued no copies or loads (the last tile)
@@ -994,9 +997,31 @@ static int ilog2(int x) {
 // Waves per workgroup of the bf16 kernel: two per SIMD where one column
 // block per wave fits the halved register budget (D <= 64; measured 8-16%
 // faster than one wave per SIMD on the GQA D=64 layers), one per SIMD at
-// D = 128, whose accumulators need more than 256 registers per wave.
+// D = 128, whose accumulators need more than 256 registers per wave. At
+// D = 128 a window of at most half the sequence gives every query tile about
+// the same number of key tiles, and 1.5 tiles of 256 columns per compute unit
+// leave half the units idle for the last round; there two workgroups of 2
+// waves (128 columns each) share a unit instead, so the tiles are half as
+// large, and one workgroup's prologue and epilogue overlap the other's tiles
+// (measured on the d12 W = 512 layer: 48.8 us against 52.4). With the full
+// causal band the longest query tiles set the time either way and the
+// 4-wave form, which splits the staging work four ways, is faster (61.0 us
+// against 64.4).
 template <int D>
 constexpr int fwd_waves() { return D == 128 ? 4 : 8; }
+template <int D>
+static bool fwd_narrow(int T, int W) { return D == 128 && 2 * (long long)W <= T; }
+
+template <int D, int NW>
+static hipError_t launch_bf16(FwdArgs a, int hpw, hipStream_t stream) {
+  using C = BfCfg<D, NW>;
+  a.bp_log2 = ilog2(C::NC / hpw);
+  a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
+  const long long grid = (long long)a.nqt * a.B * a.ngroups;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
 
 template <int D>
 static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
@@ -1007,12 +1032,10 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
     while (hpw < 32 && (a.G % (hpw * 2)) == 0) hpw *= 2;
     a.hpw_log2 = ilog2(hpw);
     a.ngroups = a.H / hpw;
-    a.bp_log2 = ilog2(BfCfg<D, fwd_waves<D>()>::NC / hpw);
-    a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
-    const long long grid = (long long)a.nqt * a.B * a.ngroups;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, fwd_waves<D>()>), dim3((unsigned)grid),
-                       dim3(BfCfg<D, fwd_waves<D>()>::NT), 0, stream, a);
+    if constexpr (D == 128) {
+      if (fwd_narrow<D>(a.T, a.W)) return launch_bf16<D, 2>(a, hpw, stream);
+    }
+    return launch_bf16<D, fwd_waves<D>()>(a, hpw, stream);
   } else {
     a.hpw_log2 = 0;
     a.ngroups = a.H;
