@@ -39,7 +39,7 @@ template <int D, typename Elem, int CPT = PREP_CPT>
 constexpr int prep_rows_per_block() {
   return 256 * CPT / (D / (sizeof(Elem) == 2 ? 8 : 4));
 }
-constexpr int ROPE_CPT = 8;  // chunks per thread of rope_qknorm_kernel
+constexpr int ROPE_CPT = 6;  // chunks per thread of rope_qknorm_kernel (96 d12 rows per workgroup)
 
 template <int D, typename Elem>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
