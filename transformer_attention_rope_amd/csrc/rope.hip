@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
 #pragma unroll
         for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
-      st16(kp + off[p], o);
+      st16_nt(kp + off[p], o);
     }
   }
 }
