@@ -35,6 +35,11 @@ Readings where the pages are silent (each is listed with its pin in the design doc):
     position L - 1; its normalised, rotated key and its raw value are written
     to the cache first, then the query attends to keys
     max(0, L - W) .. L - 1.  Older cache rows are used as stored.
+  * Prefill into the cache (chunked prefill): one pos_offset P for the whole
+    batch; the chunk's T tokens sit at cache rows and positions P .. P+T-1;
+    their normalised, rotated keys and raw values are written there first,
+    then query t (position P + t) attends to cache rows j with
+    0 <= P + t - j < W.  Rows before P are used as stored.
 """
 from __future__ import annotations
 
@@ -192,4 +197,37 @@ def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window: int,
             s = (kc[b, lo:L, g] @ qn[h]) / math.sqrt(D)
             e = np.exp(s - s.max())
             o[b, h] = (e / e.sum()) @ vc[b, lo:L, g]
+    return o, kc, vc
+
+
+def attn_prefill(q, k, v, k_cache, v_cache, window: int, base: float = 10000.0,
+                 pos_offset: int = 0):
+    """Prefill of a chunk of T tokens into a contiguous per-layer cache
+    ([S10] append K/V, then attend; [S5.5] causal mask; [TBL] window).
+
+    q (B,T,H,D), k and v (B,T,Hkv,D) raw rows of the tokens at positions
+    P .. P+T-1 (P = pos_offset); caches (B,Tmax,Hkv,D) with P + T <= Tmax,
+    rows before P used as stored.  Returns (o (B,T,H,D), k_cache_out,
+    v_cache_out), the cache copies holding the chunk's rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    G = H // Hkv
+    P = int(pos_offset)
+    qn, kn = rope_qknorm(q, k, base, P)
+    kc[:, P:P + T] = kn
+    vc[:, P:P + T] = v
+    i = P + np.arange(T)[:, None]          # query positions
+    j = np.arange(P + T)[None, :]          # cache rows, one per key position
+    vis = (i - j >= 0) & (i - j < window)
+    o = np.empty((B, T, H, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            S = (qn[b, :, h] @ kc[b, :P + T, g].T) / math.sqrt(D)
+            S = np.where(vis, S, -np.inf)
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            o[b, :, h] = (E / E.sum(axis=1, keepdims=True)) @ vc[b, :P + T, g]
     return o, kc, vc

@@ -335,4 +335,93 @@ def pin_decode_brute(O):
             _close(o[b, h], want, tol=1e-12, what=f"decode brute b={b} h={h}")
 
 
+# ------------------------------------------------------------ prefill pins
+
+def _prefill_case(seed, B=2, T=13, H=4, Hkv=2, D=8):
+    r = _rng(seed)
+    return (r.standard_normal((B, T, H, D)), r.standard_normal((B, T, Hkv, D)),
+            r.standard_normal((B, T, Hkv, D)))
+
+
+def pin_prefill_chunks_match_fwd(O):
+    """Causality makes chunking invisible: prefilling a sequence chunk by chunk
+    into one cache gives the rows of the whole-sequence forward, and leaves the
+    normalised, rotated keys and the raw values in the cache."""
+    q, k, v = _prefill_case(31)
+    T = q.shape[1]
+    _, kn = O.rope_qknorm(q, k)
+    for W in (1, 3, 5, T):
+        full = O.attn_fwd(q, k, v, W)
+        for cuts in ((0, T), (0, 4, T), (0, 1, 7, 8, T)):
+            kc = np.full((2, T + 3, 2, 8), 5.0)
+            vc = np.full((2, T + 3, 2, 8), -5.0)
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                o, kc, vc = O.attn_prefill(q[:, a:b], k[:, a:b], v[:, a:b], kc, vc, W,
+                                           pos_offset=a)
+                _close(o, full[:, a:b], tol=1e-11, what=f"chunk {a}:{b} W={W}")
+            _close(kc[:, :T], kn, tol=1e-12, what="cached keys")
+            _close(vc[:, :T], v, tol=0, what="cached values")
+
+
+def pin_prefill_then_decode(O):
+    """A prefill of T-1 tokens followed by a decode step of token T-1 gives the
+    last row of the whole-sequence forward."""
+    q, k, v = _prefill_case(32, T=10)
+    T = q.shape[1]
+    for W in (4, T):
+        full = O.attn_fwd(q, k, v, W)
+        kc = np.zeros((2, T, 2, 8))
+        vc = np.zeros((2, T, 2, 8))
+        _, kc, vc = O.attn_prefill(q[:, :T - 1], k[:, :T - 1], v[:, :T - 1], kc, vc, W)
+        o, _, _ = O.attn_decode(q[:, T - 1], k[:, T - 1], v[:, T - 1], kc, vc,
+                                np.full(2, T), W)
+        _close(o, full[:, T - 1], tol=1e-11, what=f"prefill+decode W={W}")
+
+
+def pin_prefill_touches_only_chunk_rows(O):
+    q, k, v = _prefill_case(33, T=5)
+    r = _rng(34)
+    kc0 = r.standard_normal((2, 12, 2, 8))
+    vc0 = r.standard_normal((2, 12, 2, 8))
+    _, kc, vc = O.attn_prefill(q, k, v, kc0, vc0, 4, pos_offset=6)
+    keep = (np.arange(12) < 6) | (np.arange(12) >= 11)
+    _close(kc[:, keep], kc0[:, keep], tol=0, what="k rows kept")
+    _close(vc[:, keep], vc0[:, keep], tol=0, what="v rows kept")
+
+
+def pin_prefill_brute(O):
+    """Chunk at offset P over a cache whose earlier rows are arbitrary (used as
+    stored), against scalar loops over the visible (query, key) pairs."""
+    q, k, v = _prefill_case(35, B=1, T=4, H=2, Hkv=1, D=6)
+    r = _rng(36)
+    P, W, Tmax = 5, 6, 10
+    kc0 = r.standard_normal((1, Tmax, 1, 6))
+    vc0 = r.standard_normal((1, Tmax, 1, 6))
+    o, _, _ = O.attn_prefill(q, k, v, kc0, vc0, W, pos_offset=P)
+
+    def rn(row, p):
+        out = []
+        for i in range(3):
+            a = p * 10000.0 ** (-(2.0 * i) / 6)
+            x, y = row[2 * i], row[2 * i + 1]
+            out += [x * math.cos(a) - y * math.sin(a), x * math.sin(a) + y * math.cos(a)]
+        s = 1.0 / math.sqrt(sum(z * z for z in out) / 6 + 1e-6)
+        return [z * s for z in out]
+    for t in range(4):
+        for h in range(2):
+            qh = rn(list(q[0, t, h]), P + t)
+            ss, vs = [], []
+            for j in range(P + t + 1):
+                if not 0 <= P + t - j < W:
+                    continue
+                kj = rn(list(k[0, j - P, 0]), j) if j >= P else list(kc0[0, j, 0])
+                vj = list(v[0, j - P, 0]) if j >= P else list(vc0[0, j, 0])
+                ss.append(sum(a * c for a, c in zip(qh, kj)) / math.sqrt(6))
+                vs.append(vj)
+            mx = max(ss)
+            ws = [math.exp(s - mx) for s in ss]
+            want = [sum(w * vv[d] for w, vv in zip(ws, vs)) / sum(ws) for d in range(6)]
+            _close(o[0, t, h], want, tol=1e-12, what=f"prefill brute t={t} h={h}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

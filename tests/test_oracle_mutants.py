@@ -125,6 +125,66 @@ def _decode_window_plus_one(q, k_new, v_new, k_cache, v_cache, seqlens, window, 
     return _orig_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window + 1, base)
 
 
+_orig_prefill = R.attn_prefill
+
+
+def _prefill_local_mask(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+    # masks with the chunk-local query index t instead of the position P + t
+    qf, kf, vf = R._f64(q), R._f64(k), R._f64(v)
+    kc, vc = R._f64(k_cache).copy(), R._f64(v_cache).copy()
+    B, T, H, D = qf.shape
+    G = H // kf.shape[2]
+    P = int(pos_offset)
+    qn, kn = R.rope_qknorm(qf, kf, base, P)
+    kc[:, P:P + T] = kn
+    vc[:, P:P + T] = vf
+    i = np.arange(T)[:, None]
+    j = np.arange(P + T)[None, :]
+    vis = (i - j >= 0) & (i - j < window)
+    o = np.empty((B, T, H, D))
+    for b in range(B):
+        for h in range(H):
+            S = np.where(vis, qn[b, :, h] @ kc[b, :P + T, h // G].T / math.sqrt(D), -np.inf)
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            o[b, :, h] = (E / E.sum(axis=1, keepdims=True)) @ vc[b, :P + T, h // G]
+    return o, kc, vc
+
+
+def _shifted_prefill(q, k, v, k_cache, v_cache, window, base, P):
+    qf, kf = R._f64(q), R._f64(k)
+    T = qf.shape[1]
+    qn0, kn0 = R.rope_qknorm(qf, kf, base, 0)
+    kc, vc = R._f64(k_cache).copy(), R._f64(v_cache).copy()
+    kc[:, P:P + T] = kn0
+    vc[:, P:P + T] = R._f64(v)
+    B, _, H, D = qf.shape
+    G = H // kf.shape[2]
+    i = P + np.arange(T)[:, None]
+    j = np.arange(P + T)[None, :]
+    vis = (i - j >= 0) & (i - j < window)
+    o = np.empty((B, T, H, D))
+    for b in range(B):
+        for h in range(H):
+            S = np.where(vis, qn0[b, :, h] @ kc[b, :P + T, h // G].T / math.sqrt(D), -np.inf)
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            o[b, :, h] = (E / E.sum(axis=1, keepdims=True)) @ vc[b, :P + T, h // G]
+    return o, kc, vc
+
+
+def _shifted_prefill_entry(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+    # rotates the chunk as if it started at position 0
+    return _shifted_prefill(q, k, v, k_cache, v_cache, window, base, int(pos_offset))
+
+
+def _prefill_window_plus_one(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+    return _orig_prefill(q, k, v, k_cache, v_cache, window + 1, base, pos_offset)
+
+
+def _prefill_no_v_append(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+    o, kc, _ = _orig_prefill(q, k, v, k_cache, v_cache, window, base, pos_offset)
+    return o, kc, R._f64(v_cache).copy()
+
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign),
     "rope_half_split": ("rope", _rope_half_split),
@@ -142,6 +202,10 @@ MUTANTS = {
     "core_softmax_axis": ("attention_core", _core_variant("softmax_axis")),
     "decode_raw_append": ("attn_decode", _decode_raw_append),
     "decode_window_plus_one": ("attn_decode", _decode_window_plus_one),
+    "prefill_local_mask": ("attn_prefill", _prefill_local_mask),
+    "prefill_rope_from_zero": ("attn_prefill", _shifted_prefill_entry),
+    "prefill_window_plus_one": ("attn_prefill", _prefill_window_plus_one),
+    "prefill_no_v_append": ("attn_prefill", _prefill_no_v_append),
 }
 
 
