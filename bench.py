@@ -158,7 +158,7 @@ def main():
                     help="untimed back-to-back GPU work before each timed part (clock ramp)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "copy"],
+                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -333,6 +333,73 @@ def main():
             print(json.dumps(stacks))
             return
 
+    # ------------------------------------- prefill into the KV cache (chunked)
+    pre = {}
+    if args.only in ("all", "prefill"):
+        ch = wl.CHUNK
+        B, Tc, P, Tmax, H, Hkv, D = ch["B"], ch["T"], ch["P"], ch["Tmax"], ch["H"], ch["Hkv"], ch["D"]
+        psets = []
+        for s_ in range(args.sets):
+            q, k, v, kc, vc = wl.prefill_chunk_inputs(seed=s_)
+            psets.append([t.to(dev) for t in (q, k, v, kc, vc)] + [torch.empty_like(q, device=dev)])
+        wsp = torch.empty(max(nc.attn_prefill_workspace_bytes(Tmax, D, torch.bfloat16), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def tf_entry(ms, fl, **extra):
+            tf = fl / (ms * 1e-3) / 1e12
+            return dict(extra, us_per_call=round(ms * 1e3, 2), TFLOP_per_s=round(tf, 1),
+                        frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+
+        for Wp in (2048, 512):
+            def pstep(i, Wp=Wp):
+                q, k, v, kc, vc, o = psets[i % len(psets)]
+                nc.attn_prefill(q, k, v, kc, vc, window=Wp, pos_offset=P, out=o, workspace=wsp)
+
+            prime(f"prefill_chunk_W{Wp}", pstep)
+            ms = event_time_ms(pstep, K, torch)
+            pre[f"chunk_W{Wp}"] = tf_entry(
+                ms, wl.prefill_chunk_flops(B, Tc, P, H, D, Wp),
+                workload=f"last {Tc}-token chunk at offset {P} of a {Tmax}-token context, "
+                         f"B={B} H=Hkv={H} D={D} window={Wp}: k', v into the caches, then attention")
+        del psets
+        # the whole context: four chunks of 512, and one call of 2048, into the caches
+        full = []
+        for s_ in range(args.sets):
+            q, k, v = wl.prefill_inputs(cfg, layer=s_)
+            kc = torch.empty(B, Tmax, Hkv, D, dtype=torch.bfloat16, device=dev)
+            full.append((q.to(dev), k.to(dev), v.to(dev), kc, torch.empty_like(kc),
+                         torch.empty_like(q, device=dev)))
+        cuts = [(a, a + Tc) for a in range(0, Tmax, Tc)]
+        views = [[tuple(t[:, a:b] for t in (q, k, v, o)) for a, b in cuts] for (q, k, v, _, _, o) in full]
+        chunks = [[tuple(t.contiguous() for t in vw[:3]) + (vw[3].contiguous(),) for vw in sv]
+                  for sv in views]
+
+        def cstep4(i):
+            j = i % len(full)
+            kc, vc = full[j][3], full[j][4]
+            for (a, _), (q, k, v, o) in zip(cuts, chunks[j]):
+                nc.attn_prefill(q, k, v, kc, vc, window=W, pos_offset=a, out=o, workspace=wsp)
+
+        prime("prefill_4x512", cstep4)
+        ms = event_time_ms(cstep4, K, torch)
+        pre["context_4x512_W2048"] = tf_entry(
+            ms, flops, workload=f"B={B} T={Tmax} H=Hkv={H} D={D} full causal, prefilled into the "
+                                f"caches in {len(cuts)} chunks of {Tc} (one call each)")
+
+        def cstep1(i):
+            q, k, v, kc, vc, o = full[i % len(full)]
+            nc.attn_prefill(q, k, v, kc, vc, window=W, out=o, workspace=wsp)
+
+        prime("prefill_1x2048", cstep1)
+        ms = event_time_ms(cstep1, K, torch)
+        pre["context_1x2048_W2048"] = tf_entry(
+            ms, flops, workload=f"the same context in one call (k', v written to the caches; "
+                                f"compare the headline step, which keeps k' in its workspace)")
+        del full, views, chunks, wsp
+        if args.only == "prefill":
+            print(json.dumps(pre))
+            return
+
     # ---------------------------------------------------------------- line
     step_ms = out["step_ms"]
     value = flops / (step_ms * 1e-3) / 1e12
@@ -367,6 +434,7 @@ def main():
         "decode": dec,
         "rope_qknorm": rope,
         "stacks": stacks,
+        "prefill_cache": pre,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -37,7 +37,8 @@
  *     synchronised; the library keeps no state between calls and is
  *     thread-safe;
  *   - inputs are not modified, except the two caches of nc_attn_decode
- *     (exactly one row per sequence and K/V head).
+ *     (exactly one row per sequence and K/V head) and of nc_attn_prefill
+ *     (exactly the chunk's T rows per sequence and K/V head).
  *
  * Errors: arguments are validated on the host before any HIP call. A non-OK
  * status means nothing was enqueued. NC_ERR_INVALID: bad pointer, size,
@@ -71,7 +72,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 2
+#define NC_ABI_VERSION 3
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -145,6 +146,40 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
 nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int H, int Hkv,
                        int D, int window, nc_dtype dtype, const void* ws, size_t ws_bytes,
                        void* stream);
+
+/*
+ * nc_attn_prefill -- prefill of a chunk of T tokens into a contiguous KV cache,
+ * the step before nc_attn_decode; called with increasing pos_offset it is a
+ * chunked prefill ([S10] the new tokens' K and V are appended to the per-layer
+ * cache, then their queries attend to the cache; [S5.5] causal mask; [TBL]
+ * QK-norm after RoPE, GQA, sliding window).
+ *
+ *   q        (B, T, H,   D)     raw queries of the chunk's tokens, which sit at
+ *                               positions pos_offset .. pos_offset + T - 1
+ *   k, v     (B, T, Hkv, D)     their raw keys and values
+ *   k_cache  (B, Tmax, Hkv, D)  rows 0 .. pos_offset-1 hold rotated, normalised
+ *                               keys (from earlier calls or decode steps) and
+ *                               are used as stored; rows pos_offset .. +T-1 are
+ *                               overwritten with norm(rope(k)); later rows are
+ *                               neither read nor written
+ *   v_cache  (B, Tmax, Hkv, D)  likewise; rows pos_offset .. +T-1 receive v
+ *   o        (B, T, H, D)       o[b,t,h]: softmax over cache rows j with
+ *                               0 <= pos_offset + t - j < window of
+ *                               q'.k_cache[b,j] / sqrt(D), applied to v_cache
+ * With pos_offset = 0 and Tmax = T, o equals nc_attn_fwd's. One pos_offset
+ * serves the whole batch. The caches are written by a first kernel and read by
+ * a second one on the same stream.
+ * Requires pos_offset + T <= Tmax, the sizes of nc_attn_fwd with Tmax in place
+ * of T for the caches (Tmax * Hkv * D * sizeof(element) < 2^32), and q, k, v,
+ * o pairwise disjoint and disjoint from the caches.
+ * Workspace (nc_attn_prefill_workspace_bytes): the (cos, sin) table of the
+ * chunk's positions, as in nc_attn_prep.
+ */
+size_t nc_attn_prefill_workspace_bytes(int T, int D, nc_dtype dtype);
+nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, void* o, int B, int T, int Tmax, int H, int Hkv, int D,
+                          int window, double rope_base, int pos_offset, nc_dtype dtype,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * nc_attn_decode -- one decode step per sequence over a contiguous KV cache

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 2
+    assert L.nc_abi_version() == 3
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -130,6 +130,35 @@ def test_decode_validation(kw, status, frag):
     assert frag in nc.lib().nc_last_error().decode()
 
 
+def _pre(**kw):
+    a = dict(q=P, k=P, v=P, kc=P, vc=P, o=P, B=2, T=64, Tmax=256, H=4, Hkv=2, D=64, window=128,
+             base=1e4, off=128, dt=0, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    L = nc.lib()
+    return L.nc_attn_prefill(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["o"], a["B"], a["T"],
+                             a["Tmax"], a["H"], a["Hkv"], a["D"], a["window"], a["base"], a["off"],
+                             a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(vc=None), 1, "v_cache is NULL"),
+    (dict(kc=P + 8), 1, "not 16-byte aligned"),
+    (dict(off=193), 1, "exceeds Tmax"),
+    (dict(off=-1), 1, "pos_offset"),
+    (dict(Tmax=0, off=0), 1, "Tmax"),
+    (dict(window=0), 1, "window"),
+    (dict(D=80), 2, "head dim"),
+    (dict(H=5), 1, "multiple"),
+    (dict(ws=None), 1, "ws is NULL"),
+    (dict(wsb=255), 1, "workspace"),
+    (dict(Tmax=1 << 22, H=8, Hkv=8, D=128, off=0), 2, "2^32"),
+    (dict(B=1 << 12, Tmax=1 << 18, Hkv=4, H=4, off=0), 1, "cache rows"),
+])
+def test_prefill_validation(kw, status, frag):
+    assert _pre(**kw) == status
+    assert frag in nc.lib().nc_last_error().decode()
+
+
 def test_workspace_queries():
     L = nc.lib()
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
@@ -140,6 +169,10 @@ def test_workspace_queries():
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 256 + 512  # 3*16*4, 3*2*32*2
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 1) == 512 + 768  # 3*16*8, 3*2*32*4
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 7) == 0
+    # chunked prefill: only the table of the chunk's positions
+    assert L.nc_attn_prefill_workspace_bytes(64, 64, 0) == 64 * 32 * 4
+    assert L.nc_attn_prefill_workspace_bytes(3, 32, 1) == 512
+    assert L.nc_attn_prefill_workspace_bytes(0, 32, 1) == 0
     # few (sequence, head) pairs: the key range is split and needs chunk states
     n = L.nc_attn_decode_workspace_bytes(2, 2048, 6, 6, 128, 2048)
     assert n > 0 and n % 256 == 0
@@ -155,3 +188,5 @@ def test_binding_refuses_cpu_tensors():
         nc.attn_fwd(q, q, q, window=4)
     with pytest.raises(ValueError, match="GPU"):
         nc.rope_qknorm(q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        nc.attn_prefill(q, q, q, torch.zeros(1, 8, 2, 32), torch.zeros(1, 8, 2, 32), window=4)

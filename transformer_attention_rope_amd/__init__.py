@@ -9,6 +9,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
     rope_qknorm(q, k, rope_base=1e4, pos_offset=0)          -> (q', k')
     attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
     attn_prep(k, ...) -> workspace;  attn_core(q, v, workspace, window=...) -> o
+    attn_prefill(q, k, v, k_cache, v_cache, window=..., pos_offset=0, rope_base=1e4) -> o
     attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window=..., rope_base=1e4) -> o
 """
 from __future__ import annotations
@@ -19,9 +20,10 @@ import os
 import torch
 
 __all__ = [
-    "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_decode",
+    "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_prefill", "attn_decode",
     "attn_prep", "attn_core", "decode_workspace",
-    "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes", "rope_qknorm_workspace_bytes",
+    "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
+    "rope_qknorm_workspace_bytes",
     "NC_OK", "NC_ERR_INVALID", "NC_ERR_UNSUPPORTED", "NC_ERR_HIP", "NC_BF16", "NC_F32",
 ]
 
@@ -43,6 +45,9 @@ _SIGS = {
     "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_core": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "nc_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i]),
+    "nc_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _i, _i,
+                             _vp, _sz, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
                             _vp, _sz, _vp]),
@@ -127,6 +132,10 @@ def rope_qknorm_workspace_bytes(T: int, D: int, pos_offset: int = 0) -> int:
 def attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset=0, dtype=torch.bfloat16) -> int:
     dt = NC_F32 if dtype == torch.float32 else NC_BF16
     return int(lib().nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt))
+
+def attn_prefill_workspace_bytes(T, D, dtype=torch.bfloat16) -> int:
+    dt = NC_F32 if dtype == torch.float32 else NC_BF16
+    return int(lib().nc_attn_prefill_workspace_bytes(T, D, dt))
 
 
 def attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window) -> int:
@@ -215,6 +224,33 @@ def attn_core(q, v, workspace, *, window: int, out=None):
         raise ValueError("out must have q's shape")
     _call("nc_attn_core", _ptr(q), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window), _dt(q),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    return o
+
+
+def attn_prefill(q, k, v, k_cache, v_cache, *, window: int, pos_offset: int = 0,
+                 rope_base: float = 10000.0, out=None, workspace=None):
+    """Prefill of a chunk at positions pos_offset.. into the caches (in place):
+    rows pos_offset .. pos_offset+T-1 receive norm(rope(k)) and v, then the chunk's
+    queries attend to cache rows within the window. q (B,T,H,D); k, v (B,T,Hkv,D);
+    caches (B,Tmax,Hkv,D) -> o (B,T,H,D)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    k_cache = _gpu(k_cache, "k_cache", 4, q.dtype)
+    v_cache = _gpu(v_cache, "v_cache", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    Tmax = k_cache.shape[1]
+    if (tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D)
+            or tuple(k_cache.shape) != (B, Tmax, Hkv, D) or tuple(v_cache.shape) != (B, Tmax, Hkv, D)):
+        raise ValueError("prefill tensor shapes are inconsistent")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    ws = _workspace(attn_prefill_workspace_bytes(T, D, q.dtype), q.device, workspace)
+    _call("nc_attn_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+          B, T, Tmax, H, Hkv, D, int(window), float(rope_base), int(pos_offset), _dt(q),
+          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     return o
 
 

@@ -165,7 +165,7 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
   if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, Hkv, Hkv, D, pos_offset, dt))) != NC_OK)
     return s;
   hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D, dt), ws, B, T, Hkv, D,
-                                      rope_base, pos_offset, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
+                                      rope_base, pos_offset, nullptr, nullptr, T, 0, to_dt(dt),
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
   return ok();
@@ -182,8 +182,7 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
   if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, 0, dt))) != NC_OK)
     return s;
   hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D, dt), v, o, B, T, H,
-                                      Hkv, D, window, ws, dt == NC_BF16 ? nc::kBF16 : nc::kF32,
-                                      (hipStream_t)stream);
+                                      Hkv, D, window, ws, T, 0, to_dt(dt), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core launch");
   return ok();
 }
@@ -203,6 +202,41 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
   if ((s = nc_attn_prep(k, B, T, Hkv, D, rope_base, pos_offset, dt, ws, ws_bytes, stream)) != NC_OK)
     return s;
   return nc_attn_core(q, v, o, B, T, H, Hkv, D, window, dt, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------- attn_prefill
+// Workspace: the (cos, sin) table of the chunk's T positions only; k' and v
+// go straight to the caches.
+size_t nc_attn_prefill_workspace_bytes(int T, int D, nc_dtype dtype) {
+  if (T < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
+  return prep_table_bytes(T, D, dtype);
+}
+
+nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, void* o, int B, int T, int Tmax, int H, int Hkv, int D,
+                          int window, double rope_base, int pos_offset, nc_dtype dt, void* ws,
+                          size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if (Tmax < 1) return fail(NC_ERR_INVALID, "Tmax must be >= 1 (got %d)", Tmax);
+  if ((long long)B * Tmax * Hkv > 0x7fffffffLL)
+    return fail(NC_ERR_INVALID, "B*Tmax*Hkv=%lld cache rows exceed 2^31-1", (long long)B * Tmax * Hkv);
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  if ((long long)pos_offset + T > Tmax)
+    return fail(NC_ERR_INVALID, "pos_offset + T = %lld exceeds Tmax=%d", (long long)pos_offset + T, Tmax);
+  if ((s = check_seq_bytes(Tmax, Hkv, D, dt)) != NC_OK) return s;
+  const char* names[] = {"q", "k", "v", "k_cache", "v_cache", "o"};
+  const void* ptrs[] = {q, k, v, k_cache, v_cache, o};
+  if ((s = check_ptrs(names, ptrs, 6)) != NC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, nc_attn_prefill_workspace_bytes(T, D, dt))) != NC_OK) return s;
+  hipError_t e = nc::launch_attn_prep(k, k_cache, ws, B, T, Hkv, D, rope_base, pos_offset, v,
+                                      v_cache, Tmax, pos_offset, to_dt(dt), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
+  e = nc::launch_attn_core(q, k_cache, v_cache, o, B, T, H, Hkv, D, window, ws, Tmax, pos_offset,
+                           to_dt(dt), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_core launch");
+  return ok();
 }
 
 // -------------------------------------------------------------- attn_decode

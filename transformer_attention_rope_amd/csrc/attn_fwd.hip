@@ -80,6 +80,8 @@ struct FwdArgs {
   const void* tabq;    // [T][D/2] (cos, sin) of positions pos_offset + t: fp16 pairs
                        // packed in 32 bits (bf16 kernel), float2 (fp32 kernel)
   int B, T, H, Hkv, W;
+  int kofs;      // key row (= position) of query row 0: 0, or the chunk's offset in a cache
+  int Tk;        // key rows per sequence in kp and v: T, or the cache length
   int G;         // H / Hkv
   int hpw_log2;  // log2(query heads per workgroup)
   int ngroups;   // H / hpw
@@ -356,19 +358,23 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   const int rem = (int)blockIdx.x % per_qt;
   const int b = rem / p.ngroups, grp = rem - (rem / p.ngroups) * p.ngroups;
   const int hpw = 1 << p.hpw_log2;
-  const int q0 = qt << p.bp_log2;
-  const int q_last = min(q0 + (1 << p.bp_log2), p.T) - 1;
+  // Everything below works in positions (= key rows): query row t sits at
+  // position kofs + t, and q and o rows are addressed by position - kofs.
+  const int q_end = p.kofs + p.T;                   // one past the last query position
+  const int q0 = (qt << p.bp_log2) + p.kofs;        // position of the tile's first query
+  const int q_last = min(q0 + (1 << p.bp_log2), q_end) - 1;
+  const long long qo_row0 = (long long)b * p.T - p.kofs;  // q/o row of position 0 in sequence b
   const int g = (grp * hpw) / p.G;
 
   // ---- key-tile range of the workgroup's band [max(0, q0 - W + 1), q_last]
   const int k_first = max(0, q0 - p.W + 1);
   const int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
 
-  // ---- staging: buffer resources whose ranges end at token T (reads past
-  // ---- the tail return zeros), per-thread byte offsets, per-tile bases
+  // ---- staging: buffer resources whose ranges end at key row kofs + T
+  // ---- (reads past it return zeros), per-thread byte offsets, per-tile bases
   const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
-  const size_t kv_base = ((size_t)b * p.T * p.Hkv + g) * D;
-  const uint32_t kv_records = (uint32_t)(((size_t)p.T * p.Hkv - g) * D * 2);
+  const size_t kv_base = ((size_t)b * p.Tk * p.Hkv + g) * D;
+  const uint32_t kv_records = (uint32_t)(((size_t)q_end * p.Hkv - g) * D * 2);
   const char* vseq = (const char*)((const uint16_t*)p.v + kv_base);
   const char* kseq = (const char*)((const uint16_t*)p.kp + kv_base);
   // the K row that copy j of this wave's lane fills in a tile, and the chunk
@@ -504,9 +510,9 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
         const int i = bt * PB + ii;
         int tr, hr;
         col_row(i * RPI + qr0, tr, hr);
-        const int tc = tr < p.T ? tr : p.T - 1;
-        qw[ii] = ld16(qg + (((size_t)b * p.T + tc) * p.H + hr) * D + qc * 8);
-        tq[ii] = ld16(tab + (size_t)tc * (D / 2) + qc * 4);
+        const int tc = tr < q_end ? tr : q_end - 1;
+        qw[ii] = ld16(qg + ((size_t)(qo_row0 + tc) * p.H + hr) * D + qc * 8);
+        tq[ii] = ld16(tab + (size_t)(tc - p.kofs) * (D / 2) + qc * 4);
       }
       if (bt == 0) {
         gload(ic<0>{}, kt0);
@@ -554,7 +560,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
 
   // Positions covered by this wave (its 32*CB columns): [tw0, tw1].
   const int tw0 = q0 + ((wave * 32 * CB) >> p.hpw_log2);
-  const int tw1 = min(q0 + ((wave * 32 * CB + 32 * CB - 1) >> p.hpw_log2), p.T - 1);
+  const int tw1 = min(q0 + ((wave * 32 * CB + 32 * CB - 1) >> p.hpw_log2), q_end - 1);
   constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
   // K fragment (rb, s): row rb*32 + n, chunk 2s + hf, at its swizzled position
@@ -815,8 +821,8 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   // with a window that is a multiple of the tile or wider than the wave's
   // reach, see: nothing, then (if the window bites) one kWin tile, full
   // tiles, one kDiag tile (its own positions), then nothing.
-  const bool aligned = hpw == 1 && p.W >= C::BN && tw0 <= q_last &&
-                       (p.W % C::BN == 0 || p.W >= tw0 + C::BN);
+  const bool aligned = hpw == 1 && (p.kofs & (32 * CB - 1)) == 0 && p.W >= C::BN &&
+                       tw0 <= q_last && (p.W % C::BN == 0 || p.W >= tw0 + C::BN);
   // calls f(ic<H>) with the half of the tile where the wave's positions start
   auto with_half = [&](auto f) __attribute__((always_inline)) {
     if constexpr (C::CB == 1) {
@@ -883,7 +889,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       int tr, hr;
       col_row(r, tr, hr);
       const u32x4_t w = ld16(os + r * C::QLD + qc * 8);
-      if (tr < p.T) st16_nt(og + (((size_t)b * p.T + tr) * p.H + hr) * D + qc * 8, w);
+      if (tr < q_end) st16_nt(og + ((size_t)(qo_row0 + tr) * p.H + hr) * D + qc * 8, w);
     }
   }
 }
@@ -909,10 +915,11 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   const int b = rem / p.H, h = rem - (rem / p.H) * p.H;
   const int g = h / p.G;
   const int q0 = qt * NT;
-  const int q_last = min(q0 + NT, p.T) - 1;
+  const int q_last = min(q0 + NT, p.T) - 1 + p.kofs;  // a position (= key row)
   const int t = q0 + tid;
   const bool tvalid = t < p.T;
   const int tc = tvalid ? t : p.T - 1;
+  const int ta = t + p.kofs;  // position of query row t
 
   float qv[D];
   {
@@ -938,7 +945,8 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float lsum = 0.f;
 
-  const int k_first = max(0, q0 - p.W + 1);
+  const int k_first = max(0, q0 + p.kofs - p.W + 1);
+  const int k_end = p.kofs + p.T;
   const size_t kv_row = (size_t)p.Hkv * D;
   for (int j0 = (k_first / BN) * BN; j0 <= q_last; j0 += BN) {
     __syncthreads();
@@ -946,9 +954,9 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
     {
       const int r = tid >> 2, part = tid & 3;
       const int key = j0 + r;
-      if (key < p.T) {
-        const float* krow = kg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
-        const float* vrow = vg + ((size_t)b * p.T + key) * kv_row + (size_t)g * D + part * (D / 4);
+      if (key < k_end) {
+        const float* krow = kg + ((size_t)b * p.Tk + key) * kv_row + (size_t)g * D + part * (D / 4);
+        const float* vrow = vg + ((size_t)b * p.Tk + key) * kv_row + (size_t)g * D + part * (D / 4);
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) {
           Kf[r][part * (D / 4) + i] = krow[i];
@@ -966,7 +974,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
 #pragma unroll 1
     for (int jj = 0; jj < BN; ++jj) {
       const int key = j0 + jj;
-      const int dl = t - key;
+      const int dl = ta - key;
       if (dl < 0 || dl >= p.W) continue;
       float s = 0.f;
 #pragma unroll
@@ -1049,8 +1057,8 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
 }
 
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
-                            int H, int Hkv, int D, int window, const void* tabq, Dtype dt,
-                            hipStream_t stream) {
+                            int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
+                            Dtype dt, hipStream_t stream) {
   FwdArgs a{};
   a.q = q;
   a.kp = kp;
@@ -1062,6 +1070,8 @@ hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* 
   a.H = H;
   a.Hkv = Hkv;
   a.W = window;
+  a.kofs = kofs;
+  a.Tk = Tk;
   a.G = H / Hkv;
   switch (D) {
     case 32: return attn_fwd_d<32>(a, dt, stream);

@@ -11,20 +11,24 @@ namespace nc {
 enum Dtype { kBF16 = 0, kF32 = 1 };
 
 // ---- prefill input stage: k' = RMSNorm(RoPE(k)) in k's layout and type, and
-// ---- the fp32 (cos, sin) table [T][D/2] of positions pos_offset + t for q
+// ---- the (cos, sin) table [T][D/2] of positions pos_offset + t for q. With
+// ---- vc non-null, kp and vc are (B, Tk, Hkv, D) caches: k' and a copy of v
+// ---- go to their rows row0 .. row0 + T - 1.
 size_t attn_prep_table_bytes(int T, int D, Dtype dt);
 size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt);
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
-                            double rope_base, int pos_offset, Dtype dt, hipStream_t stream);
+                            double rope_base, int pos_offset, const void* v, void* vc, int Tk,
+                            int row0, Dtype dt, hipStream_t stream);
 
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
                               int T, int H, int Hkv, int D, double rope_base, int pos_offset,
                               Dtype dt, hipStream_t stream);
 
-// attention from raw q (rotated/normalised in the kernel with tabq), k' and v
+// attention from raw q (rotated/normalised in the kernel with tabq), k' and v;
+// kp and v hold Tk key rows per sequence, query row t sits at key row kofs + t
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
-                            int H, int Hkv, int D, int window, const void* tabq, Dtype dt,
-                            hipStream_t stream);
+                            int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
+                            Dtype dt, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,

@@ -33,6 +33,10 @@ namespace nc {
 // [-pi, pi]. The rotation and the norm of the rows run in fp32; the CPR
 // 16-byte chunks of a row sit in consecutive lanes and reduce their sum of
 // squares across lanes. k' keeps k's layout (B, T, Hkv, D) and element type.
+// With CACHE the k' rows go to rows row0 + t of a (B, Tk, Hkv, D) cache
+// instead, and the v rows of the same (sequence, position, head) are copied
+// to the same rows of the value cache, so the chunk's keys and values are in
+// the cache before the attention kernel reads them there.
 constexpr int PREP_CPT = 4;  // 16-byte chunks per thread
 
 template <int D, typename Elem, int CPT = PREP_CPT>
@@ -41,12 +45,14 @@ constexpr int prep_rows_per_block() {
 }
 constexpr int ROPE_CPT = 6;  // chunks per thread of rope_qknorm_kernel (96 d12 rows per workgroup)
 
-template <int D, typename Elem>
+template <int D, typename Elem, bool CACHE>
 __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__ k,
                                                          Elem* __restrict__ kp,
                                                          void* __restrict__ tabq, int T,
                                                          int Hkv, int rows, double log2_base,
-                                                         int pos_offset, int nrb) {
+                                                         int pos_offset, int nrb,
+                                                         const Elem* __restrict__ v,
+                                                         Elem* __restrict__ vc, int Tk, int row0) {
   constexpr bool kBf = sizeof(Elem) == 2;
   constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;      // chunks per row
@@ -60,7 +66,9 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
   const int tid = threadIdx.x;
 
   u32x4_t w[PREP_CPT];
-  size_t off[PREP_CPT];
+  u32x4_t wv[CACHE ? PREP_CPT : 1];
+  size_t off[PREP_CPT];   // element offset of the chunk in k (and v)
+  size_t doff[PREP_CPT];  // and in the destination of k'
 #pragma unroll
   for (int p = 0; p < PREP_CPT; ++p) {
     const int ci = p * 256 + tid;
@@ -68,7 +76,11 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     const int cc = ci % CPR;
     const int bb = row / Hkv, g = row - bb * Hkv;
     off[p] = (((size_t)bb * T + t) * Hkv + g) * D + (size_t)cc * EPC;
-    if (ci < total) w[p] = ld16_nt(k + off[p]);
+    doff[p] = CACHE ? (((size_t)bb * Tk + row0 + t) * Hkv + g) * D + (size_t)cc * EPC : off[p];
+    if (ci < total) {
+      w[p] = ld16_nt(k + off[p]);
+      if constexpr (CACHE) wv[p] = ld16_nt(v + off[p]);
+    }
   }
 
   if (tid < D / 2) {
@@ -128,7 +140,8 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
 #pragma unroll
         for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
-      st16_nt(kp + off[p], o);
+      st16_nt(kp + doff[p], o);
+      if constexpr (CACHE) st16_nt(vc + doff[p], wv[p]);
     }
   }
 }
@@ -142,33 +155,44 @@ size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt) {
 
 template <int D, typename Elem>
 static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
-                                   double rope_base, int pos_offset, hipStream_t stream) {
+                                   double rope_base, int pos_offset, const void* v, void* vc,
+                                   int Tk, int row0, hipStream_t stream) {
   constexpr int RB = prep_rows_per_block<D, Elem>();
   const long long rows = (long long)B * Hkv;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int nrb = (int)((rows + RB - 1) / RB);
   const long long nblk = (long long)T * nrb;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_prep_kernel<D, Elem>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                     (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
-                     std::log2(rope_base), pos_offset, nrb);
+  if (vc != nullptr)
+    hipLaunchKernelGGL((attn_prep_kernel<D, Elem, true>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
+                       std::log2(rope_base), pos_offset, nrb, (const Elem*)v, (Elem*)vc, Tk, row0);
+  else
+    hipLaunchKernelGGL((attn_prep_kernel<D, Elem, false>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
+                       std::log2(rope_base), pos_offset, nrb, (const Elem*)nullptr,
+                       (Elem*)nullptr, T, 0);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t attn_prep_d(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
-                              double rope_base, int pos_offset, Dtype dt, hipStream_t stream) {
+                              double rope_base, int pos_offset, const void* v, void* vc, int Tk,
+                              int row0, Dtype dt, hipStream_t stream) {
   if (dt == kBF16)
-    return attn_prep_launch<D, uint16_t>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, stream);
-  return attn_prep_launch<D, float>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, stream);
+    return attn_prep_launch<D, uint16_t>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk,
+                                         row0, stream);
+  return attn_prep_launch<D, float>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0,
+                                    stream);
 }
 
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
-                            double rope_base, int pos_offset, Dtype dt, hipStream_t stream) {
+                            double rope_base, int pos_offset, const void* v, void* vc, int Tk,
+                            int row0, Dtype dt, hipStream_t stream) {
   switch (D) {
-    case 32: return attn_prep_d<32>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
-    case 64: return attn_prep_d<64>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
-    case 128: return attn_prep_d<128>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, dt, stream);
+    case 32: return attn_prep_d<32>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
+    case 64: return attn_prep_d<64>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
+    case 128: return attn_prep_d<128>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -124,6 +124,26 @@ def decode_inputs(cfg: DecodeConfig, set_idx: int = 0):
     return q, k_new, v_new, k_cache, v_cache, seqlens
 
 
+# Chunked prefill of the d12 layer: the last 512-token chunk of a 2048-token
+# context, whose first 1536 positions are already in the per-layer caches.
+CHUNK = dict(B=8, T=512, P=1536, Tmax=2048, H=6, Hkv=6, D=128)
+
+
+def prefill_chunk_inputs(seed: int = 0, dtype=torch.bfloat16, **kw):
+    """q (B,T,H,D), k and v (B,T,Hkv,D) of the chunk and the two caches
+    (B,Tmax,Hkv,D) of CHUNK's sizes (overridable); every cache row is N(0,1),
+    those of the chunk are overwritten by the prefill."""
+    c = dict(CHUNK, **kw)
+    B, T, Tmax, H, Hkv, D = c["B"], c["T"], c["Tmax"], c["H"], c["Hkv"], c["D"]
+    base = SEED_BASE + 900 + 10 * seed
+    q = randn((B, T, H, D), base + T_Q, dtype)
+    k = randn((B, T, Hkv, D), base + T_K, dtype)
+    v = randn((B, T, Hkv, D), base + T_V, dtype)
+    kc = randn((B, Tmax, Hkv, D), base + T_KCACHE, dtype)
+    vc = randn((B, Tmax, Hkv, D), base + T_VCACHE, dtype)
+    return q, k, v, kc, vc
+
+
 def small_prefill(B, T, H, Hkv, D, seed, dtype=torch.bfloat16, scale=1.0):
     """Seeded small case for parity sweeps (ragged T, odd windows, ...)."""
     q = randn((B, T, H, D), seed, torch.float32) * scale
@@ -140,6 +160,16 @@ def unmasked_pairs(T: int, W: int) -> int:
     if W >= T:
         return T * (T + 1) // 2
     return W * (W + 1) // 2 + (T - W) * W
+
+
+def chunk_pairs(T: int, P: int, W: int) -> int:
+    """Number of (t, j) with 0 <= P + t - j < W, j >= 0, t < T: query t of a
+    chunk at offset P sees min(W, P + t + 1) cache rows."""
+    return sum(min(W, P + t + 1) for t in range(T))
+
+
+def prefill_chunk_flops(B, T, P, H, D, W) -> int:
+    return 4 * D * chunk_pairs(T, P, W) * B * H
 
 
 def prefill_flops(B, T, H, D, W) -> int:
