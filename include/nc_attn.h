@@ -72,7 +72,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 3
+#define NC_ABI_VERSION 4
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -113,8 +113,14 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
  * Requires H % Hkv == 0, window >= 1 (window >= T: full causal), the sizes
  * of nc_rope_qknorm, T * Hkv * D * sizeof(element) < 2^32 (one sequence's K
  * or V is addressed with 32-bit byte offsets), and o not overlapping any input.
- * Workspace (nc_attn_fwd_workspace_bytes, which depends on B, T, Hkv, D and
- * dtype): the (cos, sin) table of the T positions and k' = norm(rope(k)).
+ * Workspace (nc_attn_fwd_workspace_bytes, which depends on B, T, H, Hkv, D
+ * and dtype): the (cos, sin) table of the T positions, k' = norm(rope(k)),
+ * and, for bf16 launches too small to fill the device (few sequences and
+ * heads), room for per-slice partial output rows: the key tiles of each query
+ * tile are then cut into slices run by separate workgroups, and a second
+ * kernel adds the slices' unnormalised sums and divides by their row sums
+ * (QK-norm bounds the scores, so the slices share one exponent scale). Calls
+ * that overlap in time must not share a workspace.
  * nc_attn_fwd(...) is exactly nc_attn_prep followed by nc_attn_core on the
  * same workspace.
  */
@@ -136,15 +142,18 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *     the rotated q that follows) or two fp32 values (dtype fp32), and
  *     k' = norm(rope(k)) in k's layout and element type. Arguments as for
  *     nc_attn_fwd.
- *   nc_attn_core computes o from raw q, the k' and table in ws (only read),
- *     and v; B, T, Hkv, D and dtype must be those of the nc_attn_prep call
- *     that filled ws, which must complete (same stream or an event) first.
+ *   nc_attn_core computes o from raw q, the k' and table in ws (read, not
+ *     modified), and v; it may write the partial rows after them. B, T, Hkv,
+ *     D and dtype must be those of the nc_attn_prep call that filled ws, which
+ *     must complete (same stream or an event) first; ws must hold
+ *     nc_attn_fwd_workspace_bytes for the call's H.
+ * nc_attn_prep needs only the table and k' part of that size.
  */
 nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_base,
                        int pos_offset, nc_dtype dtype, void* ws, size_t ws_bytes,
                        void* stream);
 nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int H, int Hkv,
-                       int D, int window, nc_dtype dtype, const void* ws, size_t ws_bytes,
+                       int D, int window, nc_dtype dtype, void* ws, size_t ws_bytes,
                        void* stream);
 
 /*
@@ -173,9 +182,13 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
  * of T for the caches (Tmax * Hkv * D * sizeof(element) < 2^32), and q, k, v,
  * o pairwise disjoint and disjoint from the caches.
  * Workspace (nc_attn_prefill_workspace_bytes): the (cos, sin) table of the
- * chunk's positions, as in nc_attn_prep.
+ * chunk's positions, as in nc_attn_prep, and room for partial output rows of
+ * a launch cut into key-tile slices, as in nc_attn_fwd (a chunk at a large
+ * offset has long key ranges for few query tiles). Calls that overlap in time
+ * must not share a workspace.
  */
-size_t nc_attn_prefill_workspace_bytes(int T, int D, nc_dtype dtype);
+size_t nc_attn_prefill_workspace_bytes(int B, int T, int Tmax, int H, int Hkv, int D,
+                                       nc_dtype dtype);
 nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
                           void* v_cache, void* o, int B, int T, int Tmax, int H, int Hkv, int D,
                           int window, double rope_base, int pos_offset, nc_dtype dtype,

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 3
+    assert L.nc_abi_version() == 4
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -166,13 +166,22 @@ def test_workspace_queries():
     # fp32), then k', each part rounded up to 256 bytes
     assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 4 + 8 * 2048 * 6 * 128 * 2
     assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 1) == 2048 * 64 * 8 + 8 * 2048 * 6 * 128 * 4
-    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 256 + 512  # 3*16*4, 3*2*32*2
+    assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 0) == 256 + 512  # 3*16*4, 3*2*32*2 (no slices: one key tile)
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 1) == 512 + 768  # 3*16*8, 3*2*32*4
     assert L.nc_attn_fwd_workspace_bytes(1, 3, 2, 2, 32, 0, 7) == 0
-    # chunked prefill: only the table of the chunk's positions
-    assert L.nc_attn_prefill_workspace_bytes(64, 64, 0) == 64 * 32 * 4
-    assert L.nc_attn_prefill_workspace_bytes(3, 32, 1) == 512
-    assert L.nc_attn_prefill_workspace_bytes(0, 32, 1) == 0
+    # chunked prefill: the table of the chunk's positions; fp32 never slices
+    assert L.nc_attn_prefill_workspace_bytes(2, 64, 256, 4, 2, 64, 1) == 64 * 32 * 8
+    assert L.nc_attn_prefill_workspace_bytes(1, 3, 3, 2, 2, 32, 0) == 256
+    assert L.nc_attn_prefill_workspace_bytes(1, 0, 3, 2, 2, 32, 1) == 0
+    assert L.nc_attn_prefill_workspace_bytes(1, 4, 3, 2, 2, 32, 0) == 0  # Tmax < T
+    # bf16 launches far below a full device get room for key-tile slices: the
+    # d12 chunk (96 workgroups of 256 columns, or 192 of 128) takes up to two
+    # slices of fp32 rows of D + 1 values (output and row sum)
+    rows = 8 * 512 * 6
+    assert L.nc_attn_prefill_workspace_bytes(8, 512, 2048, 6, 6, 128, 0) == \
+        512 * 64 * 4 + 2 * rows * 129 * 4
+    # a full device of workgroups (the d12 layer) gets none
+    assert L.nc_attn_fwd_workspace_bytes(8, 2048, 6, 6, 128, 0, 0) == 2048 * 64 * 4 + 8 * 2048 * 6 * 128 * 2
     # few (sequence, head) pairs: the key range is split and needs chunk states
     n = L.nc_attn_decode_workspace_bytes(2, 2048, 6, 6, 128, 2048)
     assert n > 0 and n % 256 == 0

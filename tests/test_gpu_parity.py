@@ -70,6 +70,20 @@ SMALL_BF16 = [
     (2, 400, 8, 1, 128, 200, 0),
     (1, 2048, 2, 2, 128, 1024, 0),
     (1, 1000, 4, 4, 64, 320, 0),
+    # Most cases above launch fewer workgroups than half the device and so
+    # cut their key tiles into slices; these launch enough not to
+    # (432, 192, 160 and 288 workgroups), at ragged sizes
+    (24, 300, 6, 6, 128, 100, 0),
+    (16, 129, 16, 4, 64, 64, 0),
+    (20, 130, 8, 8, 32, 37, 5),
+    (6, 600, 6, 6, 128, 2048, 0),
+    # few (sequence, head) pairs with bands of 24 or more key tiles: key
+    # tiles cut into slices (4 slices, some of them empty for the first query
+    # tiles; 3 slices with 4 query heads per workgroup; D = 32; a window of 1536)
+    (1, 2048, 2, 2, 128, 2048, 0),
+    (1, 1500, 4, 1, 64, 1500, 9),
+    (2, 1700, 2, 2, 32, 1700, 0),
+    (1, 2048, 1, 1, 128, 1536, 0),
 ]
 
 
@@ -249,7 +263,7 @@ def test_prep_core_equals_fwd():
     q, k, v = wl.small_prefill(2, 300, 8, 2, 128, seed=4242)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
     o1 = nc.attn_fwd(q, k, v, window=200, pos_offset=7)
-    ws = nc.attn_prep(k, pos_offset=7)
+    ws = nc.attn_prep(k, pos_offset=7, H=8)
     o2 = nc.attn_core(q, v, ws, window=200)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)

@@ -66,6 +66,10 @@ PREFILL_SMALL = [
     (1, 300, 1024, 96, 1, 1, 32, 192, torch.bfloat16),    # 32-column waves, offset on a half tile
     (1, 300, 1024, 160, 2, 2, 64, 128, torch.bfloat16),   # the same at D=64
     (1, 70, 200, 130, 64, 1, 32, 70, torch.bfloat16),     # 64 query heads per K/V head
+    # long key ranges for few query tiles: key tiles cut into slices
+    (1, 300, 2000, 1600, 2, 2, 128, 2048, torch.bfloat16),  # offset inside a tile
+    (1, 256, 2048, 1536, 4, 4, 64, 1536, torch.bfloat16),   # window edge inside the slices
+    (2, 200, 1800, 1536, 3, 1, 128, 2048, torch.bfloat16),  # three query heads per K/V head
     (2, 100, 300, 64, 4, 2, 64, 80, torch.float32),
     (1, 150, 400, 77, 2, 1, 128, 2048, torch.float32),
     (1, 33, 33, 0, 2, 2, 32, 5, torch.float32),

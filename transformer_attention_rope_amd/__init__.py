@@ -45,7 +45,7 @@ _SIGS = {
     "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_core": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
-    "nc_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i]),
+    "nc_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "nc_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                              _vp, _sz, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -133,9 +133,9 @@ def attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset=0, dtype=torch.bfloat16
     dt = NC_F32 if dtype == torch.float32 else NC_BF16
     return int(lib().nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt))
 
-def attn_prefill_workspace_bytes(T, D, dtype=torch.bfloat16) -> int:
+def attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, dtype=torch.bfloat16) -> int:
     dt = NC_F32 if dtype == torch.float32 else NC_BF16
-    return int(lib().nc_attn_prefill_workspace_bytes(T, D, dt))
+    return int(lib().nc_attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, dt))
 
 
 def attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window) -> int:
@@ -212,7 +212,8 @@ def attn_prep(k, *, rope_base: float = 10000.0, pos_offset: int = 0, H=None, wor
 
 def attn_core(q, v, workspace, *, window: int, out=None):
     """Second stage of attn_fwd: attention from raw q (B,T,H,D), v (B,T,Hkv,D) and the
-    workspace filled by attn_prep for the same B, T, Hkv, D and dtype."""
+    workspace filled by attn_prep for the same B, T, Hkv, D and dtype (sized by
+    attn_fwd_workspace_bytes for this H: partial rows may be written after k')."""
     q = _gpu(q, "q", 4)
     v = _gpu(v, "v", 4, q.dtype)
     B, T, H, D = q.shape
@@ -247,7 +248,7 @@ def attn_prefill(q, k, v, k_cache, v_cache, *, window: int, pos_offset: int = 0,
     o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
     if o.shape != q.shape:
         raise ValueError("out must have q's shape")
-    ws = _workspace(attn_prefill_workspace_bytes(T, D, q.dtype), q.device, workspace)
+    ws = _workspace(attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, q.dtype), q.device, workspace)
     _call("nc_attn_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o),
           B, T, Tmax, H, Hkv, D, int(window), float(rope_base), int(pos_offset), _dt(q),
           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))

@@ -121,7 +121,8 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
 
 // ---------------------------------------------------------------- attn_fwd
 // Workspace: the (cos, sin) table of the T positions (fp16 pairs for bf16,
-// fp32 pairs for fp32), then k'.
+// fp32 pairs for fp32), then k', then room for the partial rows of a launch
+// cut into key-tile slices (bf16 launches too small to fill the device).
 namespace {
 nc::Dtype to_dt(nc_dtype dt) { return dt == NC_F32 ? nc::kF32 : nc::kBF16; }
 size_t prep_table_bytes(int T, int D, nc_dtype dt) {
@@ -129,6 +130,9 @@ size_t prep_table_bytes(int T, int D, nc_dtype dt) {
 }
 size_t prep_k_bytes(int B, int T, int Hkv, int D, nc_dtype dt) {
   return round_up(nc::attn_prep_k_bytes(B, T, Hkv, D, dt == NC_F32 ? nc::kF32 : nc::kBF16));
+}
+size_t part_bytes(int B, int T, int H, int Hkv, int D, int Tk, nc_dtype dt) {
+  return nc::attn_core_part_bytes(B, T, H, Hkv, D, Tk, to_dt(dt));
 }
 nc_status check_fwd_sizes(int B, int T, int H, int Hkv, int D, nc_dtype dt) {
   nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
@@ -151,7 +155,8 @@ size_t nc_attn_fwd_workspace_bytes(int B, int T, int H, int Hkv, int D, int pos_
   (void)H;
   (void)pos_offset;
   if (B < 1 || T < 1 || Hkv < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
-  return prep_table_bytes(T, D, dtype) + prep_k_bytes(B, T, Hkv, D, dtype);
+  return prep_table_bytes(T, D, dtype) + prep_k_bytes(B, T, Hkv, D, dtype) +
+         round_up(part_bytes(B, T, H, Hkv, D, T, dtype));
 }
 
 nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_base,
@@ -162,7 +167,7 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
   const char* names[] = {"k"};
   const void* ptrs[] = {k};
   if ((s = check_ptrs(names, ptrs, 1)) != NC_OK) return s;
-  if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, Hkv, Hkv, D, pos_offset, dt))) != NC_OK)
+  if ((s = check_ws(ws, ws_bytes, prep_table_bytes(T, D, dt) + prep_k_bytes(B, T, Hkv, D, dt))) != NC_OK)
     return s;
   hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D, dt), ws, B, T, Hkv, D,
                                       rope_base, pos_offset, nullptr, nullptr, T, 0, to_dt(dt),
@@ -172,7 +177,7 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
 }
 
 nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int H, int Hkv, int D,
-                       int window, nc_dtype dt, const void* ws, size_t ws_bytes, void* stream) {
+                       int window, nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
   if (s != NC_OK) return s;
   if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
@@ -181,8 +186,10 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
   if ((s = check_ptrs(names, ptrs, 3)) != NC_OK) return s;
   if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, 0, dt))) != NC_OK)
     return s;
+  const size_t front = prep_table_bytes(T, D, dt) + prep_k_bytes(B, T, Hkv, D, dt);
   hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D, dt), v, o, B, T, H,
-                                      Hkv, D, window, ws, T, 0, to_dt(dt), (hipStream_t)stream);
+                                      Hkv, D, window, ws, T, 0, (char*)ws + front,
+                                      part_bytes(B, T, H, Hkv, D, T, dt), to_dt(dt), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core launch");
   return ok();
 }
@@ -205,11 +212,14 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
 }
 
 // ------------------------------------------------------------- attn_prefill
-// Workspace: the (cos, sin) table of the chunk's T positions only; k' and v
-// go straight to the caches.
-size_t nc_attn_prefill_workspace_bytes(int T, int D, nc_dtype dtype) {
-  if (T < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
-  return prep_table_bytes(T, D, dtype);
+// Workspace: the (cos, sin) table of the chunk's T positions, then room for
+// partial rows as in attn_fwd; k' and v go straight to the caches.
+size_t nc_attn_prefill_workspace_bytes(int B, int T, int Tmax, int H, int Hkv, int D,
+                                       nc_dtype dtype) {
+  if (B < 1 || T < 1 || Tmax < T || H < 1 || Hkv < 1 || D < 2 ||
+      (dtype != NC_BF16 && dtype != NC_F32))
+    return 0;
+  return prep_table_bytes(T, D, dtype) + round_up(part_bytes(B, T, H, Hkv, D, Tmax, dtype));
 }
 
 nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
@@ -229,12 +239,14 @@ nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_c
   const char* names[] = {"q", "k", "v", "k_cache", "v_cache", "o"};
   const void* ptrs[] = {q, k, v, k_cache, v_cache, o};
   if ((s = check_ptrs(names, ptrs, 6)) != NC_OK) return s;
-  if ((s = check_ws(ws, ws_bytes, nc_attn_prefill_workspace_bytes(T, D, dt))) != NC_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, nc_attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, dt))) != NC_OK)
+    return s;
   hipError_t e = nc::launch_attn_prep(k, k_cache, ws, B, T, Hkv, D, rope_base, pos_offset, v,
                                       v_cache, Tmax, pos_offset, to_dt(dt), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
   e = nc::launch_attn_core(q, k_cache, v_cache, o, B, T, H, Hkv, D, window, ws, Tmax, pos_offset,
-                           to_dt(dt), (hipStream_t)stream);
+                           (char*)ws + prep_table_bytes(T, D, dt),
+                           part_bytes(B, T, H, Hkv, D, Tmax, dt), to_dt(dt), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_core launch");
   return ok();
 }

@@ -88,6 +88,10 @@ struct FwdArgs {
   int nqt;       // query tiles per (b, head group)
   int bp_log2;   // log2(positions per workgroup)
   float qscale;  // log2(e) / sqrt(D): folded into q'
+  int nsplit;    // workgroups per query tile, each over a slice of its key tiles
+  int rows;      // B * T * H: output rows
+  float* part;   // nsplit > 1: per slice, unnormalised fp32 output rows [nsplit][rows][D],
+                 // then their row sums [nsplit][rows]
 };
 
 // =====================================================================
@@ -331,8 +335,11 @@ struct TileSchedTab {
   static_assert(s.ok, "tile schedule");
 };
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
+// The bf16 kernel body. With SPLIT, each workgroup runs one of nsplit slices
+// of its query tile's key tiles and writes unnormalised fp32 partial rows
+// (attn_split_combine_kernel adds them up); without, it writes o itself.
+template <int D, int NW, bool SPLIT>
+__device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
   using C = BfCfg<D, NW>;
   constexpr int CB = C::CB;
   // K and V^T double buffers. Before the first tile and after the last one
@@ -352,10 +359,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 31, hf = lane >> 5;
 
-  // ---- work item: heaviest (latest) query tiles first
-  const int per_qt = p.B * p.ngroups;
+  // ---- work item: heaviest (latest) query tiles first; a query tile's
+  // ---- key-tile slices next to each other
+  const int per_split = p.B * p.ngroups;
+  const int per_qt = SPLIT ? per_split * p.nsplit : per_split;
   const int qt = p.nqt - 1 - (int)blockIdx.x / per_qt;
-  const int rem = (int)blockIdx.x % per_qt;
+  const int rem0 = (int)blockIdx.x % per_qt;
+  const int split = SPLIT ? rem0 / per_split : 0;
+  const int rem = rem0 - split * per_split;
   const int b = rem / p.ngroups, grp = rem - (rem / p.ngroups) * p.ngroups;
   const int hpw = 1 << p.hpw_log2;
   // Everything below works in positions (= key rows): query row t sits at
@@ -368,7 +379,31 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
 
   // ---- key-tile range of the workgroup's band [max(0, q0 - W + 1), q_last]
   const int k_first = max(0, q0 - p.W + 1);
-  const int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
+  int kt0 = k_first / C::BN, kt1 = q_last / C::BN;
+  // slice `split` of nsplit near-equal slices of the range (possibly empty)
+  if constexpr (SPLIT) {
+    const int n = kt1 - kt0 + 1;
+    kt1 = kt0 + ((split + 1) * n) / p.nsplit - 1;
+    kt0 += (split * n) / p.nsplit;
+  }
+  // slice outputs, formed where they are written
+  auto part_o = [&]() __attribute__((always_inline)) { return p.part + (size_t)split * p.rows * D; };
+  auto part_l = [&]() __attribute__((always_inline)) {
+    return p.part + (size_t)p.nsplit * p.rows * D + (size_t)split * p.rows;
+  };
+  if (SPLIT && kt1 < kt0) {
+    // an empty slice contributes nothing: zero output rows and row sums
+    for (int i = threadIdx.x; i < C::NC * (D / 4); i += C::NT) {
+      const int col = i / (D / 4), c4 = i - (i / (D / 4)) * (D / 4);
+      const int tq = q0 + (col >> p.hpw_log2);
+      if (tq < q_end) {
+        const size_t row = (size_t)(qo_row0 + tq) * p.H + grp * hpw + (col & (hpw - 1));
+        st16(part_o() + row * D + 4 * c4, u32x4_t{0u, 0u, 0u, 0u});
+        if (c4 == 0) part_l()[row] = 0.f;
+      }
+    }
+    return;
+  }
 
   // ---- staging: buffer resources whose ranges end at key row kofs + T
   // ---- (reads past it return zeros), per-thread byte offsets, per-tile bases
@@ -831,7 +866,8 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       f(ic<0>{});
     }
   };
-  if (aligned) {
+  // (A slice of the key tiles runs the part of this order inside [kt0, kt1].)
+  if (!SPLIT && aligned) {
     const int ktD = tw0 / C::BN;
     const int ktW = tw0 - p.W >= 0 ? (tw0 - p.W) / C::BN : -1;
     const int kf0 = ktW >= 0 ? ktW + 1 : kt0;
@@ -851,6 +887,27 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       }
     });
     run(tile_empty, ktD + 1, kt1);
+  } else if (aligned) {
+    const int ktD = tw0 / C::BN;
+    const int ktW = tw0 - p.W >= 0 ? (tw0 - p.W) / C::BN : -1;
+    const int kf0 = max(kt0, ktW + 1);
+    run(tile_empty, kt0, min(kt1, ktW - 1));
+    if (ktW >= kt0 && ktW <= kt1)
+      with_half([&](auto Hc) {
+        one([&](auto Pc, int kt) { tile_sched(ic<kWin>{}, ic<1>{}, Pc, Hc, kt); }, ktW);
+      });
+    run(tile_full, kf0, min(kt1, ktD - 1));
+    if (ktD >= kt0 && ktD <= kt1)
+      with_half([&](auto Hc) {
+        if (ktD < kt1) {
+          one([&](auto Pc, int kt) { tile_sched(ic<kDiag>{}, ic<1>{}, Pc, Hc, kt); }, ktD);
+        } else {
+          if ((ktD - kt0) & 1) tile_sched(ic<kDiag>{}, ic<0>{}, ic<1>{}, Hc, ktD);
+          else tile_sched(ic<kDiag>{}, ic<0>{}, ic<0>{}, Hc, ktD);
+          tile_sync_all();
+        }
+      });
+    run(tile_empty, max(kt0, ktD + 1), kt1);
   } else {
     // full tiles for this wave: j0 + BN - 1 <= tw0 and tw1 - j0 < W
     const int ktA = max(kt0, tw1 - p.W + C::BN > 0 ? (tw1 - p.W + C::BN) / C::BN : 0);
@@ -864,6 +921,27 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
     }
   }
 
+  // ---- epilogue of a slice: its unnormalised fp32 output rows (lane-half hf
+  // ---- holds dims 8*r4 + 4*hf .. +3 of each 32-dim block) and row sums
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const float l = sum_halves(lsum[cb]);
+      if (t[cb] < q_end) {
+        const size_t row = (size_t)(qo_row0 + t[cb]) * p.H + h[cb];
+        float* const orow = part_o() + row * D + 4 * hf;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            st16(orow + db * 32 + 8 * r4,
+                 u32x4_t{__float_as_uint(oacc[db][cb][4 * r4]), __float_as_uint(oacc[db][cb][4 * r4 + 1]),
+                         __float_as_uint(oacc[db][cb][4 * r4 + 2]), __float_as_uint(oacc[db][cb][4 * r4 + 3])});
+        if (hf == 0) part_l()[row] = l;
+      }
+    }
+    return;
+  }
   // ---- epilogue: normalise by the row sum, write the wave's output rows to
   // ---- its LDS rows (the last barrier of the tile loop freed the buffers),
   // ---- and store them row-major, CPR lanes per row, bf16 (B, T, H, D)
@@ -892,6 +970,41 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
       if (tr < q_end) st16_nt(og + ((size_t)(qo_row0 + tr) * p.H + hr) * D + qc * 8, w);
     }
   }
+}
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
+  attn_fwd_bf16_body<D, NW, false>(p);
+}
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_split_kernel(FwdArgs p) {
+  attn_fwd_bf16_body<D, NW, true>(p);
+}
+
+// Sum of the slices of a split launch: o = (sum_s O_s) / (sum_s l_s), bf16.
+// Scores are bounded by QK-norm, so the slices share one scale (no running
+// maximum) and their partial sums add directly. One thread per 4 dims.
+template <int D>
+__global__ void __launch_bounds__(256) attn_split_combine_kernel(const float* __restrict__ part,
+                                                                 uint16_t* __restrict__ o,
+                                                                 int rows, int nsplit) {
+  constexpr int TPR = D / 4;  // threads per row
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = i / TPR;
+  if (row >= rows) return;
+  const int c4 = (int)(i - row * TPR);
+  const float* pl = part + (size_t)nsplit * rows * D;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, l = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const u32x4_t w = ld16(part + ((size_t)s * rows + row) * D + 4 * c4);
+    a0 += __uint_as_float(w[0]);
+    a1 += __uint_as_float(w[1]);
+    a2 += __uint_as_float(w[2]);
+    a3 += __uint_as_float(w[3]);
+    l += pl[(size_t)s * rows + row];
+  }
+  const float inv = 1.0f / l;
+  st8(o + row * D + 4 * c4, u32x2_t{pack_bf2(a0 * inv, a1 * inv), pack_bf2(a2 * inv, a3 * inv)});
 }
 
 // =====================================================================
@@ -1017,33 +1130,135 @@ static int ilog2(int x) {
 // against 64.4).
 template <int D>
 constexpr int fwd_waves() { return D == 128 ? 4 : 8; }
+// (For a chunk whose queries start at position kofs, the window bites for
+// most of its query tiles once it is at most kofs + T/2: 2W <= T + 2 kofs.
+// Measured on a 512-token d12 chunk at offset 1536 with W = 512: 30.2 us with
+// two waves against 32.1.)
 template <int D>
-static bool fwd_narrow(int T, int W) { return D == 128 && 2 * (long long)W <= T; }
+static bool fwd_narrow(int T, int W, int kofs) {
+  return D == 128 && 2 * (long long)W <= T + 2 * (long long)kofs;
+}
+
+// Key-tile slices. A launch of fewer workgroups than half the device holds
+// leaves compute units idle while each workgroup walks its band of key tiles
+// alone (a short prompt, a batch of one, a chunk at a large offset); there
+// each query tile's key tiles are cut into nsplit slices, one workgroup each,
+// so that up to a full device of workgroups run, every slice keeps at least
+// kMinSliceTiles tiles, and a second kernel adds the slices up. The second
+// kernel and each slice's own set-up cost a few microseconds, so bands
+// shorter than 3 * kMinSliceTiles tiles are not cut (measured on d12-shaped
+// launches: a batch of one at T = 2048 takes 37 us in 4 slices against 62
+// whole; a 512-token chunk at offset 1536, 52 us in 2 slices against 62; a
+// chunk at offset 512, 16 tiles, 40.6 us in 2 slices against 38.4 whole).
+constexpr int kCUs = 256;  // compute units of the MI355X
+constexpr int kMinSliceTiles = 8;
+constexpr int kMaxSplits = 16;
+template <int NW>
+constexpr int wg_per_cu() { return NW == 2 ? 2 : 1; }  // resident bf16 workgroups per unit
+
+static int fwd_splits(long long grid, int cap, int tiles) {
+  if (grid <= 0 || 2 * grid > cap || tiles < 3 * kMinSliceTiles) return 1;
+  int ns = (int)(cap / grid);
+  ns = min(ns, tiles / kMinSliceTiles);
+  ns = min(ns, kMaxSplits);
+  return max(ns, 1);
+}
+// key tiles of the heaviest query tile (one of the last two)
+static int max_key_tiles(const FwdArgs& a) {
+  const int np = 1 << a.bp_log2;
+  int best = 0;
+  for (int qt = max(0, a.nqt - 2); qt < a.nqt; ++qt) {
+    const int q0 = qt * np + a.kofs;
+    const int ql = min(q0 + np, a.kofs + a.T) - 1;
+    const int kf = max(0, q0 - a.W + 1);
+    best = max(best, ql / 64 - kf / 64 + 1);
+  }
+  return best;
+}
+static size_t part_bytes_for(int nsplit, long long rows, int D) {
+  return nsplit > 1 ? (size_t)nsplit * (size_t)rows * (size_t)(D + 1) * sizeof(float) : 0;
+}
+
+// The 4-wave D = 128 body with the slice bookkeeping does not fit its
+// registers; sliced D = 128 launches use the 2-wave kernel, which does (two
+// workgroups of half the columns per compute unit).
+template <int D, int NW>
+constexpr bool fwd_can_split() { return !(D == 128 && NW == 4); }
 
 template <int D, int NW>
-static hipError_t launch_bf16(FwdArgs a, int hpw, hipStream_t stream) {
+static long long bf16_grid(int B, int T, int H, int hpw) {
+  using C = BfCfg<D, NW>;
+  const int np = C::NC / hpw;
+  return (long long)((T + np - 1) / np) * B * (H / hpw);
+}
+
+// query tiles of the NW-wave kernel in a, and the slices it would cut
+template <int D, int NW>
+static int plan_bf16(FwdArgs& a, int hpw, size_t part_bytes) {
   using C = BfCfg<D, NW>;
   a.bp_log2 = ilog2(C::NC / hpw);
   a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
+  if (!fwd_can_split<D, NW>() || a.part == nullptr) return 1;
+  const int ns = fwd_splits((long long)a.nqt * a.B * a.ngroups, kCUs * wg_per_cu<NW>(), max_key_tiles(a));
+  return part_bytes_for(ns, a.rows, D) > part_bytes ? 1 : ns;
+}
+
+template <int D, int NW>
+static hipError_t launch_bf16(FwdArgs a, int hpw, size_t part_bytes, hipStream_t stream) {
+  using C = BfCfg<D, NW>;
+  a.nsplit = plan_bf16<D, NW>(a, hpw, part_bytes);
   const long long grid = (long long)a.nqt * a.B * a.ngroups;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
-  return hipGetLastError();
+  if (grid * a.nsplit > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.nsplit == 1) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+    return hipGetLastError();
+  }
+  if constexpr (fwd_can_split<D, NW>()) {
+    hipLaunchKernelGGL((attn_fwd_bf16_split_kernel<D, NW>), dim3((unsigned)(grid * a.nsplit)),
+                       dim3(C::NT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long threads = (long long)a.rows * (D / 4);
+    hipLaunchKernelGGL(attn_split_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, stream, (const float*)a.part, (uint16_t*)a.o, a.rows, a.nsplit);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidConfiguration;
+  }
+}
+
+// heads per workgroup of the bf16 kernel: largest power of two dividing G, at most 32
+static int heads_per_wg(int G) {
+  int hpw = 1;
+  while (hpw < 32 && (G % (hpw * 2)) == 0) hpw *= 2;
+  return hpw;
 }
 
 template <int D>
-static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
+static size_t part_bytes_d(int B, int T, int H, int Hkv, int Tk) {
+  const int hpw = heads_per_wg(H / Hkv);
+  const int tiles = Tk / 64 + 2;  // at least the key tiles of any query tile
+  int ns = 1;
+  if constexpr (fwd_can_split<D, fwd_waves<D>()>())
+    ns = fwd_splits(bf16_grid<D, fwd_waves<D>()>(B, T, H, hpw), kCUs * wg_per_cu<fwd_waves<D>()>(), tiles);
+  if constexpr (D == 128) ns = max(ns, fwd_splits(bf16_grid<D, 2>(B, T, H, hpw), kCUs * wg_per_cu<2>(), tiles));
+  return part_bytes_for(ns, (long long)B * T * H, D);
+}
+
+template <int D>
+static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, size_t part_bytes, hipStream_t stream) {
   a.qscale = kLog2e / sqrtf((float)D);
   if (dt == kBF16) {
-    // heads per workgroup: largest power of two dividing G, at most 32
-    int hpw = 1;
-    while (hpw < 32 && (a.G % (hpw * 2)) == 0) hpw *= 2;
+    const int hpw = heads_per_wg(a.G);
     a.hpw_log2 = ilog2(hpw);
     a.ngroups = a.H / hpw;
     if constexpr (D == 128) {
-      if (fwd_narrow<D>(a.T, a.W)) return launch_bf16<D, 2>(a, hpw, stream);
+      // the narrow band, or a launch that is cut into slices
+      FwdArgs a2 = a;
+      if (fwd_narrow<D>(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1)
+        return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
     }
-    return launch_bf16<D, fwd_waves<D>()>(a, hpw, stream);
+    return launch_bf16<D, fwd_waves<D>()>(a, hpw, part_bytes, stream);
   } else {
     a.hpw_log2 = 0;
     a.ngroups = a.H;
@@ -1056,9 +1271,19 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
+size_t attn_core_part_bytes(int B, int T, int H, int Hkv, int D, int Tk, Dtype dt) {
+  if (dt != kBF16 || B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Tk < T) return 0;
+  switch (D) {
+    case 32: return part_bytes_d<32>(B, T, H, Hkv, Tk);
+    case 64: return part_bytes_d<64>(B, T, H, Hkv, Tk);
+    case 128: return part_bytes_d<128>(B, T, H, Hkv, Tk);
+    default: return 0;
+  }
+}
+
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
                             int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
-                            Dtype dt, hipStream_t stream) {
+                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream) {
   FwdArgs a{};
   a.q = q;
   a.kp = kp;
@@ -1073,10 +1298,12 @@ hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* 
   a.kofs = kofs;
   a.Tk = Tk;
   a.G = H / Hkv;
+  a.rows = B * T * H;
+  a.part = part_bytes > 0 ? (float*)part : nullptr;
   switch (D) {
-    case 32: return attn_fwd_d<32>(a, dt, stream);
-    case 64: return attn_fwd_d<64>(a, dt, stream);
-    case 128: return attn_fwd_d<128>(a, dt, stream);
+    case 32: return attn_fwd_d<32>(a, dt, part_bytes, stream);
+    case 64: return attn_fwd_d<64>(a, dt, part_bytes, stream);
+    case 128: return attn_fwd_d<128>(a, dt, part_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

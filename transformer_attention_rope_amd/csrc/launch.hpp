@@ -25,10 +25,13 @@ hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k
                               Dtype dt, hipStream_t stream);
 
 // attention from raw q (rotated/normalised in the kernel with tabq), k' and v;
-// kp and v hold Tk key rows per sequence, query row t sits at key row kofs + t
+// kp and v hold Tk key rows per sequence, query row t sits at key row kofs + t.
+// part (part_bytes, at least attn_core_part_bytes) holds the partial rows of a
+// launch whose key tiles are cut into slices; with part_bytes 0 there is none.
+size_t attn_core_part_bytes(int B, int T, int H, int Hkv, int D, int Tk, Dtype dt);
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
                             int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
-                            Dtype dt, hipStream_t stream);
+                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
