@@ -40,6 +40,11 @@ Readings where the pages are silent (each is listed with its pin in the design doc):
     their normalised, rotated keys and raw values are written there first,
     then query t (position P + t) attends to cache rows j with
     0 <= P + t - j < W.  Rows before P are used as stored.
+  * Multi-sample decode over one shared prompt cache: the Lp prompt rows are
+    held once (batch 1) and every sample's own rows (positions Lp..) in its
+    own cache, row r holding position Lp + r; the result is that of a decode
+    step over per-sample copies of the prompt cache followed by the sample's
+    rows.  seqlens[b] = L in [Lp + 1, Lp + Tgen].
 """
 from __future__ import annotations
 
@@ -230,4 +235,44 @@ def attn_prefill(q, k, v, k_cache, v_cache, window: int, base: float = 10000.0,
             S = np.where(vis, S, -np.inf)
             E = np.exp(S - S.max(axis=1, keepdims=True))
             o[b, :, h] = (E / E.sum(axis=1, keepdims=True)) @ vc[b, :P + T, g]
+    return o, kc, vc
+
+
+def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens,
+                       window: int, base: float = 10000.0):
+    """One decode step of B samples that share one prompt cache ([S10] §10.6:
+    the prompt is prefilled once and every sample continues from its cache).
+
+    q (B,H,D); k_new, v_new (B,Hkv,D) raw; k_prompt, v_prompt (Lp,Hkv,D) the
+    prompt's rows, used as stored; k_cache, v_cache (B,Tgen,Hkv,D), row r of
+    sample b holding position Lp + r; seqlens (B,) with L in [Lp+1, Lp+Tgen]
+    counting the new token, at position L - 1.  The new token's normalised,
+    rotated key and raw value go to row L-1-Lp of its sample's caches, then its
+    query attends to positions max(0, L - W) .. L - 1.  Returns (o (B,H,D),
+    k_cache_out, v_cache_out).
+    """
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    kp, vp = _f64(k_prompt), _f64(v_prompt)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    L_all = np.asarray(_f64(seqlens), dtype=np.int64)
+    B, H, D = q.shape
+    Hkv = k_new.shape[1]
+    Lp = kp.shape[0]
+    G = H // Hkv
+    o = np.empty((B, H, D), dtype=np.float64)
+    for b in range(B):
+        L = int(L_all[b])
+        p = L - 1
+        qn = qk_norm(rope(q[b], p, base))                  # (H, D)
+        kc[b, p - Lp] = qk_norm(rope(k_new[b], p, base))
+        vc[b, p - Lp] = v_new[b]
+        lo = max(0, L - window)
+        # the rows of positions lo .. L-1: the prompt's, then the sample's own
+        keys = np.concatenate([kp[lo:Lp], kc[b, max(lo, Lp) - Lp:L - Lp]], axis=0)
+        vals = np.concatenate([vp[lo:Lp], vc[b, max(lo, Lp) - Lp:L - Lp]], axis=0)
+        for h in range(H):
+            g = h // G
+            s = (keys[:, g] @ qn[h]) / math.sqrt(D)
+            e = np.exp(s - s.max())
+            o[b, h] = (e / e.sum()) @ vals[:, g]
     return o, kc, vc

@@ -424,4 +424,43 @@ def pin_prefill_brute(O):
             _close(o[0, t, h], want, tol=1e-12, what=f"prefill brute t={t} h={h}")
 
 
+# ---------------------------------------------------- shared-prompt decode pins
+
+def pin_decode_shared_equals_copied_caches(O):
+    """One prompt prefilled once, its cache copied to every sample, each sample
+    with its own generated rows: decoding over the copies equals decoding over
+    the one shared prompt cache plus the samples' own rows."""
+    r = _rng(41)
+    B, Lp, Tgen, H, Hkv, D = 3, 7, 6, 4, 2, 8
+    kp = r.standard_normal((Lp, Hkv, D))
+    vp = r.standard_normal((Lp, Hkv, D))
+    kg = r.standard_normal((B, Tgen, Hkv, D))
+    vg = r.standard_normal((B, Tgen, Hkv, D))
+    q = r.standard_normal((B, H, D))
+    kn = r.standard_normal((B, Hkv, D))
+    vn = r.standard_normal((B, Hkv, D))
+    kfull = np.concatenate([np.broadcast_to(kp, (B, Lp, Hkv, D)), kg], axis=1)
+    vfull = np.concatenate([np.broadcast_to(vp, (B, Lp, Hkv, D)), vg], axis=1)
+    for W in (1, 3, 8, 13):
+        L = np.array([Lp + 1, Lp + 4, Lp + Tgen])
+        o1, kc1, vc1 = O.attn_decode(q, kn, vn, kfull, vfull, L, W)
+        o2, kc2, vc2 = O.attn_decode_shared(q, kn, vn, kp, vp, kg, vg, L, W)
+        _close(o2, o1, tol=1e-12, what=f"shared vs copied W={W}")
+        _close(kc2, kc1[:, Lp:], tol=0, what="sample k rows")
+        _close(vc2, vc1[:, Lp:], tol=0, what="sample v rows")
+
+
+def pin_decode_shared_first_generated_token(O):
+    """The first generated token with W = 1 sees only itself: o = v_new."""
+    r = _rng(42)
+    kp, vp = r.standard_normal((5, 2, 8)), r.standard_normal((5, 2, 8))
+    kg, vg = r.standard_normal((2, 4, 2, 8)), r.standard_normal((2, 4, 2, 8))
+    q, kn, vn = r.standard_normal((2, 4, 8)), r.standard_normal((2, 2, 8)), r.standard_normal((2, 2, 8))
+    o, kc, vc = O.attn_decode_shared(q, kn, vn, kp, vp, kg, vg, np.array([6, 6]), 1)
+    _close(o, np.repeat(vn, 2, axis=1), what="W=1")
+    keep = np.arange(4) != 0
+    _close(kc[:, keep], kg[:, keep], tol=0, what="other k rows kept")
+    _close(vc[:, 0], vn, tol=0, what="appended v")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

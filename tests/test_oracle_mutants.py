@@ -185,6 +185,17 @@ def _prefill_no_v_append(q, k, v, k_cache, v_cache, window, base=10000.0, pos_of
     return o, kc, R._f64(v_cache).copy()
 
 
+_orig_decode_shared = R.attn_decode_shared
+
+
+def _decode_shared_row_off_by_one(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens,
+                                  window, base=10000.0):
+    # reads the samples' own rows one row late (position p from row p - Lp + 1)
+    kc = np.roll(R._f64(k_cache), -1, axis=1)
+    vc = np.roll(R._f64(v_cache), -1, axis=1)
+    return _orig_decode_shared(q, k_new, v_new, k_prompt, v_prompt, kc, vc, seqlens, window, base)
+
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign),
     "rope_half_split": ("rope", _rope_half_split),
@@ -206,6 +217,7 @@ MUTANTS = {
     "prefill_rope_from_zero": ("attn_prefill", _shifted_prefill_entry),
     "prefill_window_plus_one": ("attn_prefill", _prefill_window_plus_one),
     "prefill_no_v_append": ("attn_prefill", _prefill_no_v_append),
+    "decode_shared_row_off_by_one": ("attn_decode_shared", _decode_shared_row_off_by_one),
 }
 
 
