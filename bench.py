@@ -158,7 +158,7 @@ def main():
                     help="untimed back-to-back GPU work before each timed part (clock ramp)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "copy"],
+                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "shared", "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -402,6 +402,54 @@ def main():
             print(json.dumps(pre))
             return
 
+    # ----------------------------- several samples over one shared prompt cache
+    shd = {}
+    if args.only in ("all", "shared"):
+        sc = wl.SHARED
+        B, Lp, Tgen, H, Hkv, D = sc["B"], sc["Lp"], sc["Tgen"], sc["H"], sc["Hkv"], sc["D"]
+        ssets, csets = [], []
+        for s_ in range(args.sets):
+            q, kn, vn, kp, vp, kc, vc, L = wl.decode_shared_inputs(seed=s_)
+            ssets.append([t.to(dev) for t in (q, kn, vn, kp, vp, kc, vc, L)] + [torch.empty_like(q, device=dev)])
+            # the per-sample copies of the prompt cache that the shared form avoids
+            kf = torch.cat([kp.unsqueeze(0).expand(B, -1, -1, -1), kc], dim=1).contiguous()
+            vf = torch.cat([vp.unsqueeze(0).expand(B, -1, -1, -1), vc], dim=1).contiguous()
+            csets.append((kf.to(dev), vf.to(dev)))
+        for Wd in (2048, 512):
+            wss = torch.empty(max(nc.attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, Wd), 1),
+                              dtype=torch.uint8, device=dev)
+            wsc = nc.decode_workspace(B, Lp + Tgen, H, Hkv, D, Wd, device=dev)
+
+            def sstep_(i, Wd=Wd, wss=wss):
+                q, kn, vn, kp, vp, kc, vc, L, o = ssets[i % len(ssets)]
+                nc.attn_decode_shared(q, kn, vn, kp, vp, kc, vc, L, window=Wd, out=o, workspace=wss)
+
+            def cstep_(i, Wd=Wd, wsc=wsc):
+                q, kn, vn, kp, vp, kc, vc, L, o = ssets[i % len(ssets)]
+                kf, vf = csets[i % len(csets)]
+                nc.attn_decode(q, kn, vn, kf, vf, L, window=Wd, out=o, workspace=wsc)
+
+            prime(f"shared_W{Wd}", sstep_)
+            ms_s = event_time_ms(sstep_, K, torch)
+            prime(f"copied_W{Wd}", cstep_)
+            ms_c = event_time_ms(cstep_, K, torch)
+            lens = [ss[7].cpu().tolist() for ss in ssets]
+            ub = sum(wl.decode_shared_bytes(l, Lp, Hkv, D, Wd, H) for l in lens) / len(lens)
+            cb = sum(wl.decode_bytes(l, Hkv, D, Wd, H) for l in lens) / len(lens)
+            shd[f"W{Wd}"] = {"us_per_call": round(ms_s * 1e3, 2),
+                             "unique_bytes": int(ub),
+                             "GB_per_s_unique": round(ub / (ms_s * 1e-3) / 1e9, 1),
+                             "copied_caches_us_per_call": round(ms_c * 1e3, 2),
+                             "copied_caches_bytes": int(cb),
+                             "speedup_vs_copied": round(ms_c / ms_s, 3)}
+        shd["workload"] = (f"{B} samples of a {Lp}-token prompt (one shared prompt cache), each with "
+                           f"1..{Tgen} tokens of its own, H=Hkv={H} D={D}, bf16; against nc_attn_decode "
+                           f"over per-sample copies of the prompt cache")
+        del ssets, csets
+        if args.only == "shared":
+            print(json.dumps(shd))
+            return
+
     # ---------------------------------------------------------------- line
     step_ms = out["step_ms"]
     value = flops / (step_ms * 1e-3) / 1e12
@@ -437,6 +485,7 @@ def main():
         "rope_qknorm": rope,
         "stacks": stacks,
         "prefill_cache": pre,
+        "decode_shared_prompt": shd,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_budget)

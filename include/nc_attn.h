@@ -36,9 +36,10 @@
  *     enqueued asynchronously on it and nothing is allocated, freed or
  *     synchronised; the library keeps no state between calls and is
  *     thread-safe;
- *   - inputs are not modified, except the two caches of nc_attn_decode
- *     (exactly one row per sequence and K/V head) and of nc_attn_prefill
- *     (exactly the chunk's T rows per sequence and K/V head).
+ *   - inputs are not modified, except the two caches of nc_attn_decode and
+ *     nc_attn_decode_shared (exactly one row per sequence and K/V head) and
+ *     of nc_attn_prefill (exactly the chunk's T rows per sequence and K/V
+ *     head).
  *
  * Errors: arguments are validated on the host before any HIP call. A non-OK
  * status means nothing was enqueued. NC_ERR_INVALID: bad pointer, size,
@@ -72,7 +73,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 4
+#define NC_ABI_VERSION 5
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -222,6 +223,44 @@ nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new,
                          void* o, int B, int Tmax, int H, int Hkv, int D,
                          int window, double rope_base, nc_dtype dtype,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_decode_shared -- one decode step for B samples continuing one
+ * prompt, over a single shared copy of the prompt's cache ([S10] §10.6: the
+ * prompt is prefilled once at batch 1 and every sample generates from its
+ * cache; here the samples read the one prompt cache instead of copies of it).
+ *
+ *   q         (B, H,   D)        raw query of each sample's new token
+ *   k_new     (B, Hkv, D)        raw key of the new token
+ *   v_new     (B, Hkv, D)        value of the new token
+ *   k_prompt  (Lp, Hkv, D)       rotated, normalised keys of prompt positions
+ *                                0 .. Lp-1 (for instance written by
+ *                                nc_attn_prefill with B = 1); only read
+ *   v_prompt  (Lp, Hkv, D)       their values; only read
+ *   k_cache   (B, Tgen, Hkv, D)  row r of sample b holds position Lp + r;
+ *                                rows before L-1-Lp are used as stored, row
+ *                                L-1-Lp is overwritten with norm(rope(k_new))
+ *   v_cache   (B, Tgen, Hkv, D)  row L-1-Lp is overwritten with v_new
+ *   seqlens   (B,) int32 DEVICE array, L = seqlens[b] in [Lp+1, Lp+Tgen]
+ *                                counts the prompt, the sample's earlier
+ *                                tokens and the new token (position L-1)
+ *   o         (B, H, D)          softmax over positions max(0, L-window) ..
+ *                                L-1, prompt positions from the shared cache
+ * The result equals nc_attn_decode over per-sample caches holding the prompt
+ * rows followed by the sample's rows. seqlens values outside [Lp+1, Lp+Tgen]
+ * are clamped to that range. Workspace as for nc_attn_decode (a sample's keys
+ * are processed in chunks that lie wholly in the prompt or wholly in its own
+ * rows). Requires Lp >= 1, Tgen >= 1, the sizes of nc_attn_decode, and q,
+ * k_new, v_new, o not overlapping any cache.
+ */
+size_t nc_attn_decode_shared_workspace_bytes(int B, int Lp, int Tgen, int H, int Hkv, int D,
+                                             int window);
+nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                const void* k_prompt, const void* v_prompt, int Lp,
+                                void* k_cache, void* v_cache, const int32_t* seqlens,
+                                void* o, int B, int Tgen, int H, int Hkv, int D,
+                                int window, double rope_base, nc_dtype dtype,
+                                void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

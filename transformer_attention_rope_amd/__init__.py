@@ -11,6 +11,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
     attn_prep(k, ...) -> workspace;  attn_core(q, v, workspace, window=...) -> o
     attn_prefill(q, k, v, k_cache, v_cache, window=..., pos_offset=0, rope_base=1e4) -> o
     attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window=..., rope_base=1e4) -> o
+    attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens, window=...) -> o
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_prefill", "attn_decode",
+    "attn_decode_shared", "attn_decode_shared_workspace_bytes",
     "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
     "rope_qknorm_workspace_bytes",
@@ -49,6 +51,9 @@ _SIGS = {
     "nc_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                              _vp, _sz, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_decode_shared_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "nc_attn_decode_shared": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                   _i, _d, _i, _vp, _sz, _vp]),
     "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
                             _vp, _sz, _vp]),
 }
@@ -140,6 +145,10 @@ def attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, dtype=torch.bfloat16) ->
 
 def attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window) -> int:
     return int(lib().nc_attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window))
+
+
+def attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window) -> int:
+    return int(lib().nc_attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window))
 
 
 def _workspace(nbytes: int, device, workspace):
@@ -279,4 +288,36 @@ def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, *, window: int,
     _call("nc_attn_decode", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
           _ptr(seqlens), _ptr(o), B, Tmax, H, Hkv, D, int(window), float(rope_base), _dt(q),
           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o
+
+
+def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens, *,
+                       window: int, rope_base: float = 10000.0, out=None, workspace=None):
+    """One decode step of B samples continuing one prompt: prompt positions from the
+    shared (Lp,Hkv,D) caches, the samples' own positions Lp.. from their
+    (B,Tgen,Hkv,D) caches, whose row L-1-Lp receives the new token (in place).
+    q (B,H,D); k_new, v_new (B,Hkv,D); seqlens (B,) int32 on the GPU -> o (B,H,D)."""
+    q = _gpu(q, "q", 3)
+    k_new = _gpu(k_new, "k_new", 3, q.dtype)
+    v_new = _gpu(v_new, "v_new", 3, q.dtype)
+    k_prompt = _gpu(k_prompt, "k_prompt", 3, q.dtype)
+    v_prompt = _gpu(v_prompt, "v_prompt", 3, q.dtype)
+    k_cache = _gpu(k_cache, "k_cache", 4, q.dtype)
+    v_cache = _gpu(v_cache, "v_cache", 4, q.dtype)
+    seqlens = _gpu(seqlens, "seqlens", 1, torch.int32)
+    B, H, D = q.shape
+    Hkv = k_new.shape[1]
+    Lp, Tgen = k_prompt.shape[0], k_cache.shape[1]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(k_prompt.shape) != (Lp, Hkv, D) or tuple(v_prompt.shape) != (Lp, Hkv, D)
+            or tuple(k_cache.shape) != (B, Tgen, Hkv, D) or tuple(v_cache.shape) != (B, Tgen, Hkv, D)
+            or tuple(seqlens.shape) != (B,)):
+        raise ValueError("shared decode tensor shapes are inconsistent")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 3, q.dtype)
+    need = attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window)
+    ws = _workspace(need, q.device, workspace)
+    _call("nc_attn_decode_shared", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_prompt), _ptr(v_prompt),
+          Lp, _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), B, Tgen, H, Hkv, D, int(window),
+          float(rope_base), _dt(q), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+          _stream(q))
     return o

@@ -254,7 +254,7 @@ nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_c
 // -------------------------------------------------------------- attn_decode
 size_t nc_attn_decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window) {
   if (B < 1 || Tmax < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || window < 1) return 0;
-  const size_t n = nc::decode_workspace_bytes(B, Tmax, H, Hkv, D, window);
+  const size_t n = nc::decode_workspace_bytes(B, Tmax, H, Hkv, D, window, 0);
   return n ? round_up(n) : 0;
 }
 
@@ -285,6 +285,49 @@ nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, vo
                                         dt == NC_BF16 ? nc::kBF16 : nc::kF32, ws,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
+  return ok();
+}
+
+// ------------------------------------------------- attn_decode_shared
+size_t nc_attn_decode_shared_workspace_bytes(int B, int Lp, int Tgen, int H, int Hkv, int D,
+                                             int window) {
+  if (B < 1 || Lp < 1 || Tgen < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || window < 1 ||
+      (long long)Lp + Tgen > (1LL << 30))
+    return 0;
+  const size_t n = nc::decode_workspace_bytes(B, Lp + Tgen, H, Hkv, D, window, Lp);
+  return n ? round_up(n) : 0;
+}
+
+nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                const void* k_prompt, const void* v_prompt, int Lp, void* k_cache,
+                                void* v_cache, const int32_t* seqlens, void* o, int B, int Tgen,
+                                int H, int Hkv, int D, int window, double rope_base, nc_dtype dt,
+                                void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_common(B, Tgen, H, Hkv, D, dt, "Tgen");
+  if (s != NC_OK) return s;
+  if (Lp < 1) return fail(NC_ERR_INVALID, "Lp must be >= 1 (got %d)", Lp);
+  if (H / Hkv > 64) return fail(NC_ERR_UNSUPPORTED, "H/Hkv=%d query heads per K/V head exceed 64", H / Hkv);
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, Lp, Tgen)) != NC_OK) return s;
+  if ((s = check_seq_bytes(Lp, Hkv, D, dt)) != NC_OK) return s;
+  if ((s = check_seq_bytes(Tgen, Hkv, D, dt)) != NC_OK) return s;
+  const char* names[] = {"q", "k_new", "v_new", "k_prompt", "v_prompt", "k_cache", "v_cache", "o"};
+  const void* ptrs[] = {q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, o};
+  if ((s = check_ptrs(names, ptrs, 8)) != NC_OK) return s;
+  if (seqlens == nullptr) return fail(NC_ERR_INVALID, "seqlens is NULL");
+  if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+    return fail(NC_ERR_INVALID, "seqlens is not 4-byte aligned");
+  const size_t need = nc_attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window);
+  if (need > 0) {
+    if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL but %zu bytes are required", need);
+    if (!aligned16(ws)) return fail(NC_ERR_INVALID, "ws is not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+  }
+  hipError_t e = nc::launch_attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, Lp, k_cache,
+                                               v_cache, seqlens, o, B, Tgen, H, Hkv, D, window,
+                                               rope_base, to_dt(dt), ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode_shared launch");
   return ok();
 }
 

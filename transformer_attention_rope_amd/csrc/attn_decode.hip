@@ -30,6 +30,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace nc {
@@ -38,12 +39,17 @@ struct DecArgs {
   const void* q;
   const void* k_new;
   const void* v_new;
-  void* k_cache;
+  void* k_cache;        // (B, Tgen, Hkv, D): row r holds position Lp + r
   void* v_cache;
+  const void* k_prompt;  // (Lp, Hkv, D): positions 0 .. Lp-1, shared by all sequences
+  const void* v_prompt;
   const int32_t* seqlens;
   void* o;
   float* part;  // [B][H][nsplit][D + 2]: unnormalised o (D), max, sum
-  int B, Tmax, H, Hkv, G, W;
+  int B, Tmax, H, Hkv, G, W;  // Tmax = Lp + Tgen: the longest sequence
+  int Lp;       // shared prompt rows (0: none; every position in the sequence's cache)
+  int Tgen;     // rows per sequence cache
+  int nwg;      // workgroups with an item (the shared-prompt launch pads the grid to a multiple of 8)
   int C;        // keys per chunk (multiple of the keys per workgroup step)
   int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
   int ngh;      // head groups per K/V head = ceil(G / GP)
@@ -81,7 +87,28 @@ struct ElemTraits<float> {
   __device__ static float from_f(float x) { return x; }
 };
 
-__device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
+__device__ __forceinline__ int clamp_len(int L, int Lp, int Tmax) {
+  return L < Lp + 1 ? Lp + 1 : (L > Tmax ? Tmax : L);
+}
+
+// Chunks of the visible keys [lo, L): those of the shared prompt [lo, Lp)
+// first, then those of the sequence's own rows [max(lo, Lp), L), C keys each,
+// so that no chunk spans both caches. Returns the chunk count and, for chunk
+// c, its key range [ks0, ks1). With Lp = 0 these are C-key chunks from lo.
+__device__ __forceinline__ int dec_chunks(int L, int lo, int Lp, int C, int c, int& ks0, int& ks1) {
+  const int ea = min(L, Lp);                           // end of the prompt part
+  const int na = lo < ea ? (ea - lo + C - 1) / C : 0;  // its chunks
+  const int sb = max(lo, Lp);                          // start of the own part
+  const int nb = (L - sb + C - 1) / C;
+  if (c < na) {
+    ks0 = lo + c * C;
+    ks1 = min(ks0 + C, ea);
+  } else {
+    ks0 = sb + (c - na) * C;
+    ks1 = min(ks0 + C, L);
+  }
+  return na + nb;
+}
 
 // Sum over groups of `width` consecutive lanes, width a power of two <= 64.
 template <int width>
@@ -110,7 +137,9 @@ constexpr int kDecU = 4;
 template <int GP>
 constexpr int dec_bufs() { return GP <= 4 ? 3 : 2; }
 
-template <int D, int GP, typename Elem>
+// SH: a shared prompt cache holds positions 0 .. Lp-1 (nc_attn_decode_shared);
+// without it Lp = 0 and every position is in the sequence's own cache.
+template <int D, int GP, typename Elem, bool SH>
 __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   using TR = ElemTraits<Elem>;
   constexpr int EPC = TR::EPC;
@@ -130,10 +159,28 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = (int)blockIdx.x % a.nsplit;
-  const int rest = (int)blockIdx.x / a.nsplit;
+  int split = (int)blockIdx.x % a.nsplit;
+  int rest = (int)blockIdx.x / a.nsplit;
   int hg = rest % a.ngh;
   int bg = rest / a.ngh;
+  const int Lp = SH ? a.Lp : 0;
+  const int Tgen = SH ? a.Tgen : a.Tmax;
+  if constexpr (SH) {
+    // Shared prompt: workgroup i runs on XCD i % 8. Each XCD takes a
+    // contiguous run of the items ordered head-major, (g, b, head group,
+    // chunk), so that it reads the prompt rows of at most two or three K/V
+    // heads, which then stay in its L2 for all the sequences. The grid is
+    // 8 * per_x workgroups, so (i % 8, i / 8) -> lin is one-to-one onto
+    // [0, 8 * per_x); those past the nwg items have nothing to do.
+    const int per_x = (int)gridDim.x >> 3;
+    const int lin = ((int)blockIdx.x & 7) * per_x + ((int)blockIdx.x >> 3);
+    if (lin >= a.nwg) return;
+    split = lin % a.nsplit;
+    const int item = lin / a.nsplit;  // (g * B + b) * ngh + hg
+    hg = item % a.ngh;
+    const int gb = item / a.ngh;
+    bg = (gb % a.B) * a.Hkv + gb / a.B;
+  }
   __shared__ int s_len[kDecRankMaxB];  // clamped lengths (ranked placement only)
   if (a.order) {
     // Unsplit ranges (nsplit == 1): workgroup i takes the item of rank i (by
@@ -148,7 +195,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     const int i = (int)blockIdx.x;
     const int r = i < a.ncu ? i : nitems - 1 - (i - a.ncu);
     const int br = r / per_b;
-    for (int t = tid; t < a.B; t += 256) s_len[t] = clamp_len(a.seqlens[t], a.Tmax);
+    for (int t = tid; t < a.B; t += 256) s_len[t] = clamp_len(a.seqlens[t], Lp, a.Tmax);
     __syncthreads();
     for (int t = tid; t < a.B; t += 256) {
       const int lt = min(s_len[t], a.W);  // visible keys
@@ -166,14 +213,14 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
 
-  const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], a.Tmax);
+  const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], Lp, a.Tmax);
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
-  const int nch = (L - lo + a.C - 1) / a.C;
+  int ks0, ks1;
+  const int nch = dec_chunks(L, lo, Lp, a.C, split, ks0, ks1);
   if (split >= nch) return;
-  const int ks0 = lo + split * a.C;
-  const int ks1 = min(ks0 + a.C, L);
   const bool owns_new = ks1 == L;
+  const bool in_prompt = SH && ks0 < Lp;  // this chunk's rows are the shared prompt's
 
   const int h0 = g * a.G + hg * GP;
   const int nh = min(GP, a.G - hg * GP);
@@ -190,19 +237,29 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int cc = lane % CPR;        // 16-byte piece within the row
   const int kl = lane / CPR;        // key slot within the wave
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * sizeof(Elem);
-  const size_t base_el = (((size_t)b * a.Tmax + ks0) * a.Hkv + g) * D;
+  const size_t base_el = in_prompt ? ((size_t)ks0 * a.Hkv + g) * D
+                                   : (((size_t)b * Tgen + (ks0 - Lp)) * a.Hkv + g) * D;
   const uint32_t nrec = (uint32_t)(ks1 - ks0) * row_bytes;  // the chunk's keys only
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + base_el, nrec);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base_el, nrec);
+  const Elem* const ksrc = in_prompt ? (const Elem*)a.k_prompt : kc;
+  const Elem* const vsrc_c = in_prompt ? (const Elem*)a.v_prompt : vc;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(ksrc + base_el, nrec);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc_c + base_el, nrec);
   const int slot = wave * KPW + kl;   // key slot within a workgroup step
   const int nkeys = ks1 - ks0;
   u32x4_t kw[NBUF][U], vw[NBUF][U];
+  // the sequence's own rows are read once (non-temporal); the shared prompt's
+  // rows are read by every sequence and stay cached
   auto issue = [&](int it, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t off = (uint32_t)(it * KPI + u * 4 * KPW + slot) * row_bytes + cc * 16;
-      kw[set][u] = bload16_nt(rk, off, 0);
-      vw[set][u] = bload16_nt(rv, off, 0);
+      if (SH && in_prompt) {
+        kw[set][u] = bload16(rk, off, 0);
+        vw[set][u] = bload16(rv, off, 0);
+      } else {
+        kw[set][u] = bload16_nt(rk, off, 0);
+        vw[set][u] = bload16_nt(rv, off, 0);
+      }
     }
   };
   issue(0, 0);
@@ -269,10 +326,10 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
         const Elem ke = TR::from_f(ye * inv), ko = TR::from_f(yo * inv);
         knew_s[2 * i] = TR::to_f(ke);
         knew_s[2 * i + 1] = TR::to_f(ko);
-        Elem* dst = kc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
+        Elem* dst = kc + (((size_t)b * Tgen + (pos - Lp)) * a.Hkv + g) * D;
         dst[2 * i] = ke;
         dst[2 * i + 1] = ko;
-        Elem* vdst = vc + (((size_t)b * a.Tmax + pos) * a.Hkv + g) * D;
+        Elem* vdst = vc + (((size_t)b * Tgen + (pos - Lp)) * a.Hkv + g) * D;
         const Elem v0 = vn0, v1 = vn1;
         vdst[2 * i] = v0;
         vdst[2 * i + 1] = v1;
@@ -523,9 +580,10 @@ __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
   const int lane = threadIdx.x & 63;
   if (wid >= a.B * a.H) return;
   const int b = wid / a.H, h = wid - (wid / a.H) * a.H;
-  const int L = clamp_len(a.seqlens[b], a.Tmax);
+  const int L = clamp_len(a.seqlens[b], a.Lp, a.Tmax);
   const int lo = L > a.W ? L - a.W : 0;
-  const int nch = (L - lo + a.C - 1) / a.C;
+  int ks0, ks1;
+  const int nch = dec_chunks(L, lo, a.Lp, a.C, 0, ks0, ks1);
   if (nch <= 1) return;
   constexpr int PER = (D + 63) / 64;
   constexpr int NB = 8;  // chunk states loaded per batch
@@ -615,24 +673,36 @@ static int decode_nsplit(int Tmax, int W, int C) {
   return (span + C - 1) / C;
 }
 
-size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window) {
+// A shared prompt adds at most one chunk (the one cut at the prompt's end).
+size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window, int Lp) {
   const int C = decode_chunk(B, Tmax, H, Hkv, D, window);
-  const int ns = decode_nsplit(Tmax, window, C);
+  const int ns = decode_nsplit(Tmax, window, C) + (Lp > 0 ? 1 : 0);
   if (ns <= 1) return 0;
   return (size_t)B * H * ns * (D + 2) * sizeof(float);
+}
+
+template <int D, int GP, typename Elem>
+static void launch_decode_gp(bool sh, long long grid, const DecArgs& a, hipStream_t stream) {
+  if (sh)
+    hipLaunchKernelGGL((attn_decode_kernel<D, GP, Elem, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<D, GP, Elem, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
 }
 
 template <int D, typename Elem>
 static hipError_t decode_d(DecArgs a, hipStream_t stream) {
   const int GP = decode_gp(a.G);
   a.ngh = (a.G + GP - 1) / GP;
-  const long long grid = (long long)a.B * a.Hkv * a.ngh * a.nsplit;
+  a.nwg = (int)std::min<long long>((long long)a.B * a.Hkv * a.ngh * a.nsplit, 0x7fffffffLL);
+  const long long grid = a.Lp > 0 ? ((long long)a.B * a.Hkv * a.ngh * a.nsplit + 7) / 8 * 8
+                                  : (long long)a.B * a.Hkv * a.ngh * a.nsplit;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const bool sh = a.Lp > 0;
   switch (GP) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<D, 1, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<D, 2, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 4, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_decode_kernel<D, 8, Elem>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 1: launch_decode_gp<D, 1, Elem>(sh, grid, a, stream); break;
+    case 2: launch_decode_gp<D, 2, Elem>(sh, grid, a, stream); break;
+    case 4: launch_decode_gp<D, 4, Elem>(sh, grid, a, stream); break;
+    default: launch_decode_gp<D, 8, Elem>(sh, grid, a, stream); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit <= 1) return e;
@@ -642,16 +712,22 @@ static hipError_t decode_d(DecArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                              void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
-                              int H, int Hkv, int D, int window, double rope_base, Dtype dt,
-                              void* ws, hipStream_t stream) {
+hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                     const void* k_prompt, const void* v_prompt, int Lp,
+                                     void* k_cache, void* v_cache, const int32_t* seqlens, void* o,
+                                     int B, int Tgen, int H, int Hkv, int D, int window,
+                                     double rope_base, Dtype dt, void* ws, hipStream_t stream) {
   DecArgs a{};
+  const int Tmax = Lp + Tgen;
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_prompt = k_prompt;
+  a.v_prompt = v_prompt;
+  a.Lp = Lp;
+  a.Tgen = Tgen;
   a.seqlens = seqlens;
   a.o = o;
   a.B = B;
@@ -661,7 +737,7 @@ hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_ne
   a.G = H / Hkv;
   a.W = window;
   a.C = decode_chunk(B, Tmax, H, Hkv, D, window);
-  a.nsplit = decode_nsplit(Tmax, window, a.C);
+  a.nsplit = decode_nsplit(Tmax, window, a.C) + (Lp > 0 ? 1 : 0);
   a.log2_base = std::log2(rope_base);
   a.part = (float*)ws;
   a.ncu = device_cu_count();
@@ -676,6 +752,14 @@ hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_ne
     case 128: return bf ? decode_d<128, uint16_t>(a, stream) : decode_d<128, float>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
+                              int H, int Hkv, int D, int window, double rope_base, Dtype dt,
+                              void* ws, hipStream_t stream) {
+  return launch_attn_decode_shared(q, k_new, v_new, nullptr, nullptr, 0, k_cache, v_cache, seqlens,
+                                   o, B, Tmax, H, Hkv, D, window, rope_base, dt, ws, stream);
 }
 
 }  // namespace nc

@@ -33,10 +33,17 @@ hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* 
                             int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
                             void* part, size_t part_bytes, Dtype dt, hipStream_t stream);
 
-size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
+size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window, int Lp);
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
                               void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
                               int H, int Hkv, int D, int window, double rope_base, Dtype dt,
                               void* ws, hipStream_t stream);
+// decode over a shared (Lp, Hkv, D) prompt cache and per-sequence caches of
+// Tgen rows holding positions Lp ..
+hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                     const void* k_prompt, const void* v_prompt, int Lp,
+                                     void* k_cache, void* v_cache, const int32_t* seqlens, void* o,
+                                     int B, int Tgen, int H, int Hkv, int D, int window,
+                                     double rope_base, Dtype dt, void* ws, hipStream_t stream);
 
 }  // namespace nc

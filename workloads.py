@@ -144,6 +144,28 @@ def prefill_chunk_inputs(seed: int = 0, dtype=torch.bfloat16, **kw):
     return q, k, v, kc, vc
 
 
+# Several samples continuing one d12 prompt: 64 samples of a 1536-token prompt,
+# each with 1..512 tokens of its own (the new one included).
+SHARED = dict(B=64, Lp=1536, Tgen=512, H=6, Hkv=6, D=128)
+
+
+def decode_shared_inputs(seed: int = 0, dtype=torch.bfloat16, **kw):
+    """q (B,H,D), k_new and v_new (B,Hkv,D), the prompt caches (Lp,Hkv,D), the
+    samples' caches (B,Tgen,Hkv,D) and seqlens (B,) = Lp + uniform [1, Tgen]."""
+    c = dict(SHARED, **kw)
+    B, Lp, Tgen, H, Hkv, D = c["B"], c["Lp"], c["Tgen"], c["H"], c["Hkv"], c["D"]
+    base = SEED_BASE + 800 + 10 * seed
+    q = randn((B, H, D), base + T_Q, dtype)
+    k_new = randn((B, Hkv, D), base + T_K, dtype)
+    v_new = randn((B, Hkv, D), base + T_V, dtype)
+    k_prompt = randn((Lp, Hkv, D), base + T_KCACHE + 4, dtype)
+    v_prompt = randn((Lp, Hkv, D), base + T_VCACHE + 4, dtype)
+    k_cache = randn((B, Tgen, Hkv, D), base + T_KCACHE, dtype)
+    v_cache = randn((B, Tgen, Hkv, D), base + T_VCACHE, dtype)
+    seqlens = randint(1, Tgen, (B,), base + T_SEQLENS) + Lp
+    return q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens
+
+
 def small_prefill(B, T, H, Hkv, D, seed, dtype=torch.bfloat16, scale=1.0):
     """Seeded small case for parity sweeps (ragged T, odd windows, ...)."""
     q = randn((B, T, H, D), seed, torch.float32) * scale
@@ -170,6 +192,19 @@ def chunk_pairs(T: int, P: int, W: int) -> int:
 
 def prefill_chunk_flops(B, T, P, H, D, W) -> int:
     return 4 * D * chunk_pairs(T, P, W) * B * H
+
+
+def decode_shared_bytes(seqlens, Lp, Hkv, D, W, H, elem_bytes=2):
+    """Algorithmic HBM bytes of one shared-prompt decode call: every prompt row
+    visible to some sample, once; each sample's own visible rows; q, o, k_new,
+    v_new. (decode_bytes of the same lengths counts the prompt rows once per
+    sample, as over copies.)"""
+    row = Hkv * D * 2 * elem_bytes
+    lo_min = min(max(0, int(L) - W) for L in seqlens)
+    prompt_rows = max(0, Lp - lo_min)
+    own = sum(int(L) - max(Lp, int(L) - W) for L in seqlens)
+    B = len(seqlens)
+    return prompt_rows * row + own * row + (2 * B * H * D + 2 * B * Hkv * D) * elem_bytes
 
 
 def prefill_flops(B, T, H, D, W) -> int:
