@@ -159,6 +159,34 @@ def test_prefill_validation(kw, status, frag):
     assert frag in nc.lib().nc_last_error().decode()
 
 
+def _dsh(**kw):
+    a = dict(q=P, kn=P, vn=P, kp=P, vp=P, Lp=1536, kc=P, vc=P, sl=P, o=P, B=64, Tgen=512, H=6, Hkv=6,
+             D=128, window=2048, base=1e4, dt=0, ws=P, wsb=1 << 24, stream=None)
+    a.update(kw)
+    L = nc.lib()
+    return L.nc_attn_decode_shared(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["Lp"], a["kc"], a["vc"],
+                                   a["sl"], a["o"], a["B"], a["Tgen"], a["H"], a["Hkv"], a["D"],
+                                   a["window"], a["base"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(kp=None), 1, "k_prompt is NULL"),
+    (dict(vp=P + 4), 1, "not 16-byte aligned"),
+    (dict(Lp=0), 1, "Lp"),
+    (dict(Tgen=0), 1, "sizes"),
+    (dict(sl=None), 1, "seqlens is NULL"),
+    (dict(window=0), 1, "window"),
+    (dict(H=512, Hkv=4), 2, "exceed 64"),
+    (dict(D=96), 2, "head dim"),
+    (dict(ws=None), 1, "ws is NULL"),
+    (dict(wsb=64), 1, "workspace"),
+    (dict(Lp=1 << 30), 1, "exceeds"),
+])
+def test_decode_shared_validation(kw, status, frag):
+    assert _dsh(**kw) == status
+    assert frag in nc.lib().nc_last_error().decode()
+
+
 def test_workspace_queries():
     L = nc.lib()
     assert L.nc_rope_qknorm_workspace_bytes(2048, 128, 0) == 0
@@ -188,6 +216,10 @@ def test_workspace_queries():
     # one workgroup per (sequence, head) already fills the device: no split
     assert L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048) == 0
     assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0
+    # a shared prompt cuts each sequence's keys at the prompt's end: one more
+    # chunk state per (b, h), so room for two even when the range is not split
+    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 2048) == 64 * 6 * 2 * 130 * 4
+    assert L.nc_attn_decode_shared_workspace_bytes(64, 0, 512, 6, 6, 128, 2048) == 0
 
 
 def test_binding_refuses_cpu_tensors():
