@@ -11,7 +11,7 @@ Parity status of each function is stated in its module docstring:
     (+p*theta) are readings of the pages, which fix neither:
     parity unpinned for those two conventions (everything else pinned).
   * ``qk_norm``: the epsilon (1e-6) is a reading; parity unpinned for eps.
-  * ``attention`` / ``decode`` / ``prefill`` / ``decode_shared``: pinned (see tests/test_oracle_pins.py).
+  * ``attention`` / ``decode`` / ``prefill`` / ``decode_shared`` / ``value_gate``: pinned (see tests/test_oracle_pins.py).
 """
 from .reference import (  # noqa: F401
     EPS,
@@ -26,4 +26,5 @@ from .reference import (  # noqa: F401
     attn_decode,
     attn_prefill,
     attn_decode_shared,
+    value_gate,
 )

@@ -45,6 +45,10 @@ Readings where the pages are silent (each is listed with its pin in the design doc):
     own cache, row r holding position Lp + r; the result is that of a decode
     step over per-sample copies of the prompt cache followed by the sample's
     rows.  seqlens[b] = L in [Lp + 1, Lp + Tgen].
+  * Value-embedding gate ([TBL] notes, value residual): v' = v + gate * ve,
+    with ve shaped like v and one gate per (token, K/V head), both inputs;
+    v' replaces v everywhere (the cache stores v').  The pages give only the
+    formula; the shape of the gate is a reading.
 """
 from __future__ import annotations
 
@@ -174,15 +178,16 @@ def attn_fwd_rows(q, k, v, rows, window: int, base: float = 10000.0,
 
 
 def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window: int,
-                base: float = 10000.0):
+                base: float = 10000.0, ve_new=None, ve_gate_new=None):
     """One decode step over a contiguous per-layer cache ([S10]).
 
     q (B,H,D); k_new, v_new (B,Hkv,D) raw; caches (B,Tmax,Hkv,D) whose rows
     before L-1 are used as stored; seqlens (B,) with L in [1, Tmax] counting
     the new token.  Returns (o (B,H,D), k_cache_out, v_cache_out) where the
-    cache copies hold the appended row at index L-1.
+    cache copies hold the appended row at index L-1.  With ve_new (B,Hkv,D)
+    and ve_gate_new (B,Hkv), v_new is replaced by value_gate(v_new, ...).
     """
-    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    q, k_new, v_new = _f64(q), _f64(k_new), value_gate(v_new, ve_new, ve_gate_new)
     kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
     L_all = np.asarray(_f64(seqlens), dtype=np.int64)
     B, H, D = q.shape
@@ -205,17 +210,26 @@ def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window: int,
     return o, kc, vc
 
 
+def value_gate(v, ve, gate):
+    """v + gate * ve ([TBL] value residual); gate has v's shape minus the head dim."""
+    v = _f64(v)
+    if ve is None:
+        return v
+    return v + _f64(gate)[..., None] * _f64(ve)
+
+
 def attn_prefill(q, k, v, k_cache, v_cache, window: int, base: float = 10000.0,
-                 pos_offset: int = 0):
+                 pos_offset: int = 0, ve=None, ve_gate=None):
     """Prefill of a chunk of T tokens into a contiguous per-layer cache
     ([S10] append K/V, then attend; [S5.5] causal mask; [TBL] window).
 
     q (B,T,H,D), k and v (B,T,Hkv,D) raw rows of the tokens at positions
     P .. P+T-1 (P = pos_offset); caches (B,Tmax,Hkv,D) with P + T <= Tmax,
-    rows before P used as stored.  Returns (o (B,T,H,D), k_cache_out,
-    v_cache_out), the cache copies holding the chunk's rows.
+    rows before P used as stored.  With ve (B,T,Hkv,D) and ve_gate (B,T,Hkv),
+    v is replaced by value_gate(v, ve, ve_gate).  Returns (o (B,T,H,D),
+    k_cache_out, v_cache_out), the cache copies holding the chunk's rows.
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = _f64(q), _f64(k), value_gate(v, ve, ve_gate)
     kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
     B, T, H, D = q.shape
     Hkv = k.shape[2]
@@ -239,7 +253,7 @@ def attn_prefill(q, k, v, k_cache, v_cache, window: int, base: float = 10000.0,
 
 
 def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens,
-                       window: int, base: float = 10000.0):
+                       window: int, base: float = 10000.0, ve_new=None, ve_gate_new=None):
     """One decode step of B samples that share one prompt cache ([S10] §10.6:
     the prompt is prefilled once and every sample continues from its cache).
 
@@ -249,9 +263,9 @@ def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, se
     counting the new token, at position L - 1.  The new token's normalised,
     rotated key and raw value go to row L-1-Lp of its sample's caches, then its
     query attends to positions max(0, L - W) .. L - 1.  Returns (o (B,H,D),
-    k_cache_out, v_cache_out).
+    k_cache_out, v_cache_out).  ve_new, ve_gate_new as in attn_decode.
     """
-    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    q, k_new, v_new = _f64(q), _f64(k_new), value_gate(v_new, ve_new, ve_gate_new)
     kp, vp = _f64(k_prompt), _f64(v_prompt)
     kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
     L_all = np.asarray(_f64(seqlens), dtype=np.int64)

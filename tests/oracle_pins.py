@@ -463,4 +463,47 @@ def pin_decode_shared_first_generated_token(O):
     _close(vc[:, 0], vn, tol=0, what="appended v")
 
 
+# ------------------------------------------------------- value-embedding gate
+
+def pin_ve_gate_zero_is_identity(O):
+    """A zero gate leaves v, the caches and the output unchanged."""
+    q, k, v = _prefill_case(51, T=9)
+    ve = _rng(52).standard_normal(v.shape)
+    kc, vc = np.zeros((2, 12, 2, 8)), np.zeros((2, 12, 2, 8))
+    o0, kc0, vc0 = O.attn_prefill(q, k, v, kc, vc, 4, pos_offset=2)
+    o1, kc1, vc1 = O.attn_prefill(q, k, v, kc, vc, 4, pos_offset=2, ve=ve, ve_gate=np.zeros(v.shape[:3]))
+    _close(o1, o0, tol=0, what="o")
+    _close(vc1, vc0, tol=0, what="v cache")
+
+
+def pin_ve_gate_linearity(O):
+    """Attention is linear in V: with one gate g for every token and head,
+    o(v + g ve) = o(v) + g o(ve), and the cache holds v + g ve."""
+    q, k, v = _prefill_case(53, T=11)
+    ve = _rng(54).standard_normal(v.shape)
+    kc, vc = np.zeros((2, 14, 2, 8)), np.zeros((2, 14, 2, 8))
+    for g in (0.5, -1.25):
+        gate = np.full(v.shape[:3], g)
+        og, _, vcg = O.attn_prefill(q, k, v, kc, vc, 5, pos_offset=3, ve=ve, ve_gate=gate)
+        ov, _, _ = O.attn_prefill(q, k, v, kc, vc, 5, pos_offset=3)
+        oe, _, _ = O.attn_prefill(q, k, ve, kc, vc, 5, pos_offset=3)
+        _close(og, ov + g * oe, tol=1e-12, what=f"linearity g={g}")
+        _close(vcg[:, 3:14], v + g * ve, tol=1e-15, what="cached v'")
+
+
+def pin_ve_gate_per_token_brute(O):
+    """Per-token, per-head gates against the plain sum on a decode step."""
+    q, kn, vn, kc, vc = _decode_case(55, B=2, Tmax=6, H=2, Hkv=2, D=4)
+    r = _rng(56)
+    ve, gate = r.standard_normal(vn.shape), r.standard_normal(vn.shape[:2])
+    L = np.array([6, 3])
+    o, _, vco = O.attn_decode(q, kn, vn, kc, vc, L, 3, ve_new=ve, ve_gate_new=gate)
+    o_ref, _, _ = O.attn_decode(q, kn, vn + gate[..., None] * ve, kc, vc, L, 3)
+    _close(o, o_ref, tol=1e-12, what="decode with gate")
+    for b in range(2):
+        for g in range(2):
+            want = [vn[b, g, d] + gate[b, g] * ve[b, g, d] for d in range(4)]
+            _close(vco[b, L[b] - 1, g], want, tol=1e-15, what=f"appended v' b={b} g={g}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

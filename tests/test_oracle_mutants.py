@@ -112,25 +112,26 @@ def _core_variant(kind):
 _orig_decode = R.attn_decode
 
 
-def _decode_raw_append(q, k_new, v_new, k_cache, v_cache, seqlens, window, base=10000.0):
+def _decode_raw_append(q, k_new, v_new, k_cache, v_cache, seqlens, window, base=10000.0, **kw):
     # appends the raw key instead of the rotated, normalised one
-    o, kc, vc = _orig_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window, base)
+    o, kc, vc = _orig_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window, base, **kw)
     k_new = R._f64(k_new)
     for b, L in enumerate(np.asarray(R._f64(seqlens), dtype=np.int64)):
         kc[b, L - 1] = k_new[b]
     return o, kc, vc
 
 
-def _decode_window_plus_one(q, k_new, v_new, k_cache, v_cache, seqlens, window, base=10000.0):
-    return _orig_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window + 1, base)
+def _decode_window_plus_one(q, k_new, v_new, k_cache, v_cache, seqlens, window, base=10000.0, **kw):
+    return _orig_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window + 1, base, **kw)
 
 
 _orig_prefill = R.attn_prefill
 
 
-def _prefill_local_mask(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+def _prefill_local_mask(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0, ve=None,
+                        ve_gate=None):
     # masks with the chunk-local query index t instead of the position P + t
-    qf, kf, vf = R._f64(q), R._f64(k), R._f64(v)
+    qf, kf, vf = R._f64(q), R._f64(k), R.value_gate(v, ve, ve_gate)
     kc, vc = R._f64(k_cache).copy(), R._f64(v_cache).copy()
     B, T, H, D = qf.shape
     G = H // kf.shape[2]
@@ -171,17 +172,19 @@ def _shifted_prefill(q, k, v, k_cache, v_cache, window, base, P):
     return o, kc, vc
 
 
-def _shifted_prefill_entry(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
+def _shifted_prefill_entry(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0, ve=None,
+                           ve_gate=None):
     # rotates the chunk as if it started at position 0
-    return _shifted_prefill(q, k, v, k_cache, v_cache, window, base, int(pos_offset))
+    return _shifted_prefill(q, k, R.value_gate(v, ve, ve_gate), k_cache, v_cache, window, base,
+                            int(pos_offset))
 
 
-def _prefill_window_plus_one(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
-    return _orig_prefill(q, k, v, k_cache, v_cache, window + 1, base, pos_offset)
+def _prefill_window_plus_one(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0, **kw):
+    return _orig_prefill(q, k, v, k_cache, v_cache, window + 1, base, pos_offset, **kw)
 
 
-def _prefill_no_v_append(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0):
-    o, kc, _ = _orig_prefill(q, k, v, k_cache, v_cache, window, base, pos_offset)
+def _prefill_no_v_append(q, k, v, k_cache, v_cache, window, base=10000.0, pos_offset=0, **kw):
+    o, kc, _ = _orig_prefill(q, k, v, k_cache, v_cache, window, base, pos_offset, **kw)
     return o, kc, R._f64(v_cache).copy()
 
 
@@ -189,11 +192,21 @@ _orig_decode_shared = R.attn_decode_shared
 
 
 def _decode_shared_row_off_by_one(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens,
-                                  window, base=10000.0):
+                                  window, base=10000.0, **kw):
     # reads the samples' own rows one row late (position p from row p - Lp + 1)
     kc = np.roll(R._f64(k_cache), -1, axis=1)
     vc = np.roll(R._f64(v_cache), -1, axis=1)
-    return _orig_decode_shared(q, k_new, v_new, k_prompt, v_prompt, kc, vc, seqlens, window, base)
+    return _orig_decode_shared(q, k_new, v_new, k_prompt, v_prompt, kc, vc, seqlens, window, base, **kw)
+
+
+def _value_gate_on_v(v, ve, gate):
+    # scales v by the gate instead of adding the gated embedding
+    v = R._f64(v)
+    return v if ve is None else v * R._f64(gate)[..., None] + R._f64(ve)
+
+
+def _value_gate_dropped(v, ve, gate):
+    return R._f64(v)
 
 
 MUTANTS = {
@@ -218,6 +231,8 @@ MUTANTS = {
     "prefill_window_plus_one": ("attn_prefill", _prefill_window_plus_one),
     "prefill_no_v_append": ("attn_prefill", _prefill_no_v_append),
     "decode_shared_row_off_by_one": ("attn_decode_shared", _decode_shared_row_off_by_one),
+    "value_gate_on_v": ("value_gate", _value_gate_on_v),
+    "value_gate_dropped": ("value_gate", _value_gate_dropped),
 }
 
 
