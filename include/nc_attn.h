@@ -16,6 +16,16 @@
  *           architecture table and notes: RoPE, RMSNorm without parameters,
  *           QK-norm after RoPE, GQA, SSSL sliding window (short = 1/4 context).
  *
+ * Value-embedding gate ([TBL] notes, value residual: v = v + gate * ve). The
+ * three cache entry points (nc_attn_prefill, nc_attn_decode,
+ * nc_attn_decode_shared) take an optional pair ve (shaped like the values)
+ * and ve_gate (one value per token and K/V head, the values' shape without
+ * the head dim), both in the call's element type: the values written to the
+ * cache and attended to are v' = v + ve_gate * ve, formed in fp32 and rounded
+ * once to the element type. Both NULL: v unchanged. The ungated forward
+ * nc_attn_fwd equals nc_attn_prefill at pos_offset 0 with Tmax = T bit for
+ * bit, so a gated forward is that call with the pair.
+ *
  * Conventions fixed by this library where the pages are silent:
  *   RoPE rotates adjacent pairs (x[2i], x[2i+1]) by +p*theta_i with
  *   theta_i = rope_base^(-2i/D) and 0-based positions p = pos_offset + t;
@@ -73,7 +83,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 5
+#define NC_ABI_VERSION 6
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -190,9 +200,11 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
  */
 size_t nc_attn_prefill_workspace_bytes(int B, int T, int Tmax, int H, int Hkv, int D,
                                        nc_dtype dtype);
-nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
-                          void* v_cache, void* o, int B, int T, int Tmax, int H, int Hkv, int D,
-                          int window, double rope_base, int pos_offset, nc_dtype dtype,
+/* ve (B, T, Hkv, D), ve_gate (B, T, Hkv): optional value-embedding pair (above). */
+nc_status nc_attn_prefill(const void* q, const void* k, const void* v, const void* ve,
+                          const void* ve_gate, void* k_cache, void* v_cache, void* o,
+                          int B, int T, int Tmax, int H, int Hkv, int D, int window,
+                          double rope_base, int pos_offset, nc_dtype dtype,
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -218,7 +230,10 @@ nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_c
  * {32, 64, 128}; q, k_new, v_new and o must not overlap the caches.
  */
 size_t nc_attn_decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window);
+/* ve_new (B, Hkv, D), ve_gate (B, Hkv): optional value-embedding pair of the
+ * new token (above); the appended value is v_new + ve_gate * ve_new. */
 nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new,
+                         const void* ve_new, const void* ve_gate,
                          void* k_cache, void* v_cache, const int32_t* seqlens,
                          void* o, int B, int Tmax, int H, int Hkv, int D,
                          int window, double rope_base, nc_dtype dtype,
@@ -255,7 +270,9 @@ nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new,
  */
 size_t nc_attn_decode_shared_workspace_bytes(int B, int Lp, int Tgen, int H, int Hkv, int D,
                                              int window);
+/* ve_new, ve_gate: as for nc_attn_decode. */
 nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                const void* ve_new, const void* ve_gate,
                                 const void* k_prompt, const void* v_prompt, int Lp,
                                 void* k_cache, void* v_cache, const int32_t* seqlens,
                                 void* o, int B, int Tgen, int H, int Hkv, int D,

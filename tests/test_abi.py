@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 5
+    assert L.nc_abi_version() == 6
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -105,11 +105,11 @@ def test_rope_qknorm_validation():
 
 
 def _dec(**kw):
-    a = dict(q=P, kn=P, vn=P, kc=P, vc=P, sl=P, o=P, B=4, Tmax=2048, H=8, Hkv=2, D=128,
+    a = dict(q=P, kn=P, vn=P, ve=None, vg=None, kc=P, vc=P, sl=P, o=P, B=4, Tmax=2048, H=8, Hkv=2, D=128,
              window=512, base=1e4, dt=0, ws=P, wsb=1 << 24, stream=None)
     a.update(kw)
     L = nc.lib()
-    return L.nc_attn_decode(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["sl"], a["o"], a["B"],
+    return L.nc_attn_decode(a["q"], a["kn"], a["vn"], a["ve"], a["vg"], a["kc"], a["vc"], a["sl"], a["o"], a["B"],
                             a["Tmax"], a["H"], a["Hkv"], a["D"], a["window"], a["base"], a["dt"],
                             a["ws"], a["wsb"], a["stream"])
 
@@ -124,6 +124,8 @@ def _dec(**kw):
     (dict(D=16), 2, "head dim"),
     (dict(ws=None), 1, "ws is NULL"),
     (dict(wsb=8), 1, "workspace"),
+    (dict(ve=P), 1, "both be NULL"),
+    (dict(ve=P, vg=P + 3, dt=1), 1, "ve_gate is not aligned"),
 ])
 def test_decode_validation(kw, status, frag):
     assert _dec(**kw) == status
@@ -131,11 +133,11 @@ def test_decode_validation(kw, status, frag):
 
 
 def _pre(**kw):
-    a = dict(q=P, k=P, v=P, kc=P, vc=P, o=P, B=2, T=64, Tmax=256, H=4, Hkv=2, D=64, window=128,
-             base=1e4, off=128, dt=0, ws=P, wsb=1 << 20, stream=None)
+    a = dict(q=P, k=P, v=P, ve=None, vg=None, kc=P, vc=P, o=P, B=2, T=64, Tmax=256, H=4, Hkv=2, D=64,
+             window=128, base=1e4, off=128, dt=0, ws=P, wsb=1 << 20, stream=None)
     a.update(kw)
     L = nc.lib()
-    return L.nc_attn_prefill(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["o"], a["B"], a["T"],
+    return L.nc_attn_prefill(a["q"], a["k"], a["v"], a["ve"], a["vg"], a["kc"], a["vc"], a["o"], a["B"], a["T"],
                              a["Tmax"], a["H"], a["Hkv"], a["D"], a["window"], a["base"], a["off"],
                              a["dt"], a["ws"], a["wsb"], a["stream"])
 
@@ -153,6 +155,10 @@ def _pre(**kw):
     (dict(wsb=255), 1, "workspace"),
     (dict(Tmax=1 << 22, H=8, Hkv=8, D=128, off=0), 2, "2^32"),
     (dict(B=1 << 12, Tmax=1 << 18, Hkv=4, H=4, off=0), 1, "cache rows"),
+    (dict(ve=P), 1, "both be NULL"),
+    (dict(vg=P), 1, "both be NULL"),
+    (dict(ve=P + 2, vg=P), 1, "ve is not 16-byte aligned"),
+    (dict(ve=P, vg=P + 1), 1, "ve_gate is not aligned"),
 ])
 def test_prefill_validation(kw, status, frag):
     assert _pre(**kw) == status
@@ -160,11 +166,11 @@ def test_prefill_validation(kw, status, frag):
 
 
 def _dsh(**kw):
-    a = dict(q=P, kn=P, vn=P, kp=P, vp=P, Lp=1536, kc=P, vc=P, sl=P, o=P, B=64, Tgen=512, H=6, Hkv=6,
-             D=128, window=2048, base=1e4, dt=0, ws=P, wsb=1 << 24, stream=None)
+    a = dict(q=P, kn=P, vn=P, ve=None, vg=None, kp=P, vp=P, Lp=1536, kc=P, vc=P, sl=P, o=P, B=64, Tgen=512,
+             H=6, Hkv=6, D=128, window=2048, base=1e4, dt=0, ws=P, wsb=1 << 24, stream=None)
     a.update(kw)
     L = nc.lib()
-    return L.nc_attn_decode_shared(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["Lp"], a["kc"], a["vc"],
+    return L.nc_attn_decode_shared(a["q"], a["kn"], a["vn"], a["ve"], a["vg"], a["kp"], a["vp"], a["Lp"], a["kc"], a["vc"],
                                    a["sl"], a["o"], a["B"], a["Tgen"], a["H"], a["Hkv"], a["D"],
                                    a["window"], a["base"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
@@ -181,6 +187,7 @@ def _dsh(**kw):
     (dict(ws=None), 1, "ws is NULL"),
     (dict(wsb=64), 1, "workspace"),
     (dict(Lp=1 << 30), 1, "exceeds"),
+    (dict(vg=P), 1, "both be NULL"),
 ])
 def test_decode_shared_validation(kw, status, frag):
     assert _dsh(**kw) == status

@@ -26,6 +26,17 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
+def _check_rounded(got, ref, dtype, what):
+    """A stored value against its fp64 definition: one rounding to the element
+    type, |got - ref| <= 2^-8 |ref| for bf16 (1 ulp), 1e-5 for fp32."""
+    g = got.detach().double().cpu().numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    d = np.abs(g - r)
+    bound = 1e-5 if dtype == torch.float32 else 2.0 ** -8 * np.abs(r) + 1e-6
+    print(f"[err] {what}: max {d.max():.3e}, max relative {np.max(d / np.maximum(np.abs(r), 1e-6)):.3e}", flush=True)
+    assert np.all(d <= bound), f"{what}: beyond one rounding of the element type"
+
+
 def _check(got, ref, dtype, what):
     d = np.abs(got.detach().double().cpu().numpy() - np.asarray(ref, dtype=np.float64))
     mx, mn = float(d.max()), float(d.mean())
@@ -138,3 +149,33 @@ def test_decode_shared_full_size(W):
     _say(f"decode_shared full size B64 Lp1536 Tgen512 W{W}")
     q, kn, vn, kp, vp, kc, vc, L = wl.decode_shared_inputs(seed=W)
     _run_and_check(q, kn, vn, kp, vp, kc, vc, L, W, torch.bfloat16, f"d12 shared W={W}")
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_decode_value_gate(shared):
+    """The new token's value embedding (v_new + gate * ve_new) in nc_attn_decode and
+    nc_attn_decode_shared against the oracle."""
+    _say(f"decode with value gate, shared={shared}")
+    B, Lp, Tgen, H, Hkv, D, W = 5, 200, 100, 8, 2, 128, 256
+    q, kn, vn, kp, vp, kc, vc, L = _inputs(B, Lp, Tgen, H, Hkv, D, torch.bfloat16, seed=31)
+    g = torch.Generator().manual_seed(32)
+    ve = torch.randn(B, Hkv, D, generator=g).bfloat16()
+    gate = (2 * torch.rand(B, Hkv, generator=g)).bfloat16()
+    if shared:
+        kcd, vcd = kc.to(DEV), vc.to(DEV)
+        o = nc.attn_decode_shared(q.to(DEV), kn.to(DEV), vn.to(DEV), kp.to(DEV), vp.to(DEV), kcd, vcd,
+                                  L.to(DEV), window=W, ve=ve.to(DEV), ve_gate=gate.to(DEV))
+        ro, _, rvc = oracle.attn_decode_shared(q, kn, vn, kp, vp, kc, vc, L, W, ve_new=ve, ve_gate_new=gate)
+        rows = L.long() - 1 - Lp
+    else:
+        kfull = torch.cat([kp.unsqueeze(0).expand(B, -1, -1, -1), kc], dim=1).contiguous()
+        vfull = torch.cat([vp.unsqueeze(0).expand(B, -1, -1, -1), vc], dim=1).contiguous()
+        kcd, vcd = kfull.to(DEV), vfull.to(DEV)
+        o = nc.attn_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), kcd, vcd, L.to(DEV), window=W,
+                           ve=ve.to(DEV), ve_gate=gate.to(DEV))
+        ro, _, rvc = oracle.attn_decode(q, kn, vn, kfull, vfull, L, W, ve_new=ve, ve_gate_new=gate)
+        rows = L.long() - 1
+    torch.cuda.synchronize()
+    _check(o, ro, torch.bfloat16, "o")
+    _check_rounded(vcd[torch.arange(B), rows.to(DEV)], rvc[np.arange(B), rows.numpy()], torch.bfloat16,
+                   "appended v'")

@@ -26,6 +26,17 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
+def _check_rounded(got, ref, dtype, what):
+    """A stored value against its fp64 definition: one rounding to the element
+    type, |got - ref| <= 2^-8 |ref| for bf16 (1 ulp), 1e-5 for fp32."""
+    g = got.detach().double().cpu().numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    d = np.abs(g - r)
+    bound = 1e-5 if dtype == torch.float32 else 2.0 ** -8 * np.abs(r) + 1e-6
+    print(f"[err] {what}: max {d.max():.3e}, max relative {np.max(d / np.maximum(np.abs(r), 1e-6)):.3e}", flush=True)
+    assert np.all(d <= bound), f"{what}: beyond one rounding of the element type"
+
+
 def _check(got, ref, dtype, what):
     d = np.abs(got.detach().double().cpu().numpy() - np.asarray(ref, dtype=np.float64))
     mx, mn = float(d.max()), float(d.mean())
@@ -134,3 +145,48 @@ def test_prefill_chunk_full_size(W):
     _say(f"full-size chunk B8 T512 P1536 Tmax2048 W{W}")
     q, k, v, kc, vc = wl.prefill_chunk_inputs(seed=W)
     _run_and_check(q, k, v, kc, vc, W, 1536, torch.bfloat16, f"d12 chunk W={W}")
+
+
+# ------------------------------------------------ value-embedding gate (v' = v + gate * ve)
+
+@pytest.mark.parametrize("case", [
+    (2, 130, 400, 37, 6, 6, 128, 100, torch.bfloat16),
+    (1, 300, 2000, 1600, 2, 2, 128, 2048, torch.bfloat16),  # sliced key tiles
+    (2, 100, 300, 64, 4, 2, 64, 80, torch.float32),
+], ids=lambda c: "B{}T{}Tmax{}P{}H{}Hkv{}D{}W{}-{}".format(*c[:8], str(c[8]).split(".")[-1]))
+def test_prefill_value_gate(case):
+    B, T, Tmax, P, H, Hkv, D, W, dtype = case
+    _say(f"prefill with value gate {case}")
+    g = torch.Generator().manual_seed(T + P)
+    q = torch.randn(B, T, H, D, generator=g).to(dtype)
+    k = torch.randn(B, T, Hkv, D, generator=g).to(dtype)
+    v = torch.randn(B, T, Hkv, D, generator=g).to(dtype)
+    ve = torch.randn(B, T, Hkv, D, generator=g).to(dtype)
+    gate = (2 * torch.rand(B, T, Hkv, generator=g)).to(dtype)
+    kc = torch.randn(B, Tmax, Hkv, D, generator=g).to(dtype)
+    vc = torch.randn(B, Tmax, Hkv, D, generator=g).to(dtype)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    o = nc.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), kcd, vcd, window=W, pos_offset=P,
+                        ve=ve.to(DEV), ve_gate=gate.to(DEV))
+    torch.cuda.synchronize()
+    ro, _, rvc = oracle.attn_prefill(q, k, v, kc, vc, W, 10000.0, P, ve=ve, ve_gate=gate)
+    _check(o, ro, dtype, "o")
+    _check_rounded(vcd[:, P:P + T], rvc[:, P:P + T], dtype, "cached v'")
+    keep = torch.ones(Tmax, dtype=torch.bool)
+    keep[P:P + T] = False
+    assert torch.equal(vcd.cpu()[:, keep], vc[:, keep])
+
+
+def test_prefill_zero_gate_bitwise():
+    """A zero gate reproduces the ungated call bit for bit (v + 0 * ve = v)."""
+    _say("prefill zero gate")
+    q, k, v = wl.small_prefill(2, 300, 8, 2, 128, seed=12, dtype=torch.bfloat16)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    ve = torch.randn_like(v)
+    kc1 = torch.zeros(2, 400, 2, 128, dtype=torch.bfloat16, device=DEV)
+    vc1, kc2, vc2 = torch.zeros_like(kc1), torch.zeros_like(kc1), torch.zeros_like(kc1)
+    o1 = nc.attn_prefill(q, k, v, kc1, vc1, window=200, pos_offset=64)
+    o2 = nc.attn_prefill(q, k, v, kc2, vc2, window=200, pos_offset=64, ve=ve,
+                         ve_gate=torch.zeros(2, 300, 2, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(vc1, vc2) and torch.equal(kc1, kc2)

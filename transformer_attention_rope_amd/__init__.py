@@ -48,13 +48,13 @@ _SIGS = {
     "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_core": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "nc_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
-    "nc_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _i, _i,
+    "nc_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                              _vp, _sz, _vp]),
     "nc_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "nc_attn_decode_shared_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
-    "nc_attn_decode_shared": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+    "nc_attn_decode_shared": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                    _i, _d, _i, _vp, _sz, _vp]),
-    "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
+    "nc_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i,
                             _vp, _sz, _vp]),
 }
 
@@ -151,6 +151,19 @@ def attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window) -> int:
     return int(lib().nc_attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window))
 
 
+def _ve_pair(ve, ve_gate, like, name):
+    """Checks the optional value-embedding pair against the values `like`."""
+    if (ve is None) != (ve_gate is None):
+        raise ValueError(f"{name}: ve and ve_gate must both be given or both be None")
+    if ve is None:
+        return None, None
+    ve = _gpu(ve, "ve", like.dim(), like.dtype)
+    ve_gate = _gpu(ve_gate, "ve_gate", like.dim() - 1, like.dtype)
+    if ve.shape != like.shape or tuple(ve_gate.shape) != tuple(like.shape[:-1]):
+        raise ValueError(f"{name}: ve must have the values' shape and ve_gate that shape without D")
+    return ve, ve_gate
+
+
 def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None
@@ -238,11 +251,12 @@ def attn_core(q, v, workspace, *, window: int, out=None):
 
 
 def attn_prefill(q, k, v, k_cache, v_cache, *, window: int, pos_offset: int = 0,
-                 rope_base: float = 10000.0, out=None, workspace=None):
+                 rope_base: float = 10000.0, ve=None, ve_gate=None, out=None, workspace=None):
     """Prefill of a chunk at positions pos_offset.. into the caches (in place):
-    rows pos_offset .. pos_offset+T-1 receive norm(rope(k)) and v, then the chunk's
-    queries attend to cache rows within the window. q (B,T,H,D); k, v (B,T,Hkv,D);
-    caches (B,Tmax,Hkv,D) -> o (B,T,H,D)."""
+    rows pos_offset .. pos_offset+T-1 receive norm(rope(k)) and v (v + ve_gate * ve
+    with the optional value embedding ve (B,T,Hkv,D), ve_gate (B,T,Hkv)), then the
+    chunk's queries attend to cache rows within the window. q (B,T,H,D);
+    k, v (B,T,Hkv,D); caches (B,Tmax,Hkv,D) -> o (B,T,H,D)."""
     q = _gpu(q, "q", 4)
     k = _gpu(k, "k", 4, q.dtype)
     v = _gpu(v, "v", 4, q.dtype)
@@ -258,14 +272,16 @@ def attn_prefill(q, k, v, k_cache, v_cache, *, window: int, pos_offset: int = 0,
     if o.shape != q.shape:
         raise ValueError("out must have q's shape")
     ws = _workspace(attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, q.dtype), q.device, workspace)
-    _call("nc_attn_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+    ve, ve_gate = _ve_pair(ve, ve_gate, v, "attn_prefill")
+    _call("nc_attn_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(ve_gate), _ptr(k_cache),
+          _ptr(v_cache), _ptr(o),
           B, T, Tmax, H, Hkv, D, int(window), float(rope_base), int(pos_offset), _dt(q),
           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     return o
 
 
 def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, *, window: int,
-                rope_base: float = 10000.0, out=None, workspace=None):
+                rope_base: float = 10000.0, ve=None, ve_gate=None, out=None, workspace=None):
     """One decode step: appends norm(rope(k_new)) and v_new at index seqlens-1 of the
     caches (in place), then attends. q (B,H,D); k_new, v_new (B,Hkv,D);
     caches (B,Tmax,Hkv,D); seqlens (B,) int32 on the GPU -> o (B,H,D)."""
@@ -285,14 +301,17 @@ def attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, *, window: int,
     o = torch.empty_like(q) if out is None else _gpu(out, "out", 3, q.dtype)
     need = attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window)
     ws = _workspace(need, q.device, workspace)
-    _call("nc_attn_decode", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+    ve, ve_gate = _ve_pair(ve, ve_gate, v_new, "attn_decode")
+    _call("nc_attn_decode", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ve), _ptr(ve_gate),
+          _ptr(k_cache), _ptr(v_cache),
           _ptr(seqlens), _ptr(o), B, Tmax, H, Hkv, D, int(window), float(rope_base), _dt(q),
           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     return o
 
 
 def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, seqlens, *,
-                       window: int, rope_base: float = 10000.0, out=None, workspace=None):
+                       window: int, rope_base: float = 10000.0, ve=None, ve_gate=None, out=None,
+                       workspace=None):
     """One decode step of B samples continuing one prompt: prompt positions from the
     shared (Lp,Hkv,D) caches, the samples' own positions Lp.. from their
     (B,Tgen,Hkv,D) caches, whose row L-1-Lp receives the new token (in place).
@@ -316,7 +335,9 @@ def attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, k_cache, v_cache, se
     o = torch.empty_like(q) if out is None else _gpu(out, "out", 3, q.dtype)
     need = attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window)
     ws = _workspace(need, q.device, workspace)
-    _call("nc_attn_decode_shared", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_prompt), _ptr(v_prompt),
+    ve, ve_gate = _ve_pair(ve, ve_gate, v_new, "attn_decode_shared")
+    _call("nc_attn_decode_shared", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ve), _ptr(ve_gate),
+          _ptr(k_prompt), _ptr(v_prompt),
           Lp, _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), B, Tgen, H, Hkv, D, int(window),
           float(rope_base), _dt(q), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
           _stream(q))

@@ -68,6 +68,17 @@ nc_status check_seq_bytes(int T, int Hkv, int D, nc_dtype dt) {
   return NC_OK;
 }
 
+// the value-embedding pair: both NULL (no gate) or both valid
+nc_status check_ve(const void* ve, const void* gate, nc_dtype dt) {
+  if ((ve == nullptr) != (gate == nullptr))
+    return fail(NC_ERR_INVALID, "ve and ve_gate must both be NULL or both be given");
+  if (ve == nullptr) return NC_OK;
+  if (!aligned16(ve)) return fail(NC_ERR_INVALID, "ve is not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(gate) & (dt == NC_BF16 ? 1u : 3u)) != 0)
+    return fail(NC_ERR_INVALID, "ve_gate is not aligned to its element size");
+  return NC_OK;
+}
+
 nc_status check_ptrs(const char* names[], const void* ptrs[], int n) {
   for (int i = 0; i < n; ++i) {
     if (ptrs[i] == nullptr) return fail(NC_ERR_INVALID, "%s is NULL", names[i]);
@@ -170,8 +181,8 @@ nc_status nc_attn_prep(const void* k, int B, int T, int Hkv, int D, double rope_
   if ((s = check_ws(ws, ws_bytes, prep_table_bytes(T, D, dt) + prep_k_bytes(B, T, Hkv, D, dt))) != NC_OK)
     return s;
   hipError_t e = nc::launch_attn_prep(k, (char*)ws + prep_table_bytes(T, D, dt), ws, B, T, Hkv, D,
-                                      rope_base, pos_offset, nullptr, nullptr, T, 0, to_dt(dt),
-                                      (hipStream_t)stream);
+                                      rope_base, pos_offset, nullptr, nullptr, T, 0, nullptr, nullptr,
+                                      to_dt(dt), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
   return ok();
 }
@@ -222,10 +233,10 @@ size_t nc_attn_prefill_workspace_bytes(int B, int T, int Tmax, int H, int Hkv, i
   return prep_table_bytes(T, D, dtype) + round_up(part_bytes(B, T, H, Hkv, D, Tmax, dtype));
 }
 
-nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_cache,
-                          void* v_cache, void* o, int B, int T, int Tmax, int H, int Hkv, int D,
-                          int window, double rope_base, int pos_offset, nc_dtype dt, void* ws,
-                          size_t ws_bytes, void* stream) {
+nc_status nc_attn_prefill(const void* q, const void* k, const void* v, const void* ve,
+                          const void* ve_gate, void* k_cache, void* v_cache, void* o, int B, int T,
+                          int Tmax, int H, int Hkv, int D, int window, double rope_base,
+                          int pos_offset, nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
   if (s != NC_OK) return s;
   if (Tmax < 1) return fail(NC_ERR_INVALID, "Tmax must be >= 1 (got %d)", Tmax);
@@ -241,8 +252,10 @@ nc_status nc_attn_prefill(const void* q, const void* k, const void* v, void* k_c
   if ((s = check_ptrs(names, ptrs, 6)) != NC_OK) return s;
   if ((s = check_ws(ws, ws_bytes, nc_attn_prefill_workspace_bytes(B, T, Tmax, H, Hkv, D, dt))) != NC_OK)
     return s;
+  if ((s = check_ve(ve, ve_gate, dt)) != NC_OK) return s;
   hipError_t e = nc::launch_attn_prep(k, k_cache, ws, B, T, Hkv, D, rope_base, pos_offset, v,
-                                      v_cache, Tmax, pos_offset, to_dt(dt), (hipStream_t)stream);
+                                      v_cache, Tmax, pos_offset, ve, ve_gate, to_dt(dt),
+                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_prep launch");
   e = nc::launch_attn_core(q, k_cache, v_cache, o, B, T, H, Hkv, D, window, ws, Tmax, pos_offset,
                            (char*)ws + prep_table_bytes(T, D, dt),
@@ -258,10 +271,10 @@ size_t nc_attn_decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, in
   return n ? round_up(n) : 0;
 }
 
-nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                         void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax, int H,
-                         int Hkv, int D, int window, double rope_base, nc_dtype dt, void* ws,
-                         size_t ws_bytes, void* stream) {
+nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, const void* ve_new,
+                         const void* ve_gate, void* k_cache, void* v_cache, const int32_t* seqlens,
+                         void* o, int B, int Tmax, int H, int Hkv, int D, int window,
+                         double rope_base, nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   nc_status s = check_common(B, Tmax, H, Hkv, D, dt, "Tmax");
   if (s != NC_OK) return s;
   if (H / Hkv > 64) return fail(NC_ERR_UNSUPPORTED, "H/Hkv=%d query heads per K/V head exceed 64", H / Hkv);
@@ -273,6 +286,7 @@ nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, vo
   if (seqlens == nullptr) return fail(NC_ERR_INVALID, "seqlens is NULL");
   if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
     return fail(NC_ERR_INVALID, "seqlens is not 4-byte aligned");
+  if ((s = check_ve(ve_new, ve_gate, dt)) != NC_OK) return s;
   const size_t need = nc_attn_decode_workspace_bytes(B, Tmax, H, Hkv, D, window);
   if (need > 0) {
     if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL but %zu bytes are required", need);
@@ -283,7 +297,7 @@ nc_status nc_attn_decode(const void* q, const void* k_new, const void* v_new, vo
   hipError_t e = nc::launch_attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, o, B, Tmax, H,
                                         Hkv, D, window, rope_base,
                                         dt == NC_BF16 ? nc::kBF16 : nc::kF32, ws,
-                                        (hipStream_t)stream);
+                                        (hipStream_t)stream, ve_new, ve_gate);
   if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
   return ok();
 }
@@ -299,6 +313,7 @@ size_t nc_attn_decode_shared_workspace_bytes(int B, int Lp, int Tgen, int H, int
 }
 
 nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                const void* ve_new, const void* ve_gate,
                                 const void* k_prompt, const void* v_prompt, int Lp, void* k_cache,
                                 void* v_cache, const int32_t* seqlens, void* o, int B, int Tgen,
                                 int H, int Hkv, int D, int window, double rope_base, nc_dtype dt,
@@ -317,6 +332,7 @@ nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_
   if (seqlens == nullptr) return fail(NC_ERR_INVALID, "seqlens is NULL");
   if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
     return fail(NC_ERR_INVALID, "seqlens is not 4-byte aligned");
+  if ((s = check_ve(ve_new, ve_gate, dt)) != NC_OK) return s;
   const size_t need = nc_attn_decode_shared_workspace_bytes(B, Lp, Tgen, H, Hkv, D, window);
   if (need > 0) {
     if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL but %zu bytes are required", need);
@@ -326,7 +342,8 @@ nc_status nc_attn_decode_shared(const void* q, const void* k_new, const void* v_
   }
   hipError_t e = nc::launch_attn_decode_shared(q, k_new, v_new, k_prompt, v_prompt, Lp, k_cache,
                                                v_cache, seqlens, o, B, Tgen, H, Hkv, D, window,
-                                               rope_base, to_dt(dt), ws, (hipStream_t)stream);
+                                               rope_base, to_dt(dt), ws, (hipStream_t)stream,
+                                               ve_new, ve_gate);
   if (e != hipSuccess) return hip_fail(e, "attn_decode_shared launch");
   return ok();
 }

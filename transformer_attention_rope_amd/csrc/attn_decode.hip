@@ -43,6 +43,8 @@ struct DecArgs {
   void* v_cache;
   const void* k_prompt;  // (Lp, Hkv, D): positions 0 .. Lp-1, shared by all sequences
   const void* v_prompt;
+  const void* ve_new;    // (B, Hkv, D) value embedding of the new token, or null
+  const void* ve_gate;   // (B, Hkv): the appended value is v_new + ve_gate * ve_new
   const int32_t* seqlens;
   void* o;
   float* part;  // [B][H][nsplit][D + 2]: unnormalised o (D), max, sum
@@ -287,6 +289,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
         const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
         vn0 = vsrc[2 * lane];
         vn1 = vsrc[2 * lane + 1];
+        if (a.ve_new != nullptr) {  // value embedding: v_new + gate * ve_new, rounded once
+          const Elem* esrc = (const Elem*)a.ve_new + ((size_t)b * a.Hkv + g) * D;
+          const float gg = TR::to_f(((const Elem*)a.ve_gate)[(size_t)b * a.Hkv + g]);
+          vn0 = TR::from_f(TR::to_f(vn0) + gg * TR::to_f(esrc[2 * lane]));
+          vn1 = TR::from_f(TR::to_f(vn1) + gg * TR::to_f(esrc[2 * lane + 1]));
+        }
       }
     }
   }
@@ -716,8 +724,11 @@ hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const voi
                                      const void* k_prompt, const void* v_prompt, int Lp,
                                      void* k_cache, void* v_cache, const int32_t* seqlens, void* o,
                                      int B, int Tgen, int H, int Hkv, int D, int window,
-                                     double rope_base, Dtype dt, void* ws, hipStream_t stream) {
+                                     double rope_base, Dtype dt, void* ws, hipStream_t stream,
+                                     const void* ve_new, const void* ve_gate) {
   DecArgs a{};
+  a.ve_new = ve_new;
+  a.ve_gate = ve_gate;
   const int Tmax = Lp + Tgen;
   a.q = q;
   a.k_new = k_new;
@@ -757,9 +768,11 @@ hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const voi
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
                               void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
                               int H, int Hkv, int D, int window, double rope_base, Dtype dt,
-                              void* ws, hipStream_t stream) {
+                              void* ws, hipStream_t stream, const void* ve_new,
+                              const void* ve_gate) {
   return launch_attn_decode_shared(q, k_new, v_new, nullptr, nullptr, 0, k_cache, v_cache, seqlens,
-                                   o, B, Tmax, H, Hkv, D, window, rope_base, dt, ws, stream);
+                                   o, B, Tmax, H, Hkv, D, window, rope_base, dt, ws, stream, ve_new,
+                                   ve_gate);
 }
 
 }  // namespace nc

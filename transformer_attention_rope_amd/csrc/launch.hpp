@@ -13,12 +13,14 @@ enum Dtype { kBF16 = 0, kF32 = 1 };
 // ---- prefill input stage: k' = RMSNorm(RoPE(k)) in k's layout and type, and
 // ---- the (cos, sin) table [T][D/2] of positions pos_offset + t for q. With
 // ---- vc non-null, kp and vc are (B, Tk, Hkv, D) caches: k' and a copy of v
-// ---- go to their rows row0 .. row0 + T - 1.
+// ---- go to their rows row0 .. row0 + T - 1; with ve non-null the copy is
+// ---- v + vgate * ve (vgate (B, T, Hkv), one value per row).
 size_t attn_prep_table_bytes(int T, int D, Dtype dt);
 size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt);
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
                             double rope_base, int pos_offset, const void* v, void* vc, int Tk,
-                            int row0, Dtype dt, hipStream_t stream);
+                            int row0, const void* ve, const void* vgate, Dtype dt,
+                            hipStream_t stream);
 
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
                               int T, int H, int Hkv, int D, double rope_base, int pos_offset,
@@ -34,16 +36,20 @@ hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* 
                             void* part, size_t part_bytes, Dtype dt, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window, int Lp);
+// ve_new (B, Hkv, D) and ve_gate (B, Hkv), or both null: v_new + ve_gate * ve_new
+// is appended and used in place of v_new
 hipError_t launch_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache,
                               void* v_cache, const int32_t* seqlens, void* o, int B, int Tmax,
                               int H, int Hkv, int D, int window, double rope_base, Dtype dt,
-                              void* ws, hipStream_t stream);
+                              void* ws, hipStream_t stream, const void* ve_new = nullptr,
+                              const void* ve_gate = nullptr);
 // decode over a shared (Lp, Hkv, D) prompt cache and per-sequence caches of
 // Tgen rows holding positions Lp ..
 hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
                                      const void* k_prompt, const void* v_prompt, int Lp,
                                      void* k_cache, void* v_cache, const int32_t* seqlens, void* o,
                                      int B, int Tgen, int H, int Hkv, int D, int window,
-                                     double rope_base, Dtype dt, void* ws, hipStream_t stream);
+                                     double rope_base, Dtype dt, void* ws, hipStream_t stream,
+                                     const void* ve_new = nullptr, const void* ve_gate = nullptr);
 
 }  // namespace nc

@@ -36,7 +36,10 @@ namespace nc {
 // With CACHE the k' rows go to rows row0 + t of a (B, Tk, Hkv, D) cache
 // instead, and the v rows of the same (sequence, position, head) are copied
 // to the same rows of the value cache, so the chunk's keys and values are in
-// the cache before the attention kernel reads them there.
+// the cache before the attention kernel reads them there. With ve non-null
+// the value rows written are v' = v + gate * ve (value embedding; one gate
+// per row, i.e. per (sequence, position, head)), formed in fp32 and rounded
+// once to the element type.
 constexpr int PREP_CPT = 4;  // 16-byte chunks per thread
 
 template <int D, typename Elem, int CPT = PREP_CPT>
@@ -52,7 +55,9 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
                                                          int Hkv, int rows, double log2_base,
                                                          int pos_offset, int nrb,
                                                          const Elem* __restrict__ v,
-                                                         Elem* __restrict__ vc, int Tk, int row0) {
+                                                         Elem* __restrict__ vc, int Tk, int row0,
+                                                         const Elem* __restrict__ ve,
+                                                         const Elem* __restrict__ vgate) {
   constexpr bool kBf = sizeof(Elem) == 2;
   constexpr int EPC = kBf ? 8 : 4;  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;      // chunks per row
@@ -67,6 +72,8 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
 
   u32x4_t w[PREP_CPT];
   u32x4_t wv[CACHE ? PREP_CPT : 1];
+  u32x4_t wve[CACHE ? PREP_CPT : 1];
+  float gt[CACHE ? PREP_CPT : 1];
   size_t off[PREP_CPT];   // element offset of the chunk in k (and v)
   size_t doff[PREP_CPT];  // and in the destination of k'
 #pragma unroll
@@ -79,7 +86,15 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     doff[p] = CACHE ? (((size_t)bb * Tk + row0 + t) * Hkv + g) * D + (size_t)cc * EPC : off[p];
     if (ci < total) {
       w[p] = ld16_nt(k + off[p]);
-      if constexpr (CACHE) wv[p] = ld16_nt(v + off[p]);
+      if constexpr (CACHE) {
+        wv[p] = ld16_nt(v + off[p]);
+        if (ve != nullptr) {
+          wve[p] = ld16_nt(ve + off[p]);
+          const Elem gr = vgate[((size_t)bb * T + t) * Hkv + g];
+          if constexpr (kBf) gt[p] = __uint_as_float((uint32_t)gr << 16);
+          else gt[p] = gr;
+        }
+      }
     }
   }
 
@@ -141,7 +156,20 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
         for (int m = 0; m < 4; ++m) o[m] = __float_as_uint(x[m] * inv);
       }
       st16_nt(kp + doff[p], o);
-      if constexpr (CACHE) st16_nt(vc + doff[p], wv[p]);
+      if constexpr (CACHE) {
+        u32x4_t vo = wv[p];
+        if (ve != nullptr) {
+          const float gg = gt[p];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            if constexpr (kBf)
+              vo[m] = pack_bf2(bf_lo(wv[p][m]) + gg * bf_lo(wve[p][m]), bf_hi(wv[p][m]) + gg * bf_hi(wve[p][m]));
+            else
+              vo[m] = __float_as_uint(__uint_as_float(wv[p][m]) + gg * __uint_as_float(wve[p][m]));
+          }
+        }
+        st16_nt(vc + doff[p], vo);
+      }
     }
   }
 }
@@ -156,7 +184,8 @@ size_t attn_prep_k_bytes(int B, int T, int Hkv, int D, Dtype dt) {
 template <int D, typename Elem>
 static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
                                    double rope_base, int pos_offset, const void* v, void* vc,
-                                   int Tk, int row0, hipStream_t stream) {
+                                   int Tk, int row0, const void* ve, const void* vgate,
+                                   hipStream_t stream) {
   constexpr int RB = prep_rows_per_block<D, Elem>();
   const long long rows = (long long)B * Hkv;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -166,33 +195,36 @@ static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, i
   if (vc != nullptr)
     hipLaunchKernelGGL((attn_prep_kernel<D, Elem, true>), dim3((unsigned)nblk), dim3(256), 0,
                        stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
-                       std::log2(rope_base), pos_offset, nrb, (const Elem*)v, (Elem*)vc, Tk, row0);
+                       std::log2(rope_base), pos_offset, nrb, (const Elem*)v, (Elem*)vc, Tk, row0,
+                       (const Elem*)ve, (const Elem*)vgate);
   else
     hipLaunchKernelGGL((attn_prep_kernel<D, Elem, false>), dim3((unsigned)nblk), dim3(256), 0,
                        stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
                        std::log2(rope_base), pos_offset, nrb, (const Elem*)nullptr,
-                       (Elem*)nullptr, T, 0);
+                       (Elem*)nullptr, T, 0, (const Elem*)nullptr, (const Elem*)nullptr);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t attn_prep_d(const void* k, void* kp, void* tabq, int B, int T, int Hkv,
                               double rope_base, int pos_offset, const void* v, void* vc, int Tk,
-                              int row0, Dtype dt, hipStream_t stream) {
+                              int row0, const void* ve, const void* vgate, Dtype dt,
+                              hipStream_t stream) {
   if (dt == kBF16)
     return attn_prep_launch<D, uint16_t>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk,
-                                         row0, stream);
+                                         row0, ve, vgate, stream);
   return attn_prep_launch<D, float>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0,
-                                    stream);
+                                    ve, vgate, stream);
 }
 
 hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, int Hkv, int D,
                             double rope_base, int pos_offset, const void* v, void* vc, int Tk,
-                            int row0, Dtype dt, hipStream_t stream) {
+                            int row0, const void* ve, const void* vgate, Dtype dt,
+                            hipStream_t stream) {
   switch (D) {
-    case 32: return attn_prep_d<32>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
-    case 64: return attn_prep_d<64>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
-    case 128: return attn_prep_d<128>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, dt, stream);
+    case 32: return attn_prep_d<32>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, ve, vgate, dt, stream);
+    case 64: return attn_prep_d<64>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, ve, vgate, dt, stream);
+    case 128: return attn_prep_d<128>(k, kp, tabq, B, T, Hkv, rope_base, pos_offset, v, vc, Tk, row0, ve, vgate, dt, stream);
     default: return hipErrorInvalidValue;
   }
 }
