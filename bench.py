@@ -158,7 +158,8 @@ def main():
                     help="untimed back-to-back GPU work before each timed part (clock ramp)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "shared", "copy"],
+                    choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "shared", "gate",
+                             "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -450,6 +451,49 @@ def main():
             print(json.dumps(shd))
             return
 
+    # ------------------------------- value-embedding gate (v' = v + gate * ve)
+    gate = {}
+    if args.only in ("all", "gate"):
+        ch = wl.CHUNK
+        B, Tc, P, Tmax, H, Hkv, D = ch["B"], ch["T"], ch["P"], ch["Tmax"], ch["H"], ch["Hkv"], ch["D"]
+        gsets = []
+        for s_ in range(args.sets):
+            q, k, v, kc, vc = [t.to(dev) for t in wl.prefill_chunk_inputs(seed=s_)]
+            gsets.append((q, k, v, kc, vc, torch.randn_like(v), torch.rand(B, Tc, Hkv, device=dev).to(v.dtype),
+                          torch.empty_like(q)))
+        wsg = torch.empty(max(nc.attn_prefill_workspace_bytes(B, Tc, Tmax, H, Hkv, D), 1), dtype=torch.uint8,
+                          device=dev)
+        for with_gate in (False, True):
+            def gstep(i, with_gate=with_gate):
+                q, k, v, kc, vc, ve, g, o = gsets[i % len(gsets)]
+                nc.attn_prefill(q, k, v, kc, vc, window=2048, pos_offset=P, out=o, workspace=wsg,
+                                ve=ve if with_gate else None, ve_gate=g if with_gate else None)
+
+            prime(f"gate_prefill_{with_gate}", gstep)
+            gate[f"prefill_chunk_W2048_{'gated' if with_gate else 'plain'}_us"] = round(event_time_ms(gstep, K, torch) * 1e3, 2)
+        del gsets, wsg
+        dcfg = wl.CONFIGS[4]
+        dsets = []
+        for s_ in range(args.sets):
+            q, kn, vn, kc, vc, L = [t.to(dev) for t in wl.decode_inputs(dcfg, set_idx=s_)]
+            dsets.append((q, kn, vn, kc, vc, L, torch.randn_like(vn), torch.rand(dcfg.B, dcfg.Hkv, device=dev).to(vn.dtype),
+                          torch.empty_like(q)))
+        wsd = nc.decode_workspace(dcfg.B, dcfg.Tmax, dcfg.H, dcfg.Hkv, dcfg.D, 512, device=dev)
+        for with_gate in (False, True):
+            def dstep_(i, with_gate=with_gate):
+                q, kn, vn, kc, vc, L, ve, g, o = dsets[i % len(dsets)]
+                nc.attn_decode(q, kn, vn, kc, vc, L, window=512, out=o, workspace=wsd,
+                               ve=ve if with_gate else None, ve_gate=g if with_gate else None)
+
+            prime(f"gate_decode_{with_gate}", dstep_)
+            gate[f"decode_W512_{'gated' if with_gate else 'plain'}_us"] = round(event_time_ms(dstep_, K, torch) * 1e3, 2)
+        gate["workload"] = ("nc_attn_prefill on the d12 chunk (512 tokens at offset 1536, W=2048) and nc_attn_decode "
+                            "on the B=64 d12 decode (W=512), each with and without the value-embedding pair")
+        del dsets, wsd
+        if args.only == "gate":
+            print(json.dumps(gate))
+            return
+
     # ---------------------------------------------------------------- line
     step_ms = out["step_ms"]
     value = flops / (step_ms * 1e-3) / 1e12
@@ -486,6 +530,7 @@ def main():
         "stacks": stacks,
         "prefill_cache": pre,
         "decode_shared_prompt": shd,
+        "value_gate": gate,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
