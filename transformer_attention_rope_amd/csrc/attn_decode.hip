@@ -52,6 +52,8 @@ struct DecArgs {
   int Lp;       // shared prompt rows (0: none; every position in the sequence's cache)
   int Tgen;     // rows per sequence cache
   int nwg;      // workgroups with an item (the shared-prompt launch pads the grid to a multiple of 8)
+  int cut;      // shared prompt: 1 cuts every range at the prompt's end; 0 lets a chunk span
+                // both caches (run as two segments in one workgroup)
   int C;        // keys per chunk (multiple of the keys per workgroup step)
   int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
   int ngh;      // head groups per K/V head = ceil(G / GP)
@@ -219,10 +221,15 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
   int ks0, ks1;
-  const int nch = dec_chunks(L, lo, Lp, a.C, split, ks0, ks1);
+  const int nch = dec_chunks(L, lo, SH && a.cut ? Lp : 0, a.C, split, ks0, ks1);
   if (split >= nch) return;
   const bool owns_new = ks1 == L;
-  const bool in_prompt = SH && ks0 < Lp;  // this chunk's rows are the shared prompt's
+  // The chunk's keys as one or two segments [sk0, sk1): with a shared prompt
+  // and no cut, a chunk spanning the prompt's end runs its prompt rows first,
+  // then (second segment) the sequence's own rows, with one softmax state.
+  const bool two_seg = SH && ks0 < Lp && ks1 > Lp;
+  int sk0 = ks0, sk1 = two_seg ? Lp : ks1;
+  bool in_prompt = SH && ks0 < Lp;  // the segment's rows are the shared prompt's
 
   const int h0 = g * a.G + hg * GP;
   const int nh = min(GP, a.G - hg * GP);
@@ -239,15 +246,17 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int cc = lane % CPR;        // 16-byte piece within the row
   const int kl = lane / CPR;        // key slot within the wave
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * sizeof(Elem);
-  const size_t base_el = in_prompt ? ((size_t)ks0 * a.Hkv + g) * D
-                                   : (((size_t)b * Tgen + (ks0 - Lp)) * a.Hkv + g) * D;
-  const uint32_t nrec = (uint32_t)(ks1 - ks0) * row_bytes;  // the chunk's keys only
-  const Elem* const ksrc = in_prompt ? (const Elem*)a.k_prompt : kc;
-  const Elem* const vsrc_c = in_prompt ? (const Elem*)a.v_prompt : vc;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(ksrc + base_el, nrec);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc_c + base_el, nrec);
+  auto seg_rsrc = [&](const void* kbase, const void* vbase, __amdgpu_buffer_rsrc_t& rk_,
+                      __amdgpu_buffer_rsrc_t& rv_) __attribute__((always_inline)) {
+    const size_t base_el = in_prompt ? ((size_t)sk0 * a.Hkv + g) * D
+                                     : (((size_t)b * Tgen + (sk0 - Lp)) * a.Hkv + g) * D;
+    const uint32_t nrec = (uint32_t)(sk1 - sk0) * row_bytes;  // the segment's keys only
+    rk_ = make_rsrc((const Elem*)kbase + base_el, nrec);
+    rv_ = make_rsrc((const Elem*)vbase + base_el, nrec);
+  };
+  __amdgpu_buffer_rsrc_t rk, rv;
+  seg_rsrc(in_prompt ? a.k_prompt : (const void*)kc, in_prompt ? a.v_prompt : (const void*)vc, rk, rv);
   const int slot = wave * KPW + kl;   // key slot within a workgroup step
-  const int nkeys = ks1 - ks0;
   u32x4_t kw[NBUF][U], vw[NBUF][U];
   // the sequence's own rows are read once (non-temporal); the shared prompt's
   // rows are read by every sequence and stay cached
@@ -371,8 +380,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = ks0 + it * KPI + u * 4 * KPW + slot;
-      live[u] = key < ks1;
+      const int key = sk0 + it * KPI + u * 4 * KPW + slot;
+      live[u] = key < sk1;
       if (key == pos) {  // the appended row, from LDS (its cache row may not be written yet)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
@@ -433,21 +442,21 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
       for (int mm = 0; mm < 4; ++mm) qv2[i][mm] = pack_bf2(qv[i][2 * mm], qv[i][2 * mm + 1]);
   }
   // the iteration that holds key pos (only in the chunk that owns it)
-  const int it_pos = owns_new ? (pos - ks0) / KPI : -1;
+  int it_pos = owns_new && pos < sk1 ? (pos - sk0) / KPI : -1;
   auto consume_packed = [&](int it, int set, auto) __attribute__((always_inline)) {  // generic: only built for bf16
     static_assert(U % 2 == 0, "keys are paired");
     u32x4_t kq[U], vq[U];
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      live[u] = ks0 + it * KPI + u * 4 * KPW + slot < ks1;
+      live[u] = sk0 + it * KPI + u * 4 * KPW + slot < sk1;
       kq[u] = kw[set][u];
       vq[u] = vw[set][u];
     }
     if (it == it_pos) {  // the appended row, from LDS (its cache row may not be written yet)
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (ks0 + it * KPI + u * 4 * KPW + slot == pos) {
+        if (sk0 + it * KPI + u * 4 * KPW + slot == pos) {
 #pragma unroll
           for (int mm = 0; mm < 4; ++mm) {
             kq[u][mm] = pack_bf2(knew_s[cc * 8 + 2 * mm], knew_s[cc * 8 + 2 * mm + 1]);
@@ -499,7 +508,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     if constexpr (kPacked) consume_packed(it, set, 0); else consume(it, set);
   };
 
-  const int niter = (nkeys + KPI - 1) / KPI;
+  auto run_segment = [&]() __attribute__((always_inline)) {
+  const int niter = (sk1 - sk0 + KPI - 1) / KPI;
   if constexpr (NBUF == 2) {
     for (int it = 0; it < niter; it += 2) {
       if (it + 1 < niter) issue(it + 1, 1);
@@ -518,6 +528,20 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
       if (it + 2 >= niter) break;
       if (it + 4 < niter) issue(it + 4, 1);
       step(it + 2, 2);
+    }
+  }
+  };
+  run_segment();
+  if constexpr (SH) {
+    if (two_seg) {  // the sequence's own rows: a fresh pipeline on their cache
+      sk0 = Lp;
+      sk1 = ks1;
+      in_prompt = false;
+      seg_rsrc(kc, vc, rk, rv);
+      it_pos = owns_new ? (pos - sk0) / KPI : -1;
+      issue(0, 0);
+      if constexpr (NBUF == 3) issue(1, 1);
+      run_segment();
     }
   }
 
@@ -591,7 +615,7 @@ __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
   const int L = clamp_len(a.seqlens[b], a.Lp, a.Tmax);
   const int lo = L > a.W ? L - a.W : 0;
   int ks0, ks1;
-  const int nch = dec_chunks(L, lo, a.Lp, a.C, 0, ks0, ks1);
+  const int nch = dec_chunks(L, lo, a.cut ? a.Lp : 0, a.C, 0, ks0, ks1);
   if (nch <= 1) return;
   constexpr int PER = (D + 63) / 64;
   constexpr int NB = 8;  // chunk states loaded per batch
@@ -748,14 +772,20 @@ hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const voi
   a.G = H / Hkv;
   a.W = window;
   a.C = decode_chunk(B, Tmax, H, Hkv, D, window);
-  a.nsplit = decode_nsplit(Tmax, window, a.C) + (Lp > 0 ? 1 : 0);
+  // Cut at the prompt's end where a sequence can see 1024 or more prompt rows:
+  // the prompt part then runs in parallel with the own part (measured, 64
+  // samples of a 1536-token prompt at W = 2048: 37.9 us cut). Shorter prompt
+  // parts run as the first segment of the same workgroup, with no merge pass.
+  a.cut = (Lp > 0 && std::min(window, Lp) >= 1024) ? 1 : 0;
+  a.nsplit = decode_nsplit(Tmax, window, a.C) + (a.cut ? 1 : 0);
   a.log2_base = std::log2(rope_base);
   a.part = (float*)ws;
   a.ncu = device_cu_count();
   // Ranking costs each workgroup one more dependent round trip; it pays where
   // visible lengths can differ by more than a few hundred keys.
   const int span = window < Tmax ? window : Tmax;
-  a.order = (a.nsplit == 1 && B <= kDecRankMaxB && a.ncu > 0 && span >= 1024) ? 1 : 0;
+  // (not with a shared prompt, whose workgroups take their items head-major per XCD)
+  a.order = (Lp == 0 && a.nsplit == 1 && B <= kDecRankMaxB && a.ncu > 0 && span >= 1024) ? 1 : 0;
   const bool bf = dt == kBF16;
   switch (D) {
     case 32: return bf ? decode_d<32, uint16_t>(a, stream) : decode_d<32, float>(a, stream);
