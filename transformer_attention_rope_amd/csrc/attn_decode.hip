@@ -27,6 +27,21 @@
 // which a per-workgroup device-scope release would pay for many times). The
 // chunk holding key L-1 writes the appended row and uses it from LDS, so no
 // workgroup waits on another's write.
+//
+// Shared prompt (SH, nc_attn_decode_shared; the same page, §10.6: the prompt
+// is prefilled once and several samples generate from its cache): positions
+// 0 .. Lp-1 are read from one (Lp, Hkv, D) cache shared by all sequences,
+// position p >= Lp from row p - Lp of the sequence's own cache. A chunk lies
+// wholly in one of the two caches when the range is cut at Lp (long prompt
+// parts, which then run in parallel with the own part), or runs as two
+// segments in one workgroup (prompt rows first, one softmax state). Prompt
+// rows are loaded with the temporal hint and the workgroups are ordered
+// head-major per XCD, so each XCD's L2 serves the prompt rows of a few heads
+// to every sequence. Without SH the kernel is the one described above.
+//
+// Value embedding ("Nanochat与nanoGPT对比：关键升级" §1 notes, value residual):
+// with ve_new given, the appended value is v_new + ve_gate * ve_new, formed in
+// fp32 and rounded once.
 #include "device_common.hpp"
 #include "launch.hpp"
 

@@ -7,8 +7,11 @@
 // "Nanochat与nanoGPT对比：关键升级" (lzwjava.github.io) §1 table and notes:
 // QK-norm after RoPE, GQA, sliding window):
 //   o[b,t,h] = sum_j P[t,j] v[b,j,g],  g = h / (H/Hkv),
-//   P[t,:]   = softmax_j( q'[t].k'[j] / sqrt(D) ) over 0 <= t - j < W,
+//   P[t,:]   = softmax_j( q'[t].k'[j] / sqrt(D) ) over 0 <= kofs + t - j < W,
 //   q', k'   = RMSNorm(RoPE(q)), RMSNorm(RoPE(k)) at positions pos_offset + t.
+// kofs = 0 for the forward of a whole sequence; for a chunk prefilled into a
+// cache (same page, §10.4) the queries are the chunk's, at key rows kofs ..,
+// and the keys are the cache's rows 0 .. kofs + T - 1 (Tk rows per sequence).
 //
 // Design (bf16 path):
 //  * k' is formed once per key row by the input stage: every key tile is
@@ -48,6 +51,12 @@
 //    MFMAs execute, so this work hides under the matrix pipe. Tiles crossing
 //    a wave's band edge are masked in place; tiles outside it are skipped
 //    (the wave only stages). Heaviest query tiles are dispatched first.
+//  * At D = 128 a band of at most half the sequence runs a 2-wave form (128
+//    columns, two workgroups per compute unit), whose tiles are half as long.
+//  * A launch too small to fill the device (a chunk at a large offset, a batch
+//    of one) cuts each query tile's key tiles into slices run by separate
+//    workgroups; each writes unnormalised fp32 rows and row sums, which the
+//    fixed exponent scale above lets a second kernel add directly.
 //
 // fp32 path: exact fp32 arithmetic on the vector ALUs (one thread per query
 // column), same band, same softmax without a running maximum.
