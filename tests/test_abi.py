@@ -223,9 +223,10 @@ def test_workspace_queries():
     # one workgroup per (sequence, head) already fills the device: no split
     assert L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048) == 0
     assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0
-    # a shared prompt cuts each sequence's keys at the prompt's end: one more
-    # chunk state per (b, h), so room for two even when the range is not split
+    # a shared prompt may be cut at its end: one more chunk state per (b, h)
+    # than the unsplit range, so room for two
     assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 2048) == 64 * 6 * 2 * 130 * 4
+    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 1600) == 64 * 6 * 2 * 130 * 4
     assert L.nc_attn_decode_shared_workspace_bytes(64, 0, 512, 6, 6, 128, 2048) == 0
 
 

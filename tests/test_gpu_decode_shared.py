@@ -87,6 +87,14 @@ SHARED_SMALL = [
     (70, 600, 90, 6, 6, 128, 2048, torch.bfloat16),  # enough samples that ranges are not split by size
     (3, 90, 40, 4, 2, 64, 60, torch.float32),
     (2, 33, 17, 2, 2, 32, 2048, torch.float32),
+    # prompts of which a sequence sees 1024 rows or more: each range is cut at
+    # the prompt's end (G = 1, 4, 8; a window shorter than the longest
+    # sequence; fp32)
+    (10, 1100, 60, 4, 4, 64, 4096, torch.bfloat16),
+    (5, 1030, 30, 8, 2, 128, 2048, torch.bfloat16),
+    (3, 1024, 20, 16, 2, 32, 1100, torch.bfloat16),
+    (4, 1200, 100, 4, 2, 64, 1100, torch.bfloat16),
+    (3, 1050, 20, 2, 2, 32, 4096, torch.float32),
 ]
 
 
