@@ -11,6 +11,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace nc {
@@ -40,7 +41,12 @@ namespace nc {
 // the value rows written are v' = v + gate * ve (value embedding; one gate
 // per row, i.e. per (sequence, position, head)), formed in fp32 and rounded
 // once to the element type.
-constexpr int PREP_CPT = 4;  // 16-byte chunks per thread
+// Where a position's rows fill at most half a workgroup (the d12 layer: 48 k
+// rows of 16 chunks against 96 per workgroup), one workgroup takes pp
+// consecutive positions whole, so the angle computation and the barrier are
+// paid once per pp positions.
+constexpr int PREP_CPT = 6;  // 16-byte chunks per thread
+constexpr int PREP_MAXPP = 8;  // positions per workgroup at most
 
 template <int D, typename Elem, int CPT = PREP_CPT>
 constexpr int prep_rows_per_block() {
@@ -53,7 +59,7 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
                                                          Elem* __restrict__ kp,
                                                          void* __restrict__ tabq, int T,
                                                          int Hkv, int rows, double log2_base,
-                                                         int pos_offset, int nrb,
+                                                         int pos_offset, int nrb, int pp,
                                                          const Elem* __restrict__ v,
                                                          Elem* __restrict__ vc, int Tk, int row0,
                                                          const Elem* __restrict__ ve,
@@ -63,11 +69,13 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
   constexpr int CPR = D / EPC;      // chunks per row
   constexpr int RB = prep_rows_per_block<D, Elem>();
   static_assert(64 % CPR == 0, "a row's chunks stay inside one wave");
-  __shared__ float2 cs[D / 2];
+  __shared__ float2 cs[PREP_MAXPP][D / 2];
 
-  const int t = (int)blockIdx.x / nrb;
-  const int r0 = ((int)blockIdx.x - t * nrb) * RB;
-  const int total = min(RB, rows - r0) * CPR;  // whole rows only
+  // positions t0 .. t0+npos-1 whole (pp > 1), or rows r0 .. r0+RB-1 of position t0
+  const int t0 = pp > 1 ? (int)blockIdx.x * pp : (int)blockIdx.x / nrb;
+  const int r0 = pp > 1 ? 0 : ((int)blockIdx.x - t0 * nrb) * RB;
+  const int npos = pp > 1 ? min(pp, T - t0) : 1;
+  const int total = (pp > 1 ? npos * rows : min(RB, rows - r0)) * CPR;  // whole rows only
   const int tid = threadIdx.x;
 
   u32x4_t w[PREP_CPT];
@@ -76,10 +84,15 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
   float gt[CACHE ? PREP_CPT : 1];
   size_t off[PREP_CPT];   // element offset of the chunk in k (and v)
   size_t doff[PREP_CPT];  // and in the destination of k'
+  int tls[PREP_CPT];      // the chunk's position, t0 + tls
 #pragma unroll
   for (int p = 0; p < PREP_CPT; ++p) {
     const int ci = p * 256 + tid;
-    const int row = r0 + ci / CPR;
+    const int lr = ci / CPR;  // row within the workgroup
+    const int tl = pp > 1 ? lr / rows : 0;
+    const int row = pp > 1 ? lr - tl * rows : r0 + lr;
+    const int t = t0 + tl;
+    tls[p] = ci < total ? tl : 0;  // idle chunks still read a (valid) table row
     const int cc = ci % CPR;
     const int bb = row / Hkv, g = row - bb * Hkv;
     off[p] = (((size_t)bb * T + t) * Hkv + g) * D + (size_t)cc * EPC;
@@ -98,20 +111,22 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     }
   }
 
-  if (tid < D / 2) {
-    const double theta = exp2(-(double)tid / (D / 2) * log2_base);
+  for (int idx = tid; idx < npos * (D / 2); idx += 256) {
+    const int tl = idx / (D / 2), i = idx - tl * (D / 2);
+    const int t = t0 + tl;
+    const double theta = exp2(-(double)i / (D / 2) * log2_base);
     const double a = (double)(pos_offset + t) * theta;
     const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
     double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
     r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
     float sn, c;
     sincosf((float)r, &sn, &c);
-    cs[tid] = make_float2(c, sn);
+    cs[tl][i] = make_float2(c, sn);
     if (r0 == 0) {
       if constexpr (kBf)
-        reinterpret_cast<uint32_t*>(tabq)[(size_t)t * (D / 2) + tid] = pack_h2(c, sn);
+        reinterpret_cast<uint32_t*>(tabq)[(size_t)t * (D / 2) + i] = pack_h2(c, sn);
       else
-        reinterpret_cast<float2*>(tabq)[(size_t)t * (D / 2) + tid] = make_float2(c, sn);
+        reinterpret_cast<float2*>(tabq)[(size_t)t * (D / 2) + i] = make_float2(c, sn);
     }
   }
   __syncthreads();
@@ -136,7 +151,7 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
     float ss = 0.f;
 #pragma unroll
     for (int m = 0; m < EPC / 2; ++m) {
-      const float2 r = cs[cc * (EPC / 2) + m];
+      const float2 r = cs[tls[p]][cc * (EPC / 2) + m];
       const float xe = x[2 * m], xo = x[2 * m + 1];
       const float ye = xe * r.x - xo * r.y;
       const float yo = xe * r.y + xo * r.x;
@@ -189,18 +204,19 @@ static hipError_t attn_prep_launch(const void* k, void* kp, void* tabq, int B, i
   constexpr int RB = prep_rows_per_block<D, Elem>();
   const long long rows = (long long)B * Hkv;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int nrb = (int)((rows + RB - 1) / RB);
-  const long long nblk = (long long)T * nrb;
+  const int pp = 2 * rows <= RB ? (int)std::min<long long>(PREP_MAXPP, RB / rows) : 1;
+  const int nrb = pp > 1 ? 1 : (int)((rows + RB - 1) / RB);
+  const long long nblk = pp > 1 ? ((long long)T + pp - 1) / pp : (long long)T * nrb;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (vc != nullptr)
     hipLaunchKernelGGL((attn_prep_kernel<D, Elem, true>), dim3((unsigned)nblk), dim3(256), 0,
                        stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
-                       std::log2(rope_base), pos_offset, nrb, (const Elem*)v, (Elem*)vc, Tk, row0,
+                       std::log2(rope_base), pos_offset, nrb, pp, (const Elem*)v, (Elem*)vc, Tk, row0,
                        (const Elem*)ve, (const Elem*)vgate);
   else
     hipLaunchKernelGGL((attn_prep_kernel<D, Elem, false>), dim3((unsigned)nblk), dim3(256), 0,
                        stream, (const Elem*)k, (Elem*)kp, tabq, T, Hkv, (int)rows,
-                       std::log2(rope_base), pos_offset, nrb, (const Elem*)nullptr,
+                       std::log2(rope_base), pos_offset, nrb, pp, (const Elem*)nullptr,
                        (Elem*)nullptr, T, 0, (const Elem*)nullptr, (const Elem*)nullptr);
   return hipGetLastError();
 }
