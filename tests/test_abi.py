@@ -223,10 +223,10 @@ def test_workspace_queries():
     # one workgroup per (sequence, head) already fills the device: no split
     assert L.nc_attn_decode_workspace_bytes(64, 2048, 6, 6, 128, 2048) == 0
     assert L.nc_attn_decode_workspace_bytes(0, 2048, 6, 6, 128, 2048) == 0
-    # a shared prompt may be cut at its end: one more chunk state per (b, h)
-    # than the unsplit range, so room for two
-    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 2048) == 64 * 6 * 2 * 130 * 4
-    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 1600) == 64 * 6 * 2 * 130 * 4
+    # a shared prompt may be cut at its end and its part run in two chunks:
+    # two more chunk states per (b, h) than the unsplit range, so room for three
+    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 2048) == 64 * 6 * 3 * 130 * 4
+    assert L.nc_attn_decode_shared_workspace_bytes(64, 1536, 512, 6, 6, 128, 1600) == 64 * 6 * 3 * 130 * 4
     assert L.nc_attn_decode_shared_workspace_bytes(64, 0, 512, 6, 6, 128, 2048) == 0
 
 

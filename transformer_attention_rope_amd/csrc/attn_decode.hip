@@ -69,6 +69,7 @@ struct DecArgs {
   int nwg;      // workgroups with an item (the shared-prompt launch pads the grid to a multiple of 8)
   int cut;      // shared prompt: 1 cuts every range at the prompt's end; 0 lets a chunk span
                 // both caches (run as two segments in one workgroup)
+  int Cp;       // keys per chunk of a cut prompt part (= C otherwise)
   int C;        // keys per chunk (multiple of the keys per workgroup step)
   int nsplit;   // chunks per (b, g) upper bound = ceil(min(Tmax, W) / C)
   int ngh;      // head groups per K/V head = ceil(G / GP)
@@ -114,14 +115,15 @@ __device__ __forceinline__ int clamp_len(int L, int Lp, int Tmax) {
 // first, then those of the sequence's own rows [max(lo, Lp), L), C keys each,
 // so that no chunk spans both caches. Returns the chunk count and, for chunk
 // c, its key range [ks0, ks1). With Lp = 0 these are C-key chunks from lo.
-__device__ __forceinline__ int dec_chunks(int L, int lo, int Lp, int C, int c, int& ks0, int& ks1) {
-  const int ea = min(L, Lp);                           // end of the prompt part
-  const int na = lo < ea ? (ea - lo + C - 1) / C : 0;  // its chunks
+__device__ __forceinline__ int dec_chunks(int L, int lo, int Lp, int Cp, int C, int c, int& ks0,
+                                          int& ks1) {
+  const int ea = min(L, Lp);                             // end of the prompt part
+  const int na = lo < ea ? (ea - lo + Cp - 1) / Cp : 0;  // its chunks, Cp keys each
   const int sb = max(lo, Lp);                          // start of the own part
   const int nb = (L - sb + C - 1) / C;
   if (c < na) {
-    ks0 = lo + c * C;
-    ks1 = min(ks0 + C, ea);
+    ks0 = lo + c * Cp;
+    ks1 = min(ks0 + Cp, ea);
   } else {
     ks0 = sb + (c - na) * C;
     ks1 = min(ks0 + C, L);
@@ -236,7 +238,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
   int ks0, ks1;
-  const int nch = dec_chunks(L, lo, SH && a.cut ? Lp : 0, a.C, split, ks0, ks1);
+  const int nch = dec_chunks(L, lo, SH && a.cut ? Lp : 0, SH ? a.Cp : a.C, a.C, split, ks0, ks1);
   if (split >= nch) return;
   const bool owns_new = ks1 == L;
   // The chunk's keys as one or two segments [sk0, sk1): with a shared prompt
@@ -630,7 +632,7 @@ __global__ void __launch_bounds__(256) attn_decode_combine_kernel(DecArgs a) {
   const int L = clamp_len(a.seqlens[b], a.Lp, a.Tmax);
   const int lo = L > a.W ? L - a.W : 0;
   int ks0, ks1;
-  const int nch = dec_chunks(L, lo, a.cut ? a.Lp : 0, a.C, 0, ks0, ks1);
+  const int nch = dec_chunks(L, lo, a.cut ? a.Lp : 0, a.cut ? a.Cp : a.C, a.C, 0, ks0, ks1);
   if (nch <= 1) return;
   constexpr int PER = (D + 63) / 64;
   constexpr int NB = 8;  // chunk states loaded per batch
@@ -720,10 +722,15 @@ static int decode_nsplit(int Tmax, int W, int C) {
   return (span + C - 1) / C;
 }
 
-// A shared prompt adds at most one chunk (the one cut at the prompt's end).
+// A cut prompt part is run in this many chunks, next to the sequence's own
+// chunks (measured, 64 samples of a 1536-token d12 prompt at W = 2048:
+// 38.2 us in one chunk, 35.7 in two, 37.2 in three, 39.6 in four).
+constexpr int kDecCutPromptChunks = 2;
+
+// A shared prompt adds at most kDecCutPromptChunks chunks (its cut part).
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window, int Lp) {
   const int C = decode_chunk(B, Tmax, H, Hkv, D, window);
-  const int ns = decode_nsplit(Tmax, window, C) + (Lp > 0 ? 1 : 0);
+  const int ns = decode_nsplit(Tmax, window, C) + (Lp > 0 ? kDecCutPromptChunks : 0);
   if (ns <= 1) return 0;
   return (size_t)B * H * ns * (D + 2) * sizeof(float);
 }
@@ -792,7 +799,16 @@ hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const voi
   // samples of a 1536-token prompt at W = 2048: 37.9 us cut). Shorter prompt
   // parts run as the first segment of the same workgroup, with no merge pass.
   a.cut = (Lp > 0 && std::min(window, Lp) >= 1024) ? 1 : 0;
-  a.nsplit = decode_nsplit(Tmax, window, a.C) + (a.cut ? 1 : 0);
+  a.Cp = a.C;
+  int npc = 0;  // chunks of a cut prompt part
+  if (a.cut) {
+    npc = kDecCutPromptChunks;
+    const int kpi = decode_kpi(D, dt == kBF16);
+    const int span_p = std::min(window, Lp);
+    a.Cp = std::max(kpi, ((span_p + npc - 1) / npc + kpi - 1) / kpi * kpi);
+    npc = (span_p + a.Cp - 1) / a.Cp;
+  }
+  a.nsplit = decode_nsplit(Tmax, window, a.C) + (a.cut ? npc : 0);
   a.log2_base = std::log2(rope_base);
   a.part = (float*)ws;
   a.ncu = device_cu_count();
