@@ -12,6 +12,9 @@ Parity status of each function is stated in its module docstring:
     parity unpinned for those two conventions (everything else pinned).
   * ``qk_norm``: the epsilon (1e-6) is a reading; parity unpinned for eps.
   * ``attention`` / ``decode`` / ``prefill`` / ``decode_shared`` / ``value_gate``: pinned (see tests/test_oracle_pins.py).
+  * ``backward`` (``attn_fwd_lse``, ``rope_bwd``, ``qk_norm_bwd``,
+    ``attention_core_bwd``, ``attn_bwd``): pinned by finite differences of the
+    forward, closed forms, float64 autograd of the core and the GQA identity.
 """
 from .reference import (  # noqa: F401
     EPS,
@@ -27,4 +30,11 @@ from .reference import (  # noqa: F401
     attn_prefill,
     attn_decode_shared,
     value_gate,
+)
+from .backward import (  # noqa: F401
+    attn_fwd_lse,
+    rope_bwd,
+    qk_norm_bwd,
+    attention_core_bwd,
+    attn_bwd,
 )
