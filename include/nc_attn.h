@@ -83,7 +83,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 6
+#define NC_ABI_VERSION 7
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -143,6 +143,57 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nc_attn_fwd_lse -- nc_attn_fwd that also writes the row log-sum-exp the
+ * backward pass starts from (a training step runs the forward, then
+ * backpropagates: "从文本到聊天模型" (onehacker.top) §6.5).
+ *
+ *   lse  (B, T, H) float32  lse[b,t,h] = ln sum_j exp(q'_t . k'_j / sqrt(D))
+ *                           over the visible keys j (natural log); o and the
+ *                           other arguments as for nc_attn_fwd
+ * lse must be 4-byte aligned and must not overlap any other argument. o may
+ * differ from nc_attn_fwd's in the last bit (at D = 128 the call runs the
+ * two-wave attention kernel, whose registers leave room for the extra output).
+ * Workspace: nc_attn_fwd_workspace_bytes.
+ */
+nc_status nc_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int T, int H, int Hkv, int D, int window,
+                          double rope_base, int pos_offset, nc_dtype dtype,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_bwd -- gradients of the prefill forward with respect to its RAW
+ * inputs q, k, v ("从文本到聊天模型" §6.5, the training step's backward
+ * pass; "Nanochat与nanoGPT对比：关键升级" §1 table: the training attention
+ * runs forward and backward). The chain rule through nc_attn_fwd's
+ * definition: with P = exp(q'k'^T/sqrt(D) - lse) on the band and
+ * Delta_t = dO_t . o_t,
+ *   dv[g] = sum over g's query heads of P^T dO,  dS = P (dO v^T - Delta),
+ *   dq' = dS k' / sqrt(D),  dk'[g] = sum over g's query heads of dS^T q' / sqrt(D),
+ * then through the RMSNorm (dx = r (dy - y mean(dy y)), y = x r) and the
+ * RoPE rotation (rotated back by -p theta_i).
+ *
+ *   q, k, v   the forward's raw inputs, layouts as for nc_attn_fwd
+ *   o         (B, T, H, D)   the forward's output for them
+ *   dout      (B, T, H, D)   dL/do
+ *   lse       (B, T, H) f32  the forward's row log-sum-exp (nc_attn_fwd_lse)
+ *   dq        (B, T, H, D)   dL/dq      written, element type of the inputs
+ *   dk, dv    (B, T, Hkv, D) dL/dk, dL/dv (sums over each K/V head's group)
+ * window, rope_base and pos_offset must be the forward's. Requires the sizes
+ * of nc_attn_fwd and T * H * D * sizeof(element) < 2^32; dq, dk, dv must not
+ * overlap each other or any input; lse 4-byte aligned.
+ * Workspace (nc_attn_bwd_workspace_bytes): the (cos, sin) table, k', and for
+ * bf16 the prepared MFMA operands (q' scaled, transposed copies of q', dO and
+ * k' in tiles of 32 positions) and per-row lse and dO.o; calls that overlap in
+ * time must not share a workspace.
+ */
+size_t nc_attn_bwd_workspace_bytes(int B, int T, int H, int Hkv, int D, nc_dtype dtype);
+nc_status nc_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      int B, int T, int H, int Hkv, int D, int window,
+                      double rope_base, int pos_offset, nc_dtype dtype,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * nc_attn_prep / nc_attn_core -- the two stages of nc_attn_fwd, for callers
  * that schedule them separately (for instance to overlap one layer's prep with
  * another layer's attention on a second stream).
@@ -179,13 +230,20 @@ nc_status nc_attn_core(const void* q, const void* v, void* o, int B, int T, int 
  *   k, v     (B, T, Hkv, D)     their raw keys and values
  *   k_cache  (B, Tmax, Hkv, D)  rows 0 .. pos_offset-1 hold rotated, normalised
  *                               keys (from earlier calls or decode steps) and
- *                               are used as stored; rows pos_offset .. +T-1 are
+ *                               are used as stored (see the bound below); rows pos_offset .. +T-1 are
  *                               overwritten with norm(rope(k)); later rows are
  *                               neither read nor written
  *   v_cache  (B, Tmax, Hkv, D)  likewise; rows pos_offset .. +T-1 receive v
  *   o        (B, T, H, D)       o[b,t,h]: softmax over cache rows j with
  *                               0 <= pos_offset + t - j < window of
  *                               q'.k_cache[b,j] / sqrt(D), applied to v_cache
+ * Bound on stored rows: the attention kernels exponentiate the scores with a
+ * fixed scale instead of a running maximum (QK-norm bounds the scores of the
+ * rows this library writes, whose RMS is 1). That is exact for stored key rows
+ * of RMS at most 4: the scores then lie within +-4*sqrt(D), their exponentials
+ * and the row sums stay inside the fp32 and bf16 ranges. Rows of larger RMS
+ * are outside the contract (their exponentials may overflow); nc_attn_decode,
+ * which keeps a running maximum, has no such bound.
  * With pos_offset = 0 and Tmax = T, o equals nc_attn_fwd's. One pos_offset
  * serves the whole batch. The caches are written by a first kernel and read by
  * a second one on the same stream.

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 6
+    assert L.nc_abi_version() == 7
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -239,3 +239,48 @@ def test_binding_refuses_cpu_tensors():
         nc.rope_qknorm(q, q)
     with pytest.raises(ValueError, match="GPU"):
         nc.attn_prefill(q, q, q, torch.zeros(1, 8, 2, 32), torch.zeros(1, 8, 2, 32), window=4)
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, T=8, H=2, Hkv=2, D=64, window=8,
+             base=1e4, off=0, dt=0, ws=P, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return nc.lib().nc_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                                a["dv"], a["B"], a["T"], a["H"], a["Hkv"], a["D"], a["window"],
+                                a["base"], a["off"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(dq=None), 1, "dq is NULL"),
+    (dict(do=P + 8), 1, "dout is not 16-byte aligned"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(lse=P + 2), 1, "lse is not 4-byte aligned"),
+    (dict(H=3, Hkv=2), 1, "multiple"),
+    (dict(D=80), 2, "head dim"),
+    (dict(window=0), 1, "window"),
+    (dict(off=-1), 1, "pos_offset"),
+    (dict(wsb=100), 1, "workspace"),
+    (dict(T=1 << 21, H=16, Hkv=1, D=128), 2, "2^32"),
+])
+def test_attn_bwd_validation(kw, status, frag):
+    assert _bwd(**kw) == status
+    assert frag in nc.lib().nc_last_error().decode()
+
+
+def test_attn_fwd_lse_validation():
+    L = nc.lib()
+    st = L.nc_attn_fwd_lse(P, P, P, P, None, 1, 8, 2, 2, 64, 8, 1e4, 0, 0, P, 1 << 20, None)
+    assert st == 1 and b"lse is NULL" in L.nc_last_error()
+    st = L.nc_attn_fwd_lse(P, P, P, P, P + 1, 1, 8, 2, 2, 64, 8, 1e4, 0, 0, P, 1 << 20, None)
+    assert st == 1 and b"4-byte" in L.nc_last_error()
+
+
+def test_bwd_workspace_bytes():
+    L = nc.lib()
+    # bf16 d12 layer: the table, five bf16 tensors of the layer's size and the stats
+    n = L.nc_attn_bwd_workspace_bytes(8, 2048, 6, 6, 128, 0)
+    elems = 8 * 2048 * 6 * 128
+    assert n >= 5 * elems * 2  # k', k'^T, q', q'^T, dO^T
+    assert L.nc_attn_bwd_workspace_bytes(8, 2048, 6, 6, 96, 0) == 0
+    assert L.nc_attn_bwd_workspace_bytes(8, 2048, 6, 4, 128, 0) == 0
+    assert L.nc_attn_bwd_workspace_bytes(1, 64, 2, 2, 32, 1) > 0

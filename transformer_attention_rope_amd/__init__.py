@@ -8,6 +8,8 @@ library is not built, or a tensor is not on the GPU, the call raises.
 
     rope_qknorm(q, k, rope_base=1e4, pos_offset=0)          -> (q', k')
     attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
+    attn_fwd_lse(q, k, v, window=...) -> (o, lse)
+    attn_bwd(q, k, v, o, dout, lse, window=...) -> (dq, dk, dv)
     attn_prep(k, ...) -> workspace;  attn_core(q, v, workspace, window=...) -> o
     attn_prefill(q, k, v, k_cache, v_cache, window=..., pos_offset=0, rope_base=1e4) -> o
     attn_decode(q, k_new, v_new, k_cache, v_cache, seqlens, window=..., rope_base=1e4) -> o
@@ -21,7 +23,8 @@ import os
 import torch
 
 __all__ = [
-    "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_prefill", "attn_decode",
+    "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_fwd_lse", "attn_bwd",
+    "attn_bwd_workspace_bytes", "attn_prefill", "attn_decode",
     "attn_decode_shared", "attn_decode_shared_workspace_bytes",
     "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
@@ -45,6 +48,11 @@ _SIGS = {
     "nc_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "nc_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
+    "nc_attn_fwd_lse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz,
+                             _vp]),
+    "nc_attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i,
+                         _vp, _sz, _vp]),
     "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
     "nc_attn_core": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "nc_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -218,6 +226,63 @@ def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: in
           float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     return o
+
+
+def attn_fwd_lse(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: int = 0,
+                 out=None, lse=None, workspace=None):
+    """attn_fwd that also returns the row log-sum-exp lse (B,T,H) float32,
+    ln sum_j exp(q'.k'_j/sqrt(D)) over the visible keys (the backward's input)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    lse = (torch.empty((B, T, H), dtype=torch.float32, device=q.device) if lse is None
+           else _gpu(lse, "lse", 3, torch.float32))
+    if tuple(lse.shape) != (B, T, H):
+        raise ValueError("lse must be (B, T, H)")
+    ws = _workspace(attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, q.dtype), q.device, workspace)
+    _call("nc_attn_fwd_lse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, Hkv, D, int(window),
+          float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o, lse
+
+
+def attn_bwd_workspace_bytes(B, T, H, Hkv, D, dtype=torch.bfloat16) -> int:
+    dt = NC_F32 if dtype == torch.float32 else NC_BF16
+    return int(lib().nc_attn_bwd_workspace_bytes(B, T, H, Hkv, D, dt))
+
+
+def attn_bwd(q, k, v, o, dout, lse, *, window: int, rope_base: float = 10000.0, pos_offset: int = 0,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of attn_fwd with respect to its raw q, k, v, from
+    the forward's output o, dL/do and its row log-sum-exp lse (attn_fwd_lse)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    o = _gpu(o, "o", 4, q.dtype)
+    dout = _gpu(dout, "dout", 4, q.dtype)
+    lse = _gpu(lse, "lse", 3, torch.float32)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if (tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D) or o.shape != q.shape
+            or dout.shape != q.shape or tuple(lse.shape) != (B, T, H)):
+        raise ValueError("backward tensor shapes are inconsistent")
+    dq = torch.empty_like(q) if dq is None else _gpu(dq, "dq", 4, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _gpu(dk, "dk", 4, q.dtype)
+    dv = torch.empty_like(v) if dv is None else _gpu(dv, "dv", 4, q.dtype)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shapes must match q, k, v")
+    ws = _workspace(attn_bwd_workspace_bytes(B, T, H, Hkv, D, q.dtype), q.device, workspace)
+    _call("nc_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+          _ptr(dv), B, T, H, Hkv, D, int(window), float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(q))
+    return dq, dk, dv
 
 
 def attn_prep(k, *, rope_base: float = 10000.0, pos_offset: int = 0, H=None, workspace=None):

@@ -222,6 +222,60 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
   return nc_attn_core(q, v, o, B, T, H, Hkv, D, window, dt, ws, ws_bytes, stream);
 }
 
+nc_status nc_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int T, int H, int Hkv, int D, int window, double rope_base, int pos_offset,
+                          nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  const char* names[] = {"q", "k", "v", "o"};
+  const void* ptrs[] = {q, k, v, o};
+  if ((s = check_ptrs(names, ptrs, 4)) != NC_OK) return s;
+  if (lse == nullptr) return fail(NC_ERR_INVALID, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(NC_ERR_INVALID, "lse is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt))) != NC_OK)
+    return s;
+  if ((s = nc_attn_prep(k, B, T, Hkv, D, rope_base, pos_offset, dt, ws, ws_bytes, stream)) != NC_OK)
+    return s;
+  const size_t front = prep_table_bytes(T, D, dt) + prep_k_bytes(B, T, Hkv, D, dt);
+  hipError_t e = nc::launch_attn_core(q, (const char*)ws + prep_table_bytes(T, D, dt), v, o, B, T, H,
+                                      Hkv, D, window, ws, T, 0, (char*)ws + front,
+                                      part_bytes(B, T, H, Hkv, D, T, dt), to_dt(dt),
+                                      (hipStream_t)stream, lse);
+  if (e != hipSuccess) return hip_fail(e, "attn_core launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_bwd
+size_t nc_attn_bwd_workspace_bytes(int B, int T, int H, int Hkv, int D, nc_dtype dtype) {
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || (D != 32 && D != 64 && D != 128) ||
+      (dtype != NC_BF16 && dtype != NC_F32))
+    return 0;
+  return nc::attn_bwd_workspace_bytes(B, T, H, Hkv, D, to_dt(dtype));
+}
+
+nc_status nc_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int T, int H, int Hkv,
+                      int D, int window, double rope_base, int pos_offset, nc_dtype dt, void* ws,
+                      size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  if ((s = check_seq_bytes(T, H, D, dt)) != NC_OK) return s;  // q, o, dout rows: 32-bit offsets
+  const char* names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  if ((s = check_ptrs(names, ptrs, 8)) != NC_OK) return s;
+  if (lse == nullptr) return fail(NC_ERR_INVALID, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(NC_ERR_INVALID, "lse is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, nc_attn_bwd_workspace_bytes(B, T, H, Hkv, D, dt))) != NC_OK) return s;
+  hipError_t e = nc::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, T, H, Hkv, D, window,
+                                     rope_base, pos_offset, to_dt(dt), ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
 // ------------------------------------------------------------- attn_prefill
 // Workspace: the (cos, sin) table of the chunk's T positions, then room for
 // partial rows as in attn_fwd; k' and v go straight to the caches.

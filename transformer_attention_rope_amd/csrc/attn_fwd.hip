@@ -101,6 +101,7 @@ struct FwdArgs {
   int rows;      // B * T * H: output rows
   float* part;   // nsplit > 1: per slice, unnormalised fp32 output rows [nsplit][rows][D],
                  // then their row sums [nsplit][rows]
+  float* lse;    // optional: per output row, ln of the softmax denominator, fp32 (rows of o)
 };
 
 // =====================================================================
@@ -347,7 +348,12 @@ struct TileSchedTab {
 // The bf16 kernel body. With SPLIT, each workgroup runs one of nsplit slices
 // of its query tile's key tiles and writes unnormalised fp32 partial rows
 // (attn_split_combine_kernel adds them up); without, it writes o itself.
-template <int D, int NW, bool SPLIT>
+// LSE: whether the epilogue writes the row log-sum-exp (kLseNone: never;
+// kLseIfGiven: when p.lse is set). The 4-wave D = 128 body has no registers
+// to spare for it (with the write it spills), so it is built without; forward
+// calls that ask for the log-sum-exp at D = 128 run the 2-wave body.
+enum { kLseNone = 0, kLseIfGiven = 1 };
+template <int D, int NW, bool SPLIT, int LSE = kLseIfGiven>
 __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
   using C = BfCfg<D, NW>;
   constexpr int CB = C::CB;
@@ -958,7 +964,8 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
     uint16_t* const os = qs;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const float inv_l = 1.0f / sum_halves(lsum[cb]);
+      lsum[cb] = sum_halves(lsum[cb]);
+      const float inv_l = 1.0f / lsum[cb];
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -978,12 +985,21 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
       const u32x4_t w = ld16(os + r * C::QLD + qc * 8);
       if (tr < q_end) st16_nt(og + ((size_t)(qo_row0 + tr) * p.H + hr) * D + qc * 8, w);
     }
+    // the scores were exponentiated as 2^(s log2 e), so the row sum is the
+    // natural-exponent softmax denominator and ln of it the row log-sum-exp
+    if (LSE == kLseIfGiven && p.lse != nullptr && hf == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        if (t[cb] < q_end) p.lse[(size_t)(qo_row0 + t[cb]) * p.H + h[cb]] = __builtin_amdgcn_logf(lsum[cb]) * kLn2;
+    }
   }
 }
 
 template <int D, int NW>
+constexpr bool fwd_has_lse() { return !(D == 128 && NW == 4); }
+template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
-  attn_fwd_bf16_body<D, NW, false>(p);
+  attn_fwd_bf16_body<D, NW, false, fwd_has_lse<D, NW>() ? kLseIfGiven : kLseNone>(p);
 }
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_split_kernel(FwdArgs p) {
@@ -996,6 +1012,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_split_kernel(FwdArgs
 template <int D>
 __global__ void __launch_bounds__(256) attn_split_combine_kernel(const float* __restrict__ part,
                                                                  uint16_t* __restrict__ o,
+                                                                 float* __restrict__ lse,
                                                                  int rows, int nsplit) {
   constexpr int TPR = D / 4;  // threads per row
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -1014,6 +1031,7 @@ __global__ void __launch_bounds__(256) attn_split_combine_kernel(const float* __
   }
   const float inv = 1.0f / l;
   st8(o + row * D + 4 * c4, u32x2_t{pack_bf2(a0 * inv, a1 * inv), pack_bf2(a2 * inv, a3 * inv)});
+  if (lse != nullptr && c4 == 0) lse[row] = __builtin_amdgcn_logf(l) * kLn2;
 }
 
 // =====================================================================
@@ -1110,6 +1128,7 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
   if (tvalid) {
     float* orow = og + (((size_t)b * p.T + t) * p.H + h) * D;
     const float inv_l = 1.0f / lsum;
+    if (p.lse != nullptr) p.lse[((size_t)b * p.T + t) * p.H + h] = logf(lsum);
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv_l;
   }
@@ -1219,6 +1238,7 @@ static hipError_t launch_bf16(FwdArgs a, int hpw, size_t part_bytes, hipStream_t
   const long long grid = (long long)a.nqt * a.B * a.ngroups;
   if (grid * a.nsplit > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.nsplit == 1) {
+    if (!fwd_has_lse<D, NW>() && a.lse != nullptr) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
     return hipGetLastError();
   }
@@ -1229,7 +1249,7 @@ static hipError_t launch_bf16(FwdArgs a, int hpw, size_t part_bytes, hipStream_t
     if (e != hipSuccess) return e;
     const long long threads = (long long)a.rows * (D / 4);
     hipLaunchKernelGGL(attn_split_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                       0, stream, (const float*)a.part, (uint16_t*)a.o, a.rows, a.nsplit);
+                       0, stream, (const float*)a.part, (uint16_t*)a.o, a.lse, a.rows, a.nsplit);
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;
@@ -1262,9 +1282,10 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, size_t part_bytes, hipStream_t
     a.hpw_log2 = ilog2(hpw);
     a.ngroups = a.H / hpw;
     if constexpr (D == 128) {
-      // the narrow band, or a launch that is cut into slices
+      // the narrow band, a launch that is cut into slices, or one that writes
+      // the row log-sum-exp
       FwdArgs a2 = a;
-      if (fwd_narrow<D>(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1)
+      if (fwd_narrow<D>(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
         return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
     }
     return launch_bf16<D, fwd_waves<D>()>(a, hpw, part_bytes, stream);
@@ -1292,8 +1313,9 @@ size_t attn_core_part_bytes(int B, int T, int H, int Hkv, int D, int Tk, Dtype d
 
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
                             int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
-                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream) {
+                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream, float* lse) {
   FwdArgs a{};
+  a.lse = lse;
   a.q = q;
   a.kp = kp;
   a.v = v;

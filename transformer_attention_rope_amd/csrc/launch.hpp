@@ -30,10 +30,13 @@ hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k
 // kp and v hold Tk key rows per sequence, query row t sits at key row kofs + t.
 // part (part_bytes, at least attn_core_part_bytes) holds the partial rows of a
 // launch whose key tiles are cut into slices; with part_bytes 0 there is none.
+// lse, when not null, receives ln of each output row's softmax denominator
+// (fp32, one per row of o: the row log-sum-exp of the scaled scores).
 size_t attn_core_part_bytes(int B, int T, int H, int Hkv, int D, int Tk, Dtype dt);
 hipError_t launch_attn_core(const void* q, const void* kp, const void* v, void* o, int B, int T,
                             int H, int Hkv, int D, int window, const void* tabq, int Tk, int kofs,
-                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream);
+                            void* part, size_t part_bytes, Dtype dt, hipStream_t stream,
+                            float* lse = nullptr);
 
 size_t decode_workspace_bytes(int B, int Tmax, int H, int Hkv, int D, int window, int Lp);
 // ve_new (B, Hkv, D) and ve_gate (B, Hkv), or both null: v_new + ve_gate * ve_new
@@ -51,5 +54,13 @@ hipError_t launch_attn_decode_shared(const void* q, const void* k_new, const voi
                                      int B, int Tgen, int H, int Hkv, int D, int window,
                                      double rope_base, Dtype dt, void* ws, hipStream_t stream,
                                      const void* ve_new = nullptr, const void* ve_gate = nullptr);
+
+// ---- backward: gradients with respect to the raw q, k, v from dO and the
+// ---- forward's o and row log-sum-exp; ws of attn_bwd_workspace_bytes
+size_t attn_bwd_workspace_bytes(int B, int T, int H, int Hkv, int D, Dtype dt);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                           int T, int H, int Hkv, int D, int window, double rope_base,
+                           int pos_offset, Dtype dt, void* ws, hipStream_t stream);
 
 }  // namespace nc

@@ -24,7 +24,8 @@ in for those activations. After QK-norm every q/k row has unit RMS whatever
 the input scale, so N(0,1) inputs exercise the same operand ranges.
 
 Seed scheme: seed = 20260000 + 100*config + 10*layer + tensor, where tensor is
-0 q, 1 k, 2 v, 3 k_cache, 4 v_cache, 5 seqlens. Draws use
+0 q, 1 k, 2 v, 3 k_cache, 4 v_cache, 5 seqlens, 6 dO (the upstream gradient
+of the backward pass). Draws use
 ``torch.Generator('cpu')`` and ``torch.randn`` in float32, then an RNE cast to
 bfloat16 where the config is bf16. The same host bits feed both sides.
 """
@@ -35,7 +36,7 @@ from dataclasses import dataclass, field
 import torch
 
 SEED_BASE = 20260000
-T_Q, T_K, T_V, T_KCACHE, T_VCACHE, T_SEQLENS = range(6)
+T_Q, T_K, T_V, T_KCACHE, T_VCACHE, T_SEQLENS, T_DOUT = range(7)
 
 
 def seed_for(config: int, layer: int, tensor: int) -> int:
@@ -105,6 +106,11 @@ def prefill_inputs(cfg: PrefillConfig, layer: int = 0, B=None, T=None):
     k = randn((B, T, cfg.Hkv, cfg.D), seed_for(cfg.idx, layer, T_K), cfg.dtype)
     v = randn((B, T, cfg.Hkv, cfg.D), seed_for(cfg.idx, layer, T_V), cfg.dtype)
     return q, k, v
+
+
+def prefill_dout(cfg: PrefillConfig, layer: int = 0):
+    """dL/do (B,T,H,D) for the backward of layer `layer`: N(0,1), seeded."""
+    return randn((cfg.B, cfg.T, cfg.H, cfg.D), seed_for(cfg.idx, layer, T_DOUT), cfg.dtype)
 
 
 def decode_inputs(cfg: DecodeConfig, set_idx: int = 0):
@@ -210,6 +216,12 @@ def decode_shared_bytes(seqlens, Lp, Hkv, D, W, H, elem_bytes=2):
 def prefill_flops(B, T, H, D, W) -> int:
     """4*D flops per unmasked pair (2D for q.k, 2D for p*v)."""
     return 4 * D * unmasked_pairs(T, W) * B * H
+
+
+def backward_flops(B, T, H, D, W) -> int:
+    """10*D flops per unmasked pair: the five products of the attention
+    backward (q.k again, dO.v, P^T dO, dS k, dS^T q), 2D each."""
+    return 10 * D * unmasked_pairs(T, W) * B * H
 
 
 def decode_bytes(seqlens, Hkv, D, W, H, elem_bytes=2) -> int:
