@@ -513,8 +513,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "d12 L-layer prefill attention forward (RoPE + QK-norm fused), "
-                               "B=8 T=2048 H=Hkv=6 D=128 window=2048 (full causal), bf16",
+        "config": {"workload": "d12 L-layer prefill attention forward, B=8 T=2048 H=Hkv=6 D=128 "
+                               "window=2048 (full causal), bf16: q rotated and normalised in the "
+                               "attention kernel's load, k through the input-stage kernel "
+                               "(attn_prep_kernel writes k' and the q table), then the attention kernel",
                    "B": cfg.B, "T": cfg.T, "H": cfg.H, "Hkv": cfg.Hkv, "D": cfg.D, "window": W,
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

@@ -2,9 +2,9 @@
 
 Tolerances (the stated bar for this path): bf16 I/O with fp32 accumulation:
 max-abs <= 2e-2 and mean-abs <= 2e-3; fp32 I/O: max-abs <= 1e-5.
-Small shapes compare every output element; the full-size workloads (the same
-launches the benchmark times) compare sampled rows the oracle evaluates one
-by one, plus properties that hold at any size on every row.
+Small shapes and the full-size workloads (every layer of the prefill
+configurations, in the launches the benchmark times) compare every output
+element.
 """
 import numpy as np
 import pytest
@@ -130,46 +130,42 @@ def test_config0_tiny_fp32():
     _check(ko, rk, torch.float32, "config 0 k'")
 
 
-def _sample_rows(B, T, H, n, seed):
-    r = np.random.default_rng(seed)
-    rows = {(0, 0, 0), (B - 1, T - 1, H - 1)}
-    for t in (1, 31, 32, 63, 64, 127, 128, 511, 512, 1023, 2047):
-        if t < T:
-            rows.add((int(r.integers(B)), t, int(r.integers(H))))
-    while len(rows) < n:
-        rows.add((int(r.integers(B)), int(r.integers(T)), int(r.integers(H))))
-    return sorted(rows)
-
-
 def _full_size_properties(o, v, H, Hkv, W):
-    """Every row: finite; row 0 equals v row 0; each output lies in the range
-    spanned by that (b, kv-head)'s values (a convex combination)."""
+    """Every row: finite; row 0 equals v row 0 (its only visible key)."""
     G = H // Hkv
-    vg = v.repeat_interleave(G, dim=2).float()                  # (B,T,H,D)
     of = o.float()
     assert torch.isfinite(of).all()
-    d0 = (of[:, 0] - vg[:, 0]).abs().max().item()
+    d0 = (of[:, 0] - v[:, 0].float().repeat_interleave(G, dim=1)).abs().max().item()
     assert d0 <= BF_MAX, f"row 0 vs v0: {d0}"
-    lo = vg.amin(dim=1, keepdim=True) - BF_MAX
-    hi = vg.amax(dim=1, keepdim=True) + BF_MAX
-    assert ((of >= lo) & (of <= hi)).all(), "output outside the convex hull of v"
 
 
-@pytest.mark.parametrize("cidx,layer", [(1, 0), (2, 0), (2, 3), (3, 0), (3, 3)])
-def test_full_size_prefill_sampled(cidx, layer):
+# Every layer of configs 1-3 at full size, in the launch configuration the
+# benchmark times, against the oracle on the WHOLE output tensor: the oracle
+# runs one sequence at a time (bounded memory) and max-abs / mean-abs are
+# taken over every element of o.
+FULL_LAYERS = [(1, 0), (2, 0), (2, 1), (2, 2), (2, 3), (3, 0), (3, 1), (3, 2), (3, 3)]
+
+
+@pytest.mark.parametrize("cidx,layer", FULL_LAYERS, ids=lambda x: str(x))
+def test_full_size_prefill_whole(cidx, layer):
     cfg = wl.CONFIGS[cidx]
     W = cfg.windows[layer]
-    _say(f"config {cidx} layer {layer} W={W} full size")
+    _say(f"config {cidx} layer {layer} W={W} full size, whole tensor")
     q, k, v = wl.prefill_inputs(cfg, layer)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o = nc.attn_fwd(qd, kd, vd, window=W)
     torch.cuda.synchronize()
     _full_size_properties(o, vd, cfg.H, cfg.Hkv, W)
-    rows = _sample_rows(cfg.B, cfg.T, cfg.H, 48, seed=cidx * 10 + layer)
-    ref = oracle.attn_fwd_rows(q, k, v, rows, W)
     oc = o.cpu()
-    got = torch.stack([oc[b, t, h] for b, t, h in rows])
-    _check(got, ref, torch.bfloat16, f"config {cidx} layer {layer} sampled rows")
+    mx, tot = 0.0, 0.0
+    for b in range(cfg.B):
+        ref = oracle.attn_fwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], W)
+        d = np.abs(oc[b:b + 1].double().numpy() - ref)
+        mx = max(mx, float(d.max()))
+        tot += float(d.sum())
+    mn = tot / oc.numel()
+    print(f"[err] config {cidx} layer {layer} whole tensor: max {mx:.3e} mean {mn:.3e}", flush=True)
+    assert mx <= BF_MAX and mn <= BF_MEAN, f"config {cidx} layer {layer}: max {mx:.3e} mean {mn:.3e}"
 
 
 def test_full_window_equals_causal_bitwise():

@@ -190,3 +190,23 @@ def test_prefill_zero_gate_bitwise():
                          ve_gate=torch.zeros(2, 300, 2, dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(vc1, vc2) and torch.equal(kc1, kc2)
+
+
+@pytest.mark.parametrize("D,sliced", [(128, False), (64, True)])
+def test_prefill_cache_rows_at_rms_bound(D, sliced):
+    """Cache rows before the chunk are used as stored; the attention kernels
+    exponentiate with a fixed scale, which is exact for stored rows of RMS up
+    to 4 (the bound nc_attn_prefill states). Rows at RMS 4 (peaky softmax,
+    scores up to 4*sqrt(D)) against the oracle, unsliced and sliced."""
+    B, T, Tmax, P, H, Hkv = (2, 128, 640, 512, 4, 2) if not sliced else (1, 256, 2048, 1792, 2, 1)
+    _say(f"prefill cache rows at the RMS bound D={D} sliced={sliced}")
+    g = torch.Generator().manual_seed(515 + D)
+    q = torch.randn(B, T, H, D, generator=g).bfloat16()
+    k = torch.randn(B, T, Hkv, D, generator=g).bfloat16()
+    v = torch.randn(B, T, Hkv, D, generator=g).bfloat16()
+    kc = torch.randn(B, Tmax, Hkv, D, generator=g)
+    kc = (kc * (4.0 / kc.pow(2).mean(-1, keepdim=True).sqrt())).bfloat16()  # every row at RMS 4
+    vc = torch.randn(B, Tmax, Hkv, D, generator=g).bfloat16()
+    rms = kc[:, :P].float().pow(2).mean(-1).sqrt().max().item()
+    assert rms <= 4.0 * (1 + 2 ** -7), rms
+    _run_and_check(q, k, v, kc, vc, 2048, P, torch.bfloat16, f"rms-bound D={D}")
