@@ -83,7 +83,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 7
+#define NC_ABI_VERSION 8
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -192,6 +192,25 @@ nc_status nc_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       int B, int T, int H, int Hkv, int D, int window,
                       double rope_base, int pos_offset, nc_dtype dtype,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_fwd_noalloc -- nc_attn_fwd for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, result and kernels
+ * as nc_attn_fwd minus the workspace: the workspace lives in a static 64 MiB
+ * device array of the library (one per GPU, held from module load until the
+ * process ends), on the CURRENT device (hipGetDevice), where q, k, v, o and
+ * stream must be. Nothing is allocated or freed, and nothing needs clearing
+ * (every byte the kernels read is written earlier in the same call).
+ * Errors: NC_ERR_INVALID when nc_attn_fwd_workspace_bytes for the sizes
+ * exceeds 64 MiB (k' alone takes B*T*Hkv*D*sizeof(element): B = 8, T = 2048,
+ * Hkv = 6, D = 128 in bf16 needs 25.7 MB in all, B = 32 does not fit),
+ * otherwise as nc_attn_fwd. Calls that overlap in time on one GPU (several
+ * streams or threads) share the array and race: serialise them.
+ */
+nc_status nc_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                              int B, int T, int H, int Hkv, int D, int window,
+                              double rope_base, int pos_offset, nc_dtype dtype, void* stream);
 
 /*
  * nc_attn_prep / nc_attn_core -- the two stages of nc_attn_fwd, for callers

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 7
+    assert L.nc_abi_version() == 8
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -284,3 +284,14 @@ def test_bwd_workspace_bytes():
     assert L.nc_attn_bwd_workspace_bytes(8, 2048, 6, 6, 96, 0) == 0
     assert L.nc_attn_bwd_workspace_bytes(8, 2048, 6, 4, 128, 0) == 0
     assert L.nc_attn_bwd_workspace_bytes(1, 64, 2, 2, 32, 1) > 0
+
+
+def test_fwd_noalloc_rejects_beyond_scratch():
+    """Sizes whose workspace exceeds the static 64 MiB scratch are refused on
+    the host, before any HIP call."""
+    L = nc.lib()
+    # B=32 d12 layer: k' alone is 100 MB
+    st = L.nc_attn_fwd_noalloc(P, P, P, P, 32, 2048, 6, 6, 128, 2048, 1e4, 0, 0, None)
+    assert st == 1 and b"beyond the library's static" in L.nc_last_error()
+    st = L.nc_attn_fwd_noalloc(P, P, P, P, 1, 8, 2, 2, 48, 8, 1e4, 0, 0, None)
+    assert st == 2 and b"head dim" in L.nc_last_error()

@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_fwd_lse", "attn_bwd",
-    "attn_bwd_workspace_bytes", "attn_prefill", "attn_decode",
+    "attn_bwd_workspace_bytes", "attn_fwd_noalloc", "attn_prefill", "attn_decode",
     "attn_decode_shared", "attn_decode_shared_workspace_bytes",
     "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
@@ -51,6 +51,7 @@ _SIGS = {
     "nc_attn_fwd_lse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz,
                              _vp]),
     "nc_attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp]),
     "nc_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                          _vp, _sz, _vp]),
     "nc_attn_prep": (_i, [_vp, _i, _i, _i, _i, _d, _i, _i, _vp, _sz, _vp]),
@@ -251,6 +252,24 @@ def attn_fwd_lse(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset
           float(rope_base), int(pos_offset), _dt(q), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     return o, lse
+
+
+def attn_fwd_noalloc(q, k, v, *, window: int, out, rope_base: float = 10000.0, pos_offset: int = 0):
+    """attn_fwd into the caller's `out` with the library's static scratch as its
+    workspace: the C entry point allocates nothing (q, k, v, out on the current
+    device). Calls overlapping on one GPU race on the shared scratch."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    o = _gpu(out, "out", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D) or o.shape != q.shape:
+        raise ValueError("attn_fwd_noalloc tensor shapes are inconsistent")
+    with torch.cuda.device(q.device):
+        _call("nc_attn_fwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
+              float(rope_base), int(pos_offset), _dt(q), _stream(q))
+    return o
 
 
 def attn_bwd_workspace_bytes(B, T, H, Hkv, D, dtype=torch.bfloat16) -> int:

@@ -247,6 +247,27 @@ nc_status nc_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, 
   return ok();
 }
 
+nc_status nc_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int T,
+                              int H, int Hkv, int D, int window, double rope_base, int pos_offset,
+                              nc_dtype dt, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  const size_t need = nc_attn_fwd_workspace_bytes(B, T, H, Hkv, D, pos_offset, dt);
+  if (need > nc::scratch_capacity())
+    return fail(NC_ERR_INVALID, "the call needs %zu bytes of scratch, beyond the library's static %zu",
+                need, nc::scratch_capacity());
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  const char* names[] = {"q", "k", "v", "o"};
+  const void* ptrs[] = {q, k, v, o};
+  if ((s = check_ptrs(names, ptrs, 4)) != NC_OK) return s;
+  void* ws = nullptr;
+  hipError_t e = nc::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return nc_attn_fwd(q, k, v, o, B, T, H, Hkv, D, window, rope_base, pos_offset, dt, ws,
+                     nc::scratch_capacity(), stream);
+}
+
 // ---------------------------------------------------------------- attn_bwd
 size_t nc_attn_bwd_workspace_bytes(int B, int T, int H, int Hkv, int D, nc_dtype dtype) {
   if (B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || (D != 32 && D != 64 && D != 128) ||

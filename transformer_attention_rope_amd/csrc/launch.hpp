@@ -63,4 +63,10 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            int T, int H, int Hkv, int D, int window, double rope_base,
                            int pos_offset, Dtype dt, void* ws, hipStream_t stream);
 
+// ---- the static per-device scratch of the entry point that allocates
+// ---- nothing: its size, and its address on the current device (looked up
+// ---- once per device)
+size_t scratch_capacity();
+hipError_t scratch_address(void** out);
+
 }  // namespace nc
