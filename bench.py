@@ -92,6 +92,17 @@ def event_time_ms(fn, n, torch):
     return s.elapsed_time(e) / n
 
 
+def trial_times_ms(fn, trials, n, torch):
+    """Per-call ms of `trials` separate runs of n back-to-back calls each."""
+    return [event_time_ms(fn, n, torch) for _ in range(trials)]
+
+
+def median(xs):
+    xs = sorted(xs)
+    m = len(xs) // 2
+    return xs[m] if len(xs) % 2 else 0.5 * (xs[m - 1] + xs[m])
+
+
 def settle(fn, ms, torch):
     """Run fn(i) untimed, keeping the GPU busy, until at least ms of GPU time
     has passed since the first call; returns the number of calls made."""
@@ -146,7 +157,38 @@ def cpu_baseline(budget_s: float):
             "kind": "oracle",
             "sample": f"d12 L-layer prefill, {n} of {cfg.B * cfg.H} (b,h) heads "
                       f"(T=2048, D=128, full causal), fp64 NumPy, {dt:.1f} s wall",
-            "host_cpu_count": os.cpu_count()}
+            "host_cpu_count": os.cpu_count(),
+            "per_config_wall_s": oracle_wall_per_config()}
+
+
+def oracle_wall_per_config():
+    """Oracle wall time of each whole configuration, from a timed sample:
+    config 0 whole; configs 1-3 one (b, h) head per layer, scaled by the
+    heads; config 4 eight sequences per window, scaled by the batch."""
+    import oracle
+    import workloads as wl
+    res = {}
+    c0 = wl.CONFIGS[0]
+    q, k, v = wl.prefill_inputs(c0)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, c0.windows[0])
+    res["0"] = round(time.perf_counter() - t0, 4)
+    for cidx in (1, 2, 3):
+        c = wl.CONFIGS[cidx]
+        tot = 0.0
+        for l, w in enumerate(c.windows):
+            q, k, v = wl.prefill_inputs(c, l, B=1)
+            t0 = time.perf_counter()
+            oracle.attn_fwd(q[:, :, :1], k[:, :, :1], v[:, :, :1], w)
+            tot += (time.perf_counter() - t0) * c.B * c.H
+        res[str(cidx)] = round(tot, 2)
+    c4 = wl.CONFIGS[4]
+    q, kn, vn, kc, vc, L = wl.decode_inputs(c4)
+    for w in c4.windows:
+        t0 = time.perf_counter()
+        oracle.attn_decode(q[:8], kn[:8], vn[:8], kc[:8], vc[:8], L[:8], w)
+        res[f"4_W{w}"] = round((time.perf_counter() - t0) * c4.B / 8, 3)
+    return res
 
 
 def main():
@@ -159,7 +201,7 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
                     choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "shared", "gate",
-                             "copy"],
+                             "bwd", "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -185,6 +227,7 @@ def main():
     settled = {}   # calls made by the settling run of each part
 
     def prime(name, fn):
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
         settled[name] = settle(fn, args.settle_ms, torch)
         for i in range(Wm):
             fn(i)
@@ -219,6 +262,17 @@ def main():
             prime("step", step)
             ms = event_time_ms(step, K, torch)
             out["step_ms"] = ms
+            # the timing protocol's median of 5 trials of 50 launches, and the
+            # same with one input set (no rotation: the 256 MB last-level cache
+            # then holds part of the inputs between steps)
+            out["trials_ms"] = trial_times_ms(step, 5, min(50, K), torch)
+
+            def step1(i):
+                q, k, v, o = sets[0]
+                nc.attn_fwd(q, k, v, window=W, out=o, workspace=ws)
+
+            prime("step_one_set", step1)
+            out["one_set_trials_ms"] = trial_times_ms(step1, 5, min(50, K), torch)
         if args.only in ("all", "core"):
             # one prepared workspace (k' and table) per input set
             wss = [nc.attn_prep(k, workspace=torch.empty_like(ws)) for (q, k, v, o) in sets]
@@ -328,10 +382,84 @@ def main():
             stacks[c.name] = {"shape": f"B={c.B} T={c.T} H={c.H} Hkv={c.Hkv} D={c.D} "
                                        f"windows={list(c.windows)}",
                               "us_per_stack": round(ms * 1e3, 2), "TFLOP_per_s": round(tf, 1),
-                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "stack_trials_median_us": round(
+                                  median(trial_times_ms(sstep, 5, min(13, K), torch)) * 1e3, 2)}
+            # each layer alone (prep + attention), and its attention kernel alone
+            per = []
+            for l, (q, k, v) in enumerate(layers):
+                w_l = c.windows[l]
+
+                def lstep(i, q=q, k=k, v=v, l=l, w_l=w_l):
+                    nc.attn_fwd(q, k, v, window=w_l, out=outs[l], workspace=wsc)
+
+                wsl = nc.attn_prep(k, H=c.H, workspace=torch.empty_like(wsc))
+
+                def kstep(i, q=q, v=v, l=l, w_l=w_l, wsl=wsl):
+                    nc.attn_core(q, v, wsl, window=w_l, out=outs[l])
+
+                prime(f"{c.name}_layer{l}", lstep)
+                ms_l = event_time_ms(lstep, K, torch)
+                prime(f"{c.name}_core{l}", kstep)
+                ms_k = event_time_ms(kstep, K, torch)
+                fl_l = wl.prefill_flops(c.B, c.T, c.H, c.D, w_l)
+                per.append({"window": w_l, "us": round(ms_l * 1e3, 2),
+                            "frac_bf16_peak": round(fl_l / (ms_l * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "kernel_us": round(ms_k * 1e3, 2),
+                            "kernel_frac_bf16_peak": round(fl_l / (ms_k * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+                del wsl
+            stacks[c.name]["layers"] = per
             del layers, outs, wsc
         if args.only == "stacks":
             print(json.dumps(stacks))
+            return
+
+    # ------------------------------------------- training: forward + backward
+    bwd = {}
+    if args.only in ("all", "bwd"):
+        for cidx in (1, 2, 3):
+            c = wl.CONFIGS[cidx]
+            per = []
+            for l in range(len(c.windows)):
+                if cidx == 2 and l > 0 and c.windows[l] == c.windows[0]:
+                    continue  # layers 1, 2 of a stack repeat layer 0's shape and window
+                if cidx == 3 and l > 0 and c.windows[l] == c.windows[0]:
+                    continue
+                w_l = c.windows[l]
+                q, k, v = (t.to(dev) for t in wl.prefill_inputs(c, layer=l))
+                do = wl.prefill_dout(c, layer=l).to(dev)
+                o = torch.empty_like(q)
+                lse = torch.empty(c.B, c.T, c.H, dtype=torch.float32, device=dev)
+                wsf = torch.empty(nc.attn_fwd_workspace_bytes(c.B, c.T, c.H, c.Hkv, c.D, 0, c.dtype),
+                                  dtype=torch.uint8, device=dev)
+                wsb = torch.empty(nc.attn_bwd_workspace_bytes(c.B, c.T, c.H, c.Hkv, c.D, c.dtype),
+                                  dtype=torch.uint8, device=dev)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+                def fstep(i, q=q, k=k, v=v, o=o, lse=lse, wsf=wsf, w_l=w_l):
+                    nc.attn_fwd_lse(q, k, v, window=w_l, out=o, lse=lse, workspace=wsf)
+
+                def bstep(i, q=q, k=k, v=v, o=o, lse=lse, do=do, wsb=wsb, w_l=w_l, dq=dq, dk=dk, dv=dv):
+                    nc.attn_bwd(q, k, v, o, do, lse, window=w_l, dq=dq, dk=dk, dv=dv, workspace=wsb)
+
+                prime(f"fwd_lse_c{cidx}_l{l}", fstep)
+                ms_f = event_time_ms(fstep, K, torch)
+                prime(f"bwd_c{cidx}_l{l}", bstep)
+                ms_b = event_time_ms(bstep, K, torch)
+                pairs = wl.unmasked_pairs(c.T, w_l) * c.B * c.H
+                tf_b = wl.backward_flops(c.B, c.T, c.H, c.D, w_l) / (ms_b * 1e-3) / 1e12
+                tf_f = wl.prefill_flops(c.B, c.T, c.H, c.D, w_l) / (ms_f * 1e-3) / 1e12
+                per.append({"layer": l, "window": w_l, "fwd_lse_us": round(ms_f * 1e3, 2),
+                            "fwd_lse_frac_bf16_peak": round(tf_f / PEAK_BF16_TFLOPS, 4),
+                            "bwd_us": round(ms_b * 1e3, 2), "bwd_TFLOP_per_s": round(tf_b, 1),
+                            "bwd_frac_bf16_peak": round(tf_b / PEAK_BF16_TFLOPS, 4),
+                            "unmasked_pairs": pairs})
+                del q, k, v, do, o, lse, wsf, wsb, dq, dk, dv
+            bwd[c.name] = {"shape": f"B={c.B} T={c.T} H={c.H} Hkv={c.Hkv} D={c.D}", "layers": per}
+        bwd["flops"] = ("backward: 10*D per unmasked pair (q.k recomputed, dO.v, P^T dO, dS k, dS^T q); "
+                        "forward: 4*D")
+        if args.only == "bwd":
+            print(json.dumps(bwd))
             return
 
     # ------------------------------------- prefill into the KV cache (chunked)
@@ -520,6 +648,11 @@ def main():
                    "B": cfg.B, "T": cfg.T, "H": cfg.H, "Hkv": cfg.Hkv, "D": cfg.D, "window": W,
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "step_trials": {"trials": 5, "launches": min(50, K), "median_ms": round(median(out["trials_ms"]), 5),
+                        "ms": [round(x, 5) for x in out["trials_ms"]],
+                        "one_input_set_median_ms": round(median(out["one_set_trials_ms"]), 5),
+                        "note": "rotated: 4 input sets (~300 MB, beyond the 256 MB last-level cache); "
+                                "one set: the same inputs every step"},
         "roofline": {"bound": "mfma", "achieved": round(kern_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(),
@@ -530,6 +663,7 @@ def main():
         "decode": dec,
         "rope_qknorm": rope,
         "stacks": stacks,
+        "backward": bwd,
         "prefill_cache": pre,
         "decode_shared_prompt": shd,
         "value_gate": gate,

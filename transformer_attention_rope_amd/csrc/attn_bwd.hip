@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_bf16_kernel(BwdArgs p) {
 // kernel A (bf16): dK, dV per (b, g, 128 keys)
 // =====================================================================
 template <int D>
-__global__ void __launch_bounds__(256, 1) attn_bwd_kv_bf16_kernel(BwdArgs p) {
+__global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_kv_bf16_kernel(BwdArgs p) {
   using C = BwCfg<D>;
   // stage: Q rows, dO rows, Q^T, dO^T, then the stats block (lse2[32], delta[32])
   constexpr int STAGE = 2 * C::ROWT + 2 * C::TRT + 512;  // bf16 elements
@@ -357,14 +357,18 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kv_bf16_kernel(BwdArgs p) {
     const int buf = step & 1;
     if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
     const int t0 = (qt_lo + step % nqt) * 32;
-    // this wave's 32x32 block: skip when no pair is visible
+    // this wave's 32x32 block: the score work is skipped when no pair is
+    // visible; the dV, dK products then run on zero operands, so that the
+    // accumulators are updated on every path (a conditional update makes the
+    // compiler copy all of them between register files on every step)
     const bool any = t0 + 31 >= j0 && t0 - (j0 + 31) < p.W && t0 < p.T;
+    const uint16_t* st = smem + buf * STAGE;
+    const uint16_t* qtt = st + 2 * C::ROWT;
+    const uint16_t* dtt = st + 2 * C::ROWT + C::TRT;
+    uint32_t pw[4][2], sw[4][2];
     if (any) {
-      const uint16_t* st = smem + buf * STAGE;
       const uint16_t* qt = st;
       const uint16_t* dt = st + C::ROWT;
-      const uint16_t* qtt = st + 2 * C::ROWT;
-      const uint16_t* dtt = st + 2 * C::ROWT + C::TRT;
       const float* stat = reinterpret_cast<const float*>(st + 2 * C::ROWT + 2 * C::TRT);
       f32x16_t sa, pa;
 #pragma unroll
@@ -379,7 +383,6 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kv_bf16_kernel(BwdArgs p) {
       }
       // rows of the accumulators: query t0 + 8 (r / 4) + 4 hf + r % 4
       const bool full = t0 >= j0 + 31 && t0 + 31 - j0 < p.W && t0 + 31 < p.T;
-      uint32_t pw[4][2], sw[4][2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(stat + 8 * r4 + 4 * hf);
@@ -402,18 +405,21 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kv_bf16_kernel(BwdArgs p) {
         sw[r4][0] = pack_bf2(sv[0], sv[1]);
         sw[r4][1] = pack_bf2(sv[2], sv[3]);
       }
-      // k-step s2 of the next products takes registers 8 s2 .. 8 s2 + 7
+    } else {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t bp = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{pw[2 * s2][0], pw[2 * s2][1], pw[2 * s2 + 1][0], pw[2 * s2 + 1][1]});
-        const bf16x8_t bs = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{sw[2 * s2][0], sw[2 * s2][1], sw[2 * s2 + 1][0], sw[2 * s2 + 1][1]});
+      for (int r4 = 0; r4 < 4; ++r4) pw[r4][0] = pw[r4][1] = sw[r4][0] = sw[r4][1] = 0u;
+    }
+    // k-step s2 of the next products takes registers 8 s2 .. 8 s2 + 7
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(dtt, db, s2), bp, dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(qtt, db, s2), bs, dka[db], 0, 0, 0);
-        }
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8_t bp = __builtin_bit_cast(
+          bf16x8_t, u32x4_t{pw[2 * s2][0], pw[2 * s2][1], pw[2 * s2 + 1][0], pw[2 * s2 + 1][1]});
+      const bf16x8_t bs = __builtin_bit_cast(
+          bf16x8_t, u32x4_t{sw[2 * s2][0], sw[2 * s2][1], sw[2 * s2 + 1][0], sw[2 * s2 + 1][1]});
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(dtt, db, s2), bp, dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(qtt, db, s2), bs, dka[db], 0, 0, 0);
       }
     }
     wg_sync();
