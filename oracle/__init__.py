@@ -15,6 +15,8 @@ Parity status of each function is stated in its module docstring:
   * ``backward`` (``attn_fwd_lse``, ``rope_bwd``, ``qk_norm_bwd``,
     ``attention_core_bwd``, ``attn_bwd``): pinned by finite differences of the
     forward, closed forms, float64 autograd of the core and the GQA identity.
+  * ``projection`` (``qkv_rope_qknorm``): pinned by scalar brute force, the
+    identity-weight and zero-weight cases and linearity.
 """
 from .reference import (  # noqa: F401
     EPS,
@@ -31,6 +33,7 @@ from .reference import (  # noqa: F401
     attn_decode_shared,
     value_gate,
 )
+from .projection import qkv_rope_qknorm  # noqa: F401
 from .backward import (  # noqa: F401
     attn_fwd_lse,
     rope_bwd,
