@@ -201,7 +201,7 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the MALL)")
     ap.add_argument("--only", default="all",
                     choices=["all", "fwd", "core", "decode", "rope", "stacks", "prefill", "shared", "gate",
-                             "bwd", "copy"],
+                             "bwd", "qkv", "copy"],
                     help="run one part (used for profiler runs); 'copy' runs a plain "
                          "1 GiB device copy for counter calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -462,6 +462,39 @@ def main():
             print(json.dumps(bwd))
             return
 
+    # ---------------------- fused q, k, v projection with RoPE + QK-norm epilogue
+    qkv = {}
+    if args.only in ("all", "qkv"):
+        for name, sh in wl.QKV.items():
+            qsets = []
+            for s_ in range(args.sets):
+                x, wq, wk, wv = (t.to(dev) for t in wl.qkv_inputs(**sh, seed=s_))
+                qsets.append((x, wq, wk, wv))
+            B, T, C, H, Hkv, D = sh["B"], sh["T"], sh["C"], sh["H"], sh["Hkv"], sh["D"]
+            qo = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=dev)
+            ko = torch.empty(B, T, Hkv, D, dtype=torch.bfloat16, device=dev)
+            vo = torch.empty_like(ko)
+            wsq = torch.empty(nc.qkv_rope_qknorm_workspace_bytes(T, D), dtype=torch.uint8, device=dev)
+
+            def qstep(i, qsets=qsets, H=H, Hkv=Hkv, qo=qo, ko=ko, vo=vo, wsq=wsq):
+                x, wq, wk, wv = qsets[i % len(qsets)]
+                nc.qkv_rope_qknorm(x, wq, wk, wv, H=H, Hkv=Hkv, q_out=qo, k_out=ko, v_out=vo, workspace=wsq)
+
+            prime(f"qkv_{name}", qstep)
+            ms = event_time_ms(qstep, K, torch)
+            fl = wl.qkv_flops(B, T, C, H, Hkv, D)
+            tf = fl / (ms * 1e-3) / 1e12
+            nbytes = (B * T * C + (H + 2 * Hkv) * D * C + B * T * (H + 2 * Hkv) * D) * 2
+            qkv[name] = {"shape": f"x (B={B}, T={T}, C={C}) -> q' (H={H}), k', v (Hkv={Hkv}), D={D}, bf16",
+                         "us_per_call": round(ms * 1e3, 2), "TFLOP_per_s": round(tf, 1),
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "GFLOP": round(fl / 1e9, 2),
+                         "algorithmic_bytes": nbytes}
+            del qsets, qo, ko, vo, wsq
+        qkv["flops"] = "2 per multiply-add of the three projections (table and epilogue not counted)"
+        if args.only == "qkv":
+            print(json.dumps(qkv))
+            return
+
     # ------------------------------------- prefill into the KV cache (chunked)
     pre = {}
     if args.only in ("all", "prefill"):
@@ -664,6 +697,7 @@ def main():
         "rope_qknorm": rope,
         "stacks": stacks,
         "backward": bwd,
+        "qkv_projection": qkv,
         "prefill_cache": pre,
         "decode_shared_prompt": shd,
         "value_gate": gate,

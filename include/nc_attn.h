@@ -83,7 +83,7 @@ typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 8
+#define NC_ABI_VERSION 9
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -109,6 +109,35 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
                          int B, int T, int H, int Hkv, int D,
                          double rope_base, int pos_offset, nc_dtype dtype,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_qkv_rope_qknorm -- the bias-free q, k, v projections of the block input
+ * followed by RoPE and QK-norm on q and k, in one kernel ("从文本到聊天模型"
+ * §5.4: q = c_q(x), k = c_k(x), v = c_v(x), viewed as (B, T, H, D) and
+ * (B, T, Hkv, D); "Nanochat与nanoGPT对比：关键升级" §1 table: no bias, QK-norm
+ * after RoPE).
+ *
+ *   x      (B, T, C)     block input (after the block's pre-norm)
+ *   w_q    (H*D, C)      weights in the linear-layer layout (out, in): output
+ *   w_k    (Hkv*D, C)    column h*D + d is element d of head h; the element
+ *   w_v    (Hkv*D, C)    type of the call (fp32 master weights are cast by
+ *                        the caller)
+ *   q_out  (B, T, H, D)   norm(rope(x w_q^T)) at positions pos_offset + t
+ *   k_out  (B, T, Hkv, D) norm(rope(x w_k^T))
+ *   v_out  (B, T, Hkv, D) x w_v^T
+ * q_out and k_out equal nc_rope_qknorm applied to the plain projections, but
+ * formed from the fp32 accumulators with one rounding to the element type.
+ * Requires C >= 64 and C % 64 == 0 (else NC_ERR_UNSUPPORTED), the sizes of
+ * nc_rope_qknorm, outputs disjoint from each other and from the inputs.
+ * Workspace (nc_qkv_rope_qknorm_workspace_bytes): the (cos, sin) table of the
+ * T positions.
+ */
+size_t nc_qkv_rope_qknorm_workspace_bytes(int T, int D, nc_dtype dtype);
+nc_status nc_qkv_rope_qknorm(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                             void* q_out, void* k_out, void* v_out,
+                             int B, int T, int C, int H, int Hkv, int D,
+                             double rope_base, int pos_offset, nc_dtype dtype,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * nc_attn_fwd -- prefill forward of one attention layer from RAW q, k, v

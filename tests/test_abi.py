@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 8
+    assert L.nc_abi_version() == 9
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -295,3 +295,23 @@ def test_fwd_noalloc_rejects_beyond_scratch():
     assert st == 1 and b"beyond the library's static" in L.nc_last_error()
     st = L.nc_attn_fwd_noalloc(P, P, P, P, 1, 8, 2, 2, 48, 8, 1e4, 0, 0, None)
     assert st == 2 and b"head dim" in L.nc_last_error()
+
+
+def test_qkv_validation():
+    L = nc.lib()
+
+    def call(**kw):
+        a = dict(x=P, wq=P, wk=P, wv=P, q=P, k=P, v=P, B=1, T=8, C=64, H=2, Hkv=2, D=64, base=1e4, off=0,
+                 dt=0, ws=P, wsb=1 << 20)
+        a.update(kw)
+        return L.nc_qkv_rope_qknorm(a["x"], a["wq"], a["wk"], a["wv"], a["q"], a["k"], a["v"], a["B"],
+                                    a["T"], a["C"], a["H"], a["Hkv"], a["D"], a["base"], a["off"], a["dt"],
+                                    a["ws"], a["wsb"], None)
+    assert call(C=100) == 2 and b"multiple of 64" in L.nc_last_error()
+    assert call(C=0) == 1
+    assert call(wk=None) == 1 and b"w_k is NULL" in L.nc_last_error()
+    assert call(v=P + 8) == 1 and b"v_out is not 16-byte aligned" in L.nc_last_error()
+    assert call(D=96) == 2
+    assert call(wsb=8) == 1 and b"workspace" in L.nc_last_error()
+    assert call(ws=None) == 1
+    assert L.nc_qkv_rope_qknorm_workspace_bytes(2048, 128, 0) >= 2048 * 64 * 4

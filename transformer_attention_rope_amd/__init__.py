@@ -7,6 +7,7 @@ current torch stream of the tensors' device. There is no CPU fallback: if the
 library is not built, or a tensor is not on the GPU, the call raises.
 
     rope_qknorm(q, k, rope_base=1e4, pos_offset=0)          -> (q', k')
+    qkv_rope_qknorm(x, w_q, w_k, w_v, H=..., Hkv=...)        -> (q', k', v)
     attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
     attn_fwd_lse(q, k, v, window=...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, window=...) -> (dq, dk, dv)
@@ -24,7 +25,7 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_fwd_lse", "attn_bwd",
-    "attn_bwd_workspace_bytes", "attn_fwd_noalloc", "attn_prefill", "attn_decode",
+    "attn_bwd_workspace_bytes", "attn_fwd_noalloc", "qkv_rope_qknorm", "qkv_rope_qknorm_workspace_bytes", "attn_prefill", "attn_decode",
     "attn_decode_shared", "attn_decode_shared_workspace_bytes",
     "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
@@ -51,6 +52,9 @@ _SIGS = {
     "nc_attn_fwd_lse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp, _sz,
                              _vp]),
     "nc_attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_qkv_rope_qknorm_workspace_bytes": (_sz, [_i, _i, _i]),
+    "nc_qkv_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp,
+                                _sz, _vp]),
     "nc_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp]),
     "nc_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                          _vp, _sz, _vp]),
@@ -206,6 +210,42 @@ def rope_qknorm(q, k, *, rope_base: float = 10000.0, pos_offset: int = 0, q_out=
           float(rope_base), int(pos_offset), _dt(q), _ptr(ws), 0 if ws is None else ws.numel(),
           _stream(q))
     return q_out, k_out
+
+
+def qkv_rope_qknorm_workspace_bytes(T, D, dtype=torch.bfloat16) -> int:
+    dt = NC_F32 if dtype == torch.float32 else NC_BF16
+    return int(lib().nc_qkv_rope_qknorm_workspace_bytes(T, D, dt))
+
+
+def qkv_rope_qknorm(x, w_q, w_k, w_v, *, H: int, Hkv: int, rope_base: float = 10000.0,
+                    pos_offset: int = 0, q_out=None, k_out=None, v_out=None, workspace=None):
+    """x (B,T,C) and bias-free weights w_q (H*D,C), w_k, w_v (Hkv*D,C) ->
+    (norm(rope(x w_q^T)) (B,T,H,D), norm(rope(x w_k^T)) (B,T,Hkv,D), x w_v^T (B,T,Hkv,D))."""
+    x = _gpu(x, "x", 3)
+    w_q = _gpu(w_q, "w_q", 2, x.dtype)
+    w_k = _gpu(w_k, "w_k", 2, x.dtype)
+    w_v = _gpu(w_v, "w_v", 2, x.dtype)
+    B, T, C = x.shape
+    if w_q.shape[0] % H != 0:
+        raise ValueError("w_q rows must be H * D")
+    D = w_q.shape[0] // H
+    if (tuple(w_q.shape) != (H * D, C) or tuple(w_k.shape) != (Hkv * D, C)
+            or tuple(w_v.shape) != (Hkv * D, C)):
+        raise ValueError("projection weight shapes are inconsistent")
+    q_out = (torch.empty((B, T, H, D), dtype=x.dtype, device=x.device) if q_out is None
+             else _gpu(q_out, "q_out", 4, x.dtype))
+    k_out = (torch.empty((B, T, Hkv, D), dtype=x.dtype, device=x.device) if k_out is None
+             else _gpu(k_out, "k_out", 4, x.dtype))
+    v_out = (torch.empty((B, T, Hkv, D), dtype=x.dtype, device=x.device) if v_out is None
+             else _gpu(v_out, "v_out", 4, x.dtype))
+    if (tuple(q_out.shape) != (B, T, H, D) or tuple(k_out.shape) != (B, T, Hkv, D)
+            or tuple(v_out.shape) != (B, T, Hkv, D)):
+        raise ValueError("output shapes are inconsistent")
+    ws = _workspace(qkv_rope_qknorm_workspace_bytes(T, D, x.dtype), x.device, workspace)
+    _call("nc_qkv_rope_qknorm", _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(q_out), _ptr(k_out),
+          _ptr(v_out), B, T, C, H, Hkv, D, float(rope_base), int(pos_offset), _dt(x), _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(x))
+    return q_out, k_out, v_out
 
 
 def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: int = 0,

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnc_attn.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "rope.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "rope.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "noalloc.hip",
+           "qkv.hip"]
 
 ARCH = "gfx950"
 COMMON = [

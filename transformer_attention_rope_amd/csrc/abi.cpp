@@ -130,6 +130,39 @@ nc_status nc_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out,
   return ok();
 }
 
+// ------------------------------------------------------ qkv_rope_qknorm
+size_t nc_qkv_rope_qknorm_workspace_bytes(int T, int D, nc_dtype dtype) {
+  if (T < 1 || (D != 32 && D != 64 && D != 128) || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
+  return round_up(nc::attn_prep_table_bytes(T, D, dtype == NC_F32 ? nc::kF32 : nc::kBF16));
+}
+
+nc_status nc_qkv_rope_qknorm(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                             void* q_out, void* k_out, void* v_out, int B, int T, int C, int H,
+                             int Hkv, int D, double rope_base, int pos_offset, nc_dtype dt,
+                             void* ws, size_t ws_bytes, void* stream) {
+  nc_status s = check_common(B, T, H, Hkv, D, dt, "T");
+  if (s != NC_OK) return s;
+  if (C < 1) return fail(NC_ERR_INVALID, "C must be >= 1 (got %d)", C);
+  if (C % 64 != 0) return fail(NC_ERR_UNSUPPORTED, "C=%d is not a multiple of 64", C);
+  if (C > (1 << 20)) return fail(NC_ERR_UNSUPPORTED, "C=%d exceeds 2^20", C);
+  if ((s = check_rope(rope_base, pos_offset, T)) != NC_OK) return s;
+  const char* names[] = {"x", "w_q", "w_k", "w_v", "q_out", "k_out", "v_out"};
+  const void* ptrs[] = {x, w_q, w_k, w_v, q_out, k_out, v_out};
+  if ((s = check_ptrs(names, ptrs, 7)) != NC_OK) return s;
+  const size_t need = nc_qkv_rope_qknorm_workspace_bytes(T, D, dt);
+  if (ws == nullptr) return fail(NC_ERR_INVALID, "ws is NULL");
+  if (!aligned16(ws)) return fail(NC_ERR_INVALID, "ws is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(NC_ERR_INVALID, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+  const nc::Dtype d = dt == NC_F32 ? nc::kF32 : nc::kBF16;
+  hipError_t e = nc::launch_rope_table(ws, T, D, rope_base, pos_offset, d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  e = nc::launch_qkv_rope_qknorm(x, w_q, w_k, w_v, q_out, k_out, v_out, ws, B, T, C, H, Hkv, D, d,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "qkv launch");
+  return ok();
+}
+
 // ---------------------------------------------------------------- attn_fwd
 // Workspace: the (cos, sin) table of the T positions (fp16 pairs for bf16,
 // fp32 pairs for fp32), then k', then room for the partial rows of a launch

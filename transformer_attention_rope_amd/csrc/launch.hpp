@@ -22,6 +22,11 @@ hipError_t launch_attn_prep(const void* k, void* kp, void* tabq, int B, int T, i
                             int row0, const void* ve, const void* vgate, Dtype dt,
                             hipStream_t stream);
 
+// the (cos, sin) table of positions pos_offset .. pos_offset + T - 1 alone,
+// in the layout and type of attn_prep's (attn_prep_table_bytes(T, D, dt))
+hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset, Dtype dt,
+                             hipStream_t stream);
+
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,
                               int T, int H, int Hkv, int D, double rope_base, int pos_offset,
                               Dtype dt, hipStream_t stream);
@@ -68,5 +73,11 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
 // ---- once per device)
 size_t scratch_capacity();
 hipError_t scratch_address(void** out);
+
+// ---- fused bias-free q, k, v projection of x (B*T, C) with the RoPE and
+// ---- QK-norm epilogue on q and k; tab: launch_rope_table's table for T, D
+hipError_t launch_qkv_rope_qknorm(const void* x, const void* wq, const void* wk, const void* wv,
+                                  void* q, void* k, void* v, const void* tab, int B, int T, int C,
+                                  int H, int Hkv, int D, Dtype dt, hipStream_t stream);
 
 }  // namespace nc

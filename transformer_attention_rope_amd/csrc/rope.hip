@@ -45,6 +45,20 @@ namespace nc {
 // rows of 16 chunks against 96 per workgroup), one workgroup takes pp
 // consecutive positions whole, so the angle computation and the barrier are
 // paid once per pp positions.
+// (cos, sin) of p * theta_i, theta_i = base^(-2i/D): the angle is formed in
+// fp64 (theta as exp2(-(2i/D) log2 base)), reduced modulo 2*pi with a
+// two-constant Cody-Waite step, and evaluated with sincosf on [-pi, pi].
+__device__ __forceinline__ float2 rope_cs(long long p, int i, int D, double log2_base) {
+  const double theta = exp2(-(double)i / (D / 2) * log2_base);
+  const double a = (double)p * theta;
+  const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
+  double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
+  r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
+  float sn, c;
+  sincosf((float)r, &sn, &c);
+  return make_float2(c, sn);
+}
+
 constexpr int PREP_CPT = 6;  // 16-byte chunks per thread
 constexpr int PREP_MAXPP = 8;  // positions per workgroup at most
 
@@ -114,14 +128,9 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const Elem* __restrict__
   for (int idx = tid; idx < npos * (D / 2); idx += 256) {
     const int tl = idx / (D / 2), i = idx - tl * (D / 2);
     const int t = t0 + tl;
-    const double theta = exp2(-(double)i / (D / 2) * log2_base);
-    const double a = (double)(pos_offset + t) * theta;
-    const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
-    double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
-    r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
-    float sn, c;
-    sincosf((float)r, &sn, &c);
-    cs[tl][i] = make_float2(c, sn);
+    const float2 csv = rope_cs((long long)pos_offset + t, i, D, log2_base);
+    const float c = csv.x, sn = csv.y;
+    cs[tl][i] = csv;
     if (r0 == 0) {
       if constexpr (kBf)
         reinterpret_cast<uint32_t*>(tabq)[(size_t)t * (D / 2) + i] = pack_h2(c, sn);
@@ -288,16 +297,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_kernel(const Elem* q, const E
     if (ci < total) w[p] = ld16(isq[p] ? q + off[p] : k + off[p]);
   }
 
-  if (tid < D / 2) {
-    const double theta = exp2(-(double)tid / (D / 2) * log2_base);
-    const double a = (double)(pos_offset + t) * theta;
-    const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
-    double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
-    r = fma(-kq, 2.4492935982947064e-16, r);          // 2 pi, low part
-    float sn, c;
-    sincosf((float)r, &sn, &c);
-    cs[tid] = make_float2(c, sn);
-  }
+  if (tid < D / 2) cs[tid] = rope_cs((long long)pos_offset + t, tid, D, log2_base);
   __syncthreads();
 
 #pragma unroll
@@ -369,6 +369,33 @@ static hipError_t rope_qknorm_d(const void* q, const void* k, void* q_out, void*
                                            stream);
   return rope_qknorm_launch<D, float>(q, k, q_out, k_out, B, T, H, Hkv, rope_base, pos_offset,
                                       stream);
+}
+
+// The (cos, sin) table alone: tab[t][i] of positions pos_offset + t, t < T,
+// i < D/2, fp16 pairs in 32 bits (bf16) or float2 (fp32), as the input stage
+// writes it. One thread per entry.
+template <bool kBf>
+__global__ void __launch_bounds__(256) rope_table_kernel(void* __restrict__ tab, int T, int D,
+                                                          double log2_base, int pos_offset) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)T * (D / 2)) return;
+  const int t = (int)(idx / (D / 2)), i = (int)(idx % (D / 2));
+  const float2 c = rope_cs((long long)pos_offset + t, i, D, log2_base);
+  if constexpr (kBf) reinterpret_cast<uint32_t*>(tab)[idx] = pack_h2(c.x, c.y);
+  else reinterpret_cast<float2*>(tab)[idx] = c;
+}
+
+hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset, Dtype dt,
+                             hipStream_t stream) {
+  const long long n = (long long)T * (D / 2);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (dt == kBF16)
+    hipLaunchKernelGGL(rope_table_kernel<true>, dim3(grid), dim3(256), 0, stream, tab, T, D,
+                       std::log2(rope_base), pos_offset);
+  else
+    hipLaunchKernelGGL(rope_table_kernel<false>, dim3(grid), dim3(256), 0, stream, tab, T, D,
+                       std::log2(rope_base), pos_offset);
+  return hipGetLastError();
 }
 
 hipError_t launch_rope_qknorm(const void* q, const void* k, void* q_out, void* k_out, int B,

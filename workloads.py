@@ -236,3 +236,30 @@ def decode_bytes(seqlens, Hkv, D, W, H, elem_bytes=2) -> int:
     B = len(seqlens)
     small = (2 * B * H * D + 2 * B * Hkv * D) * elem_bytes
     return kv + small
+
+
+# Fused q, k, v projection before the attention: the d12 block (hidden 768,
+# 6 heads of 128) and the hidden-1024 GQA block (16 query and 4 K/V heads of
+# 64), over the same B x T tokens as the prefill workloads.
+QKV = {
+    "d12": dict(B=8, T=2048, C=768, H=6, Hkv=6, D=128),
+    "gqa": dict(B=16, T=2048, C=1024, H=16, Hkv=4, D=64),
+}
+
+
+def qkv_inputs(B, T, C, H, Hkv, D, seed=0, dtype=torch.bfloat16):
+    """x (B,T,C) ~ N(0,1), and bias-free weights w_q (H*D,C), w_k, w_v
+    (Hkv*D,C): N(0,1)/sqrt(C) drawn in fp32 (the master weights) and cast to
+    the compute type, as a linear layer does."""
+    base = SEED_BASE + 700 + 10 * seed
+    x = randn((B, T, C), base, dtype)
+    s = C ** -0.5
+    wq = (randn((H * D, C), base + 1, torch.float32) * s).to(dtype)
+    wk = (randn((Hkv * D, C), base + 2, torch.float32) * s).to(dtype)
+    wv = (randn((Hkv * D, C), base + 3, torch.float32) * s).to(dtype)
+    return x, wq, wk, wv
+
+
+def qkv_flops(B, T, C, H, Hkv, D) -> int:
+    """2 flops per multiply-add of the three projections."""
+    return 2 * B * T * C * (H + 2 * Hkv) * D
