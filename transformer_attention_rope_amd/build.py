@@ -9,6 +9,7 @@ this file, where the Python binding loads it.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,6 +50,28 @@ def _run(cmd):
     return err
 
 
+# The kernels keep every value in registers: no scratch (spill) memory. Besides
+# the cost, the attention tile loops wait for their LDS copies with a hand-
+# counted vmcnt that assumes the only vector-memory operations of a tile are
+# the copies and loads the code issues itself; spill traffic would add others.
+# The compiler's resource-usage remarks give each kernel's scratch bytes.
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def scratch_kernels(remarks: str):
+    """(kernel, scratch bytes per lane) for every kernel with scratch."""
+    bad, cur = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and cur is not None and int(m.group(1)) > 0:
+            bad.append((cur, int(m.group(1))))
+    return bad
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
@@ -56,13 +79,18 @@ def build(verbose: bool = False) -> str:
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", *REMARKS] if src.endswith(".hip") else []
         cmds.append([cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
-        for err in ex.map(_run, cmds):
-            if verbose and err.strip():
-                print(err, file=sys.stderr)
+        for src, err in zip(SOURCES, ex.map(_run, cmds)):
+            bad = scratch_kernels(err)
+            if bad:
+                raise RuntimeError(f"{src}: kernels with scratch (register spills): {bad}")
+            if verbose:
+                rest = "\n".join(l for l in err.splitlines() if "kernel-resource-usage" not in l)
+                if rest.strip():
+                    print(rest, file=sys.stderr)
     tmp = OUT + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, OUT)
