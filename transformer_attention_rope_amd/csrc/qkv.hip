@@ -18,10 +18,12 @@
 // Nothing round-trips through memory between the product and q', k'.
 //  * A workgroup owns 256 tokens (4 waves x 64) and one head (D output dims):
 //    every weight fragment read from LDS feeds two MFMAs (two 32-token blocks).
-//  * The x and weight tiles of each 64-column chunk of the input dimension go
+//  * The x and weight tiles of each 32-column chunk of the input dimension go
 //    memory -> LDS with 16-byte buffer-to-LDS copies (no registers),
-//    double-buffered, one barrier per chunk; rows of 128 bytes are XOR-
+//    double-buffered, one barrier per chunk; rows of 64 bytes are XOR-
 //    swizzled so the row-strided fragment reads spread over all LDS banks.
+//    48 KB of LDS and at most 256 registers per wave at D = 128, so two or
+//    three workgroups share a compute unit and hide each other's waits.
 //  * XCD-aware order: workgroup b runs on XCD b mod 8; XCD x takes a
 //    contiguous run of token blocks, and within it all heads of a token block
 //    back to back, so the block's x rows are read from HBM once into that
@@ -46,7 +48,9 @@ template <int D>
 struct QkvCfg {
   static constexpr int NW = 4, CB = 2;
   static constexpr int BT = 64 * NW;            // tokens per workgroup
-  static constexpr int KC = 64;                 // input columns per LDS chunk
+  static constexpr int KC = 32;                 // input columns per LDS chunk
+  static constexpr int CPRK = KC / 8;           // 16-byte chunks per tile row
+  static constexpr int RPS = 256 / (KC * 2);    // tile rows per 256-byte span of the LDS banks
   static constexpr int DB = D / 32;
   static constexpr int XT = BT * KC;            // bf16 elements of the x tile
   static constexpr int WT = D * KC;             // of the weight tile
@@ -55,8 +59,14 @@ struct QkvCfg {
   static constexpr int WCOPY = WT * 2 / 1024;   // per weight tile
 };
 
-// LDS chunk of logical 16-byte chunk c (0..7) of row r in a 128-byte-row tile
-__device__ __forceinline__ int q_chunk(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+// LDS chunk of logical 16-byte chunk c of row r in a tile of KC-column rows:
+// chunk c of row r sits at c ^ ((r / RPS) mod CPRK), so the rows of a 16-row
+// fragment read land on distinct 16-byte bank groups
+template <int D>
+__device__ __forceinline__ int q_chunk(int r, int c) {
+  using C = QkvCfg<D>;
+  return r * C::CPRK + (c ^ ((r / C::RPS) % C::CPRK));
+}
 
 // output head -> (matrix, head within it)
 struct HeadSel {
@@ -67,7 +77,7 @@ struct HeadSel {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256, 1) qkv_bf16_kernel(QkvArgs p) {
+__global__ void __launch_bounds__(256, 2) qkv_bf16_kernel(QkvArgs p) {
   using C = QkvCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -103,8 +113,9 @@ __global__ void __launch_bounds__(256, 1) qkv_bf16_kernel(QkvArgs p) {
       if (f % C::NW != wave) continue;
       const int ff = f < C::XCOPY ? f : f - C::XCOPY;
       const int e = ff * 64 + lane;
-      const int r = e >> 3, c = e & 7;
-      const uint32_t off = (uint32_t)r * rowb + (uint32_t)kc * (C::KC * 2) + (uint32_t)((c ^ ((r >> 1) & 7)) * 16);
+      const int r = e / C::CPRK, c = e % C::CPRK;
+      const uint32_t off = (uint32_t)r * rowb + (uint32_t)kc * (C::KC * 2) +
+                           (uint32_t)((c ^ ((r / C::RPS) % C::CPRK)) * 16);
       if (f < C::XCOPY) lds_copy16(rx, st + ff * 512, off);
       else lds_copy16(rw, st + C::XT + ff * 512, off);
     }
@@ -136,10 +147,10 @@ __global__ void __launch_bounds__(256, 1) qkv_bf16_kernel(QkvArgs p) {
       bf16x8_t xb[C::CB];
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
-        xb[cb] = *reinterpret_cast<const bf16x8_t*>(xs + q_chunk(wave * 64 + cb * 32 + n, 2 * s + hf) * 8);
+        xb[cb] = *reinterpret_cast<const bf16x8_t*>(xs + q_chunk<D>(wave * 64 + cb * 32 + n, 2 * s + hf) * 8);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8_t wa = *reinterpret_cast<const bf16x8_t*>(ws + q_chunk(db * 32 + n, 2 * s + hf) * 8);
+        const bf16x8_t wa = *reinterpret_cast<const bf16x8_t*>(ws + q_chunk<D>(db * 32 + n, 2 * s + hf) * 8);
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
           acc[db][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb[cb], acc[db][cb], 0, 0, 0);
