@@ -255,22 +255,35 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_bf16_kernel(BwdArgs p) {
 // =====================================================================
 // kernel A (bf16): dK, dV per (b, g, 128 keys)
 // =====================================================================
+// A step covers 64 query positions of one head as two 32-position sub-tiles,
+// whose score products are issued before either softmax: one sub-tile's
+// vector work then runs under the other's MFMAs (one wave per SIMD at
+// D = 128 leaves nothing else to hide it).
+template <int D>
+struct BwACfg {
+  using C = BwCfg<D>;
+  static constexpr int ROWT = 64 * D;             // bf16 elements of a 64-row tile
+  static constexpr int TRT = D * 64;              // of a transposed tile [D][64]
+  static constexpr int RCOPY = 64 * C::CPR / 64;  // 1 KB copies per row tile
+  static constexpr int TCOPY = D * 8 / 64;        // per transposed tile
+  static constexpr int STAGE = 2 * ROWT + 2 * TRT + 512;  // + stats: 2 x (lse2[32], delta[32])
+};
+// LDS chunk of logical chunk c (0..7) of row d of a [D][64] transposed tile
+__device__ __forceinline__ int tr64_chunk(int d, int c) { return d * 8 + (c ^ ((d >> 1) & 7)); }
+
 template <int D>
 __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_kv_bf16_kernel(BwdArgs p) {
   using C = BwCfg<D>;
-  // stage: Q rows, dO rows, Q^T, dO^T, then the stats block (lse2[32], delta[32])
-  constexpr int STAGE = 2 * C::ROWT + 2 * C::TRT + 512;  // bf16 elements
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  using A = BwACfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * A::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
 
-  const int nkb = (p.T + 127) / 128;
   const int per = p.B * p.Hkv;
   const int kb = (int)blockIdx.x / per;  // lower key blocks have more queries: first
   const int bg = (int)blockIdx.x % per;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
-  (void)nkb;
   const int j0 = kb * 128 + wave * 32;  // this wave's first key
   const int key = j0 + n;
 
@@ -297,131 +310,137 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_kv_bf16_kernel
       dka[db][r] = 0.f;
     }
 
-  // query tiles that see this workgroup's keys [kb*128, kb*128 + 127]
-  const int qt_lo = (kb * 128) / 32;
-  const int qt_hi = min(p.T - 1, kb * 128 + 127 + p.W - 1) / 32;
-  const int nqt = qt_hi - qt_lo + 1;
-  const int nsteps = p.G * nqt;
+  // query positions that see this workgroup's keys [kb*128, kb*128 + 127]:
+  // from kb*128 (a multiple of 64) to min(T, kb*128 + 127 + W) - 1, in steps of 64
+  const int q_lo = kb * 128;
+  const int q_hi = min(p.T - 1, kb * 128 + 127 + p.W - 1);
+  const int nq = (q_hi - q_lo) / 64 + 1;
+  const int nsteps = p.G * nq;
 
   const uint32_t qrow = (uint32_t)p.H * D * 2;
   auto issue = [&](int step, int buf) __attribute__((always_inline)) {
-    const int hh = g * p.G + step / nqt;
-    const int t0 = (qt_lo + step % nqt) * 32;
-    uint16_t* st = smem + buf * STAGE;
-    // row tiles: positions t0 .. t0 + 31 of head hh; past T reads zeros
+    const int hh = g * p.G + step / nq;
+    const int t0 = q_lo + (step % nq) * 64;
+    uint16_t* st = smem + buf * A::STAGE;
+    // row tiles: positions t0 .. t0 + 63 of head hh; past T reads zeros
     const size_t rbase = (((size_t)b * p.T + t0) * p.H + hh) * D;
     const uint32_t rrec = (uint32_t)((p.T - t0) * (size_t)qrow);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.qs + rbase, rrec);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const uint16_t*)p.dout + rbase, rrec);
+    // transposed tiles: t0 + 64 <= Tp (a multiple of 64), padded with zeros
     const size_t tbase = ((size_t)b * p.H + hh) * D * p.Tp + t0;
     const __amdgpu_buffer_rsrc_t rqt = make_rsrc(p.qst + tbase, 0x7fffffff);
     const __amdgpu_buffer_rsrc_t rdt = make_rsrc(p.dot + tbase, 0x7fffffff);
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(p.stats + (((size_t)b * p.H + hh) * (p.Tp / 32) + t0 / 32) * 64, 256);
-    constexpr int NI = 2 * C::RCOPY + 2 * C::TCOPY + 1;
+        make_rsrc(p.stats + (((size_t)b * p.H + hh) * (p.Tp / 32) + t0 / 32) * 64, 512);
+    constexpr int NI = 2 * A::RCOPY + 2 * A::TCOPY + 1;
 #pragma unroll
     for (int f = 0; f < NI; ++f) {
       if (f % 4 != wave) continue;
-      if (f < 2 * C::RCOPY) {
-        const int ff = f % C::RCOPY;
+      if (f < 2 * A::RCOPY) {
+        const int ff = f % A::RCOPY;
         const int e = ff * 64 + lane;
         const int r = e / C::CPR, c = e % C::CPR;
         const uint32_t off = (uint32_t)r * qrow + (uint32_t)((c ^ ((r / C::KSW) % C::CPR)) * 16);
-        lds_copy16(f < C::RCOPY ? rq : rd, st + (f < C::RCOPY ? 0 : C::ROWT) + ff * 512, off);
-      } else if (f < 2 * C::RCOPY + 2 * C::TCOPY) {
-        const int f2 = f - 2 * C::RCOPY;
-        const int ff = f2 % C::TCOPY;
+        lds_copy16(f < A::RCOPY ? rq : rd, st + (f < A::RCOPY ? 0 : A::ROWT) + ff * 512, off);
+      } else if (f < 2 * A::RCOPY + 2 * A::TCOPY) {
+        const int f2 = f - 2 * A::RCOPY;
+        const int ff = f2 % A::TCOPY;
         const int e = ff * 64 + lane;
-        const int d = e >> 2, c = e & 3;
-        const uint32_t off = (uint32_t)d * p.Tp * 2 + (uint32_t)((c ^ ((d >> 2) & 3)) * 16);
-        lds_copy16(f2 < C::TCOPY ? rqt : rdt,
-                   st + 2 * C::ROWT + (f2 < C::TCOPY ? 0 : C::TRT) + ff * 512, off);
+        const int d = e >> 3, c = e & 7;
+        const uint32_t off = (uint32_t)d * p.Tp * 2 + (uint32_t)((c ^ ((d >> 1) & 7)) * 16);
+        lds_copy16(f2 < A::TCOPY ? rqt : rdt,
+                   st + 2 * A::ROWT + (f2 < A::TCOPY ? 0 : A::TRT) + ff * 512, off);
       } else {
-        // lanes 0..15: the tile's 64 stats floats; the rest read nothing
-        lds_copy16(rs, st + 2 * C::ROWT + 2 * C::TRT, lane < 16 ? lane * 16 : 0xF0000000u);
+        // lanes 0..31: the 2 x 64 stats floats of the two sub-tiles; the rest read nothing
+        lds_copy16(rs, st + 2 * A::ROWT + 2 * A::TRT, lane < 32 ? lane * 16 : 0xF0000000u);
       }
     }
   };
 
-  // A-operand fragment reads
-  auto rowfrag = [&](const uint16_t* t, int s) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8_t*>(t + row_chunk<D>(n, 2 * s + hf) * 8);
+  // A-operand fragment reads: row tile (row 32 u + n) and transposed tile
+  // (row 32 db + n, sub-tile u's slots 32 u + 16 s2 + 8 hf ..)
+  auto rowfrag = [&](const uint16_t* t, int u, int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(t + row_chunk<D>(32 * u + n, 2 * s + hf) * 8);
   };
-  auto trfrag = [&](const uint16_t* t, int db, int s2) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8_t*>(t + tr_chunk(db * 32 + n, 2 * s2 + hf) * 8);
+  auto trfrag = [&](const uint16_t* t, int db, int u, int s2) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(t + tr64_chunk(db * 32 + n, 4 * u + 2 * s2 + hf) * 8);
   };
 
-  if (nsteps > 0) issue(0, 0);
+  issue(0, 0);
   wg_sync();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
-    const int t0 = (qt_lo + step % nqt) * 32;
-    // this wave's 32x32 block: the score work is skipped when no pair is
-    // visible; the dV, dK products then run on zero operands, so that the
-    // accumulators are updated on every path (a conditional update makes the
-    // compiler copy all of them between register files on every step)
-    const bool any = t0 + 31 >= j0 && t0 - (j0 + 31) < p.W && t0 < p.T;
-    const uint16_t* st = smem + buf * STAGE;
-    const uint16_t* qtt = st + 2 * C::ROWT;
-    const uint16_t* dtt = st + 2 * C::ROWT + C::TRT;
-    uint32_t pw[4][2], sw[4][2];
-    if (any) {
-      const uint16_t* qt = st;
-      const uint16_t* dt = st + C::ROWT;
-      const float* stat = reinterpret_cast<const float*>(st + 2 * C::ROWT + 2 * C::TRT);
-      f32x16_t sa, pa;
+    const int t0 = q_lo + (step % nq) * 64;
+    const uint16_t* st = smem + buf * A::STAGE;
+    const uint16_t* qt = st;
+    const uint16_t* dt = st + A::ROWT;
+    const uint16_t* qtt = st + 2 * A::ROWT;
+    const uint16_t* dtt = st + 2 * A::ROWT + A::TRT;
+    const float* stat = reinterpret_cast<const float*>(st + 2 * A::ROWT + 2 * A::TRT);
+    // Every product runs on every step (a conditional update of the dK, dV
+    // accumulators makes the compiler copy all of them between register
+    // files); sub-tiles the wave cannot see are masked to zero below.
+    f32x16_t sa[2], pa[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sa[r] = 0.f;
-        pa[r] = 0.f;
+        sa[u][r] = 0.f;
+        pa[u][r] = 0.f;
       }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(qt, s), kf[s], sa, 0, 0, 0);
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(dt, s), vf[s], pa, 0, 0, 0);
+        sa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(qt, u, s), kf[s], sa[u], 0, 0, 0);
+        pa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(dt, u, s), vf[s], pa[u], 0, 0, 0);
       }
-      // rows of the accumulators: query t0 + 8 (r / 4) + 4 hf + r % 4
-      const bool full = t0 >= j0 + 31 && t0 + 31 - j0 < p.W && t0 + 31 < p.T;
+    uint32_t pw[2][4][2], sw[2][4][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // register r holds query tq = t0 + 32 u + 8 (r / 4) + 4 hf + r % 4 against key `key`:
+      // visible iff 0 <= tq - key < W and tq < T, i.e. e = 8 (r / 4) + r % 4 lies in
+      // [key - base, min(key - base + W, T - base)), base = t0 + 32 u + 4 hf
+      const int base = t0 + 32 * u + 4 * hf;
+      const int lo = key - base;
+      const int hi = min(lo + p.W, p.T - base);
+      const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;  // empty past T
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(stat + 8 * r4 + 4 * hf);
-        const f32x4_t dl = *reinterpret_cast<const f32x4_t*>(stat + 32 + 8 * r4 + 4 * hf);
+        const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 8 * r4 + 4 * hf);
+        const f32x4_t dl = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 32 + 8 * r4 + 4 * hf);
         float pv[4], sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * r4 + i;
-          float pr = fast_exp2(sa[r] - l2[i]);
-          if (!full) {
-            const int tq = t0 + 8 * r4 + 4 * hf + i;
-            const int dl2 = tq - key;
-            if (!(dl2 >= 0 && dl2 < p.W && tq < p.T)) pr = 0.f;
-          }
+          const bool vis = (unsigned)(8 * r4 + i - lo) < span;
+          const float pr = vis ? fast_exp2(sa[u][r] - l2[i]) : 0.f;
           pv[i] = pr;
-          sv[i] = pr * (pa[r] - dl[i]);
+          sv[i] = pr * (pa[u][r] - dl[i]);
         }
-        pw[r4][0] = pack_bf2(pv[0], pv[1]);
-        pw[r4][1] = pack_bf2(pv[2], pv[3]);
-        sw[r4][0] = pack_bf2(sv[0], sv[1]);
-        sw[r4][1] = pack_bf2(sv[2], sv[3]);
-      }
-    } else {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) pw[r4][0] = pw[r4][1] = sw[r4][0] = sw[r4][1] = 0u;
-    }
-    // k-step s2 of the next products takes registers 8 s2 .. 8 s2 + 7
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8_t bp = __builtin_bit_cast(
-          bf16x8_t, u32x4_t{pw[2 * s2][0], pw[2 * s2][1], pw[2 * s2 + 1][0], pw[2 * s2 + 1][1]});
-      const bf16x8_t bs = __builtin_bit_cast(
-          bf16x8_t, u32x4_t{sw[2 * s2][0], sw[2 * s2][1], sw[2 * s2 + 1][0], sw[2 * s2 + 1][1]});
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(dtt, db, s2), bp, dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(qtt, db, s2), bs, dka[db], 0, 0, 0);
+        pw[u][r4][0] = pack_bf2(pv[0], pv[1]);
+        pw[u][r4][1] = pack_bf2(pv[2], pv[3]);
+        sw[u][r4][0] = pack_bf2(sv[0], sv[1]);
+        sw[u][r4][1] = pack_bf2(sv[2], sv[3]);
       }
     }
+    // k-step s2 of sub-tile u takes registers 8 s2 .. 8 s2 + 7
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8_t bp = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{pw[u][2 * s2][0], pw[u][2 * s2][1], pw[u][2 * s2 + 1][0], pw[u][2 * s2 + 1][1]});
+        const bf16x8_t bs = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{sw[u][2 * s2][0], sw[u][2 * s2][1], sw[u][2 * s2 + 1][0], sw[u][2 * s2 + 1][1]});
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(dtt, db, u, s2), bp, dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(qtt, db, u, s2), bs, dka[db], 0, 0, 0);
+        }
+      }
     wg_sync();
   }
 
@@ -752,7 +771,7 @@ struct BwdWs {
 };
 static BwdWs bwd_ws(int B, int T, int H, int Hkv, int D, Dtype dt) {
   const size_t el = dt == kBF16 ? 2 : 4;
-  const size_t Tp = (size_t)(T + 31) / 32 * 32;
+  const size_t Tp = (size_t)(T + 63) / 64 * 64;
   BwdWs w{};
   size_t o = 0;
   w.tab = o;
@@ -845,7 +864,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.Hkv = Hkv;
   a.G = H / Hkv;
   a.W = window;
-  a.Tp = (T + 31) / 32 * 32;
+  a.Tp = (T + 63) / 64 * 64;
   switch (D) {
     case 32: return attn_bwd_d<32>(a, dt, stream);
     case 64: return attn_bwd_d<64>(a, dt, stream);
