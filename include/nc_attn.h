@@ -70,14 +70,25 @@
 extern "C" {
 #endif
 
+/* The two enumerations span the whole int range (the _MIN_ and _MAX_
+ * members), so that any int a caller passes is a value of the type: unknown
+ * codes are reported as such (nc_status_string) or rejected (NC_ERR_INVALID),
+ * never undefined. Both are int-sized. */
 typedef enum {
   NC_OK = 0,
   NC_ERR_INVALID = 1,
   NC_ERR_UNSUPPORTED = 2,
-  NC_ERR_HIP = 3
+  NC_ERR_HIP = 3,
+  NC_STATUS_MIN_ = -2147483647 - 1,
+  NC_STATUS_MAX_ = 2147483647
 } nc_status;
 
-typedef enum { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
+typedef enum {
+  NC_BF16 = 0,
+  NC_F32 = 1,
+  NC_DTYPE_MIN_ = -2147483647 - 1,
+  NC_DTYPE_MAX_ = 2147483647
+} nc_dtype;
 
 /* RMSNorm epsilon inside QK-norm. */
 #define NC_QKNORM_EPS 1e-6

@@ -85,7 +85,9 @@ def _status_name(s):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree libnc_attn.so, or the build named by NC_ATTN_LIBRARY (another
+    build of the same sources, such as a host-sanitizer build of the ABI layer)."""
+    return os.environ.get("NC_ATTN_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def lib() -> ctypes.CDLL:
