@@ -48,8 +48,7 @@ namespace nc {
 // (cos, sin) of p * theta_i, theta_i = base^(-2i/D): the angle is formed in
 // fp64 (theta as exp2(-(2i/D) log2 base)), reduced modulo 2*pi with a
 // two-constant Cody-Waite step, and evaluated with sincosf on [-pi, pi].
-__device__ __forceinline__ float2 rope_cs(long long p, int i, int D, double log2_base) {
-  const double theta = exp2(-(double)i / (D / 2) * log2_base);
+__device__ __forceinline__ float2 rope_cs_theta(long long p, double theta) {
   const double a = (double)p * theta;
   const double kq = rint(a * 0.15915494309189535);  // a / (2 pi)
   double r = fma(-kq, 6.283185307179586, a);        // 2 pi, high part
@@ -57,6 +56,9 @@ __device__ __forceinline__ float2 rope_cs(long long p, int i, int D, double log2
   float sn, c;
   sincosf((float)r, &sn, &c);
   return make_float2(c, sn);
+}
+__device__ __forceinline__ float2 rope_cs(long long p, int i, int D, double log2_base) {
+  return rope_cs_theta(p, exp2(-(double)i / (D / 2) * log2_base));
 }
 
 constexpr int PREP_CPT = 6;  // 16-byte chunks per thread
@@ -373,21 +375,28 @@ static hipError_t rope_qknorm_d(const void* q, const void* k, void* q_out, void*
 
 // The (cos, sin) table alone: tab[t][i] of positions pos_offset + t, t < T,
 // i < D/2, fp16 pairs in 32 bits (bf16) or float2 (fp32), as the input stage
-// writes it. One thread per entry.
+// writes it. A thread takes one frequency i and kTabPos consecutive
+// positions, so theta_i (an fp64 exp2) is formed once per kTabPos entries;
+// the lanes of a wave write consecutive i of one position.
+constexpr int kTabPos = 8;
 template <bool kBf>
 __global__ void __launch_bounds__(256) rope_table_kernel(void* __restrict__ tab, int T, int D,
                                                           double log2_base, int pos_offset) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)T * (D / 2)) return;
-  const int t = (int)(idx / (D / 2)), i = (int)(idx % (D / 2));
-  const float2 c = rope_cs((long long)pos_offset + t, i, D, log2_base);
-  if constexpr (kBf) reinterpret_cast<uint32_t*>(tab)[idx] = pack_h2(c.x, c.y);
-  else reinterpret_cast<float2*>(tab)[idx] = c;
+  const int half = D / 2;
+  if (idx >= (long long)((T + kTabPos - 1) / kTabPos) * half) return;
+  const int i = (int)(idx % half), t0 = (int)(idx / half) * kTabPos;
+  const double theta = exp2(-(double)i / half * log2_base);
+  for (int t = t0; t < min(T, t0 + kTabPos); ++t) {
+    const float2 c = rope_cs_theta((long long)pos_offset + t, theta);
+    if constexpr (kBf) reinterpret_cast<uint32_t*>(tab)[(size_t)t * half + i] = pack_h2(c.x, c.y);
+    else reinterpret_cast<float2*>(tab)[(size_t)t * half + i] = c;
+  }
 }
 
 hipError_t launch_rope_table(void* tab, int T, int D, double rope_base, int pos_offset, Dtype dt,
                              hipStream_t stream) {
-  const long long n = (long long)T * (D / 2);
+  const long long n = (long long)((T + kTabPos - 1) / kTabPos) * (D / 2);
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (dt == kBF16)
     hipLaunchKernelGGL(rope_table_kernel<true>, dim3(grid), dim3(256), 0, stream, tab, T, D,
