@@ -485,12 +485,36 @@ def main():
             fl = wl.qkv_flops(B, T, C, H, Hkv, D)
             tf = fl / (ms * 1e-3) / 1e12
             nbytes = (B * T * C + (H + 2 * Hkv) * D * C + B * T * (H + 2 * Hkv) * D) * 2
+            # the attention block's input side end to end: x -> q', k', v -> o
+            # (causal, full window), attention read straight from q', k'
+            oo = torch.empty_like(qo)
+            wsn = nc.attn_fwd_normed_workspace_bytes(B, T, H, Hkv, D)
+            wsn = torch.empty(max(wsn, 1), dtype=torch.uint8, device=dev)
+
+            def nstep(i, qo=qo, ko=ko, vo=vo, oo=oo, wsn=wsn, T=T):
+                nc.attn_fwd_normed(qo, ko, vo, window=T, out=oo, workspace=wsn)
+
+            def bstep(i, qstep=qstep, nstep=nstep):
+                qstep(i)
+                nstep(i)
+
+            prime(f"normed_{name}", nstep)
+            ms_n = event_time_ms(nstep, K, torch)
+            prime(f"block_{name}", bstep)
+            ms_b = event_time_ms(bstep, K, torch)
+            fl_a = wl.prefill_flops(B, T, H, D, T)
             qkv[name] = {"shape": f"x (B={B}, T={T}, C={C}) -> q' (H={H}), k', v (Hkv={Hkv}), D={D}, bf16",
                          "us_per_call": round(ms * 1e3, 2), "TFLOP_per_s": round(tf, 1),
                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "GFLOP": round(fl / 1e9, 2),
-                         "algorithmic_bytes": nbytes}
-            del qsets, qo, ko, vo, wsq
-        qkv["flops"] = "2 per multiply-add of the three projections (table and epilogue not counted)"
+                         "algorithmic_bytes": nbytes,
+                         "attn_from_normed_us": round(ms_n * 1e3, 2),
+                         "attn_from_normed_frac_bf16_peak": round(
+                             fl_a / (ms_n * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "x_to_o_us": round(ms_b * 1e3, 2),
+                         "x_to_o_TFLOP_per_s": round((fl + fl_a) / (ms_b * 1e-3) / 1e12, 1)}
+            del qsets, qo, ko, vo, wsq, oo, wsn
+        qkv["flops"] = ("2 per multiply-add of the three projections (table and epilogue not counted); "
+                        "attention 4*D per unmasked pair, causal")
         if args.only == "qkv":
             print(json.dumps(qkv))
             return

@@ -94,7 +94,7 @@ typedef enum {
 #define NC_QKNORM_EPS 1e-6
 
 /* ABI version of this header (bumped on any signature change). */
-#define NC_ABI_VERSION 9
+#define NC_ABI_VERSION 10
 int nc_abi_version(void);
 
 /* Static description of a status code. Never NULL. */
@@ -181,6 +181,27 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o,
                       int B, int T, int H, int Hkv, int D, int window,
                       double rope_base, int pos_offset, nc_dtype dtype,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_attn_fwd_normed -- the attention of nc_attn_fwd from rows that are
+ * already rotated and normalised ([S5.4] scores, softmax, weighted sum; [S5.5]
+ * causal mask; [TBL] GQA and window), e.g. the outputs of nc_qkv_rope_qknorm
+ * or nc_rope_qknorm: no input stage runs, q' and k' are read as given.
+ *
+ *   q  (B, T, H,   D)  q' = norm(rope(q))
+ *   k  (B, T, Hkv, D)  k' = norm(rope(k))
+ *   v  (B, T, Hkv, D)  values
+ *   o  (B, T, H,   D)  o[b,t,h] = sum_j softmax_j(q'_t . k'_j / sqrt(D)) v_j over
+ *                      0 <= t - j < window
+ * The bound on stored rows of nc_attn_prefill applies to q and k (RMS at
+ * most 4; the library's own rows have RMS 1). Sizes and errors as for
+ * nc_attn_fwd. Workspace (nc_attn_fwd_normed_workspace_bytes, possibly 0):
+ * the partial rows of a launch cut into key-tile slices.
+ */
+size_t nc_attn_fwd_normed_workspace_bytes(int B, int T, int H, int Hkv, int D, nc_dtype dtype);
+nc_status nc_attn_fwd_normed(const void* q, const void* k, const void* v, void* o,
+                             int B, int T, int H, int Hkv, int D, int window, nc_dtype dtype,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * nc_attn_fwd_lse -- nc_attn_fwd that also writes the row log-sum-exp the

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = nc.lib()
-    assert L.nc_abi_version() == 9
+    assert L.nc_abi_version() == 10
     for s in range(4):
         assert L.nc_status_string(s)
     assert b"unknown" in L.nc_status_string(99)
@@ -315,3 +315,20 @@ def test_qkv_validation():
     assert call(wsb=8) == 1 and b"workspace" in L.nc_last_error()
     assert call(ws=None) == 1
     assert L.nc_qkv_rope_qknorm_workspace_bytes(2048, 128, 0) >= 2048 * 64 * 4
+
+
+def test_fwd_normed_validation():
+    L = nc.lib()
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, o=P, B=1, T=8, H=2, Hkv=2, D=64, W=8, dt=0, ws=P, wsb=1 << 20)
+        a.update(kw)
+        return L.nc_attn_fwd_normed(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["H"], a["Hkv"],
+                                    a["D"], a["W"], a["dt"], a["ws"], a["wsb"], None)
+    assert call(W=0) == 1 and b"window" in L.nc_last_error()
+    assert call(k=None) == 1 and b"k is NULL" in L.nc_last_error()
+    assert call(D=48) == 2 and b"head dim" in L.nc_last_error()
+    assert call(H=3) != 0
+    # a short sequence on many heads runs in one slice: no workspace at all
+    assert L.nc_attn_fwd_normed_workspace_bytes(1, 8, 2, 2, 64, 0) == 0
+    assert L.nc_attn_fwd_normed_workspace_bytes(0, 8, 2, 2, 64, 0) == 0

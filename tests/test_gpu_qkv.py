@@ -94,3 +94,69 @@ def test_qkv_full_size(name):
         _check_unit(qc[b:b + 1], rq, torch.bfloat16, f"q' b={b}")
         _check_unit(kc[b:b + 1], rk, torch.bfloat16, f"k' b={b}")
         _check_v(vc[b:b + 1], rv, torch.bfloat16)
+
+
+def _chain_max_bar(rv):
+    """Max-abs bar of the chained block. The forward's own bar (2e-2: q', k'
+    rounded to bf16 before the score products, P rounded for the value product,
+    o rounded once) plus the rounding of v, which the projection stores in bf16
+    while the oracle keeps it in fp64: |v~_j - v_j| <= 2^-9 |v_j| moves
+    o = sum_j p_j v_j by at most 2^-9 sum_j p_j |v_j| <= 2^-9 max |v|."""
+    return 2e-2 + 2.0 ** -9 * float(np.abs(rv).max())
+
+
+CHAIN = [
+    # B, T, C, H, Hkv, D, W, pos_offset
+    (2, 300, 128, 4, 2, 64, 100, 5),
+    (1, 257, 256, 6, 6, 128, 257, 0),
+    (1, 130, 64, 16, 1, 32, 40, 0),
+    (1, 2048, 256, 2, 2, 128, 2048, 0),  # few heads, long band: key-tile slices
+]
+
+
+@pytest.mark.parametrize("case", CHAIN, ids=lambda c: "B{}T{}C{}H{}Hkv{}D{}W{}off{}".format(*c))
+def test_projection_then_attention(case):
+    """x -> nc_qkv_rope_qknorm -> nc_attn_fwd_normed, the block's attention from
+    its input with q', k' written once and read once, against the oracle's
+    projection followed by its attention core on the same x and weights."""
+    B, T, C, H, Hkv, D, W, off = case
+    _say(f"projection then attention {case}")
+    (x, wq, wk, wv), (q, k, v) = _run(B, T, C, H, Hkv, D, off, torch.bfloat16, seed=T + 5)
+    o = nc.attn_fwd_normed(q, k, v, window=W)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_qknorm(x, wq, wk, wv, H, Hkv, 10000.0, off)
+    ro = oracle.attention_core(rq, rk, rv, W)
+    d = np.abs(_np(o) - ro)
+    print(f"[err] o: max {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    assert d.max() <= _chain_max_bar(rv) and d.mean() <= 2e-3
+
+
+def test_projection_then_attention_full_size_d12():
+    s = wl.QKV["d12"]
+    _say("projection then attention, d12 block, full size")
+    (x, wq, wk, wv), (q, k, v) = _run(s["B"], s["T"], s["C"], s["H"], s["Hkv"], s["D"], 0, torch.bfloat16,
+                                      seed=1)
+    o = nc.attn_fwd_normed(q, k, v, window=s["T"]).cpu()
+    mx, tot, bar = 0.0, 0.0, float("inf")
+    for b in range(s["B"]):
+        rq, rk, rv = oracle.qkv_rope_qknorm(x[b:b + 1], wq, wk, wv, s["H"], s["Hkv"])
+        d = np.abs(o[b:b + 1].double().numpy() - oracle.attention_core(rq, rk, rv, s["T"]))
+        mx, tot, bar = max(mx, float(d.max())), tot + float(d.sum()), min(bar, _chain_max_bar(rv))
+    print(f"[err] o whole tensor: max {mx:.3e} (bar {bar:.3e}) mean {tot / o.numel():.3e}", flush=True)
+    assert mx <= bar and tot / o.numel() <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_normed_equals_fwd_after_rope_qknorm(dtype):
+    """nc_rope_qknorm then nc_attn_fwd_normed against the oracle forward from raw q, k, v."""
+    _say(f"rope_qknorm then attn_fwd_normed {dtype}")
+    q, k, v = wl.small_prefill(2, 200, 8, 2, 64, seed=88, dtype=dtype)
+    qn, kn = nc.rope_qknorm(q.to(DEV), k.to(DEV), pos_offset=3)
+    o = nc.attn_fwd_normed(qn, kn, v.to(DEV), window=90)
+    torch.cuda.synchronize()
+    d = np.abs(_np(o) - oracle.attn_fwd(q, k, v, 90, 10000.0, 3))
+    print(f"[err] o: max {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    if dtype == torch.float32:
+        assert d.max() <= 1e-5
+    else:
+        assert d.max() <= 2e-2 and d.mean() <= 2e-3

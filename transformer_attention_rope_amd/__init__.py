@@ -10,6 +10,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
     qkv_rope_qknorm(x, w_q, w_k, w_v, H=..., Hkv=...)        -> (q', k', v)
     attn_fwd(q, k, v, window=..., rope_base=1e4, pos_offset=0) -> o
     attn_fwd_lse(q, k, v, window=...) -> (o, lse)
+    attn_fwd_normed(q', k', v, window=...) -> o      (q', k' already rotated, normalised)
     attn_bwd(q, k, v, o, dout, lse, window=...) -> (dq, dk, dv)
     attn_prep(k, ...) -> workspace;  attn_core(q, v, workspace, window=...) -> o
     attn_prefill(q, k, v, k_cache, v_cache, window=..., pos_offset=0, rope_base=1e4) -> o
@@ -25,7 +26,8 @@ import torch
 
 __all__ = [
     "NcError", "lib", "library_path", "rope_qknorm", "attn_fwd", "attn_fwd_lse", "attn_bwd",
-    "attn_bwd_workspace_bytes", "attn_fwd_noalloc", "qkv_rope_qknorm", "qkv_rope_qknorm_workspace_bytes", "attn_prefill", "attn_decode",
+    "attn_bwd_workspace_bytes", "attn_fwd_noalloc", "attn_fwd_normed", "attn_fwd_normed_workspace_bytes",
+    "qkv_rope_qknorm", "qkv_rope_qknorm_workspace_bytes", "attn_prefill", "attn_decode",
     "attn_decode_shared", "attn_decode_shared_workspace_bytes",
     "attn_prep", "attn_core", "decode_workspace",
     "attn_fwd_workspace_bytes", "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
@@ -55,6 +57,8 @@ _SIGS = {
     "nc_qkv_rope_qknorm_workspace_bytes": (_sz, [_i, _i, _i]),
     "nc_qkv_rope_qknorm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp,
                                 _sz, _vp]),
+    "nc_attn_fwd_normed_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "nc_attn_fwd_normed": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "nc_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i, _vp]),
     "nc_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _i,
                          _vp, _sz, _vp]),
@@ -271,6 +275,26 @@ def attn_fwd(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: in
     return o
 
 
+def attn_fwd_normed(q, k, v, *, window: int, out=None, workspace=None):
+    """Attention from q' (B,T,H,D) and k' (B,T,Hkv,D) that are already rotated and
+    normalised (e.g. qkv_rope_qknorm's outputs), and v -> o (B,T,H,D)."""
+    q = _gpu(q, "q", 4)
+    k = _gpu(k, "k", 4, q.dtype)
+    v = _gpu(v, "v", 4, q.dtype)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    o = torch.empty_like(q) if out is None else _gpu(out, "out", 4, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    dt = _dt(q)
+    ws = _workspace(int(lib().nc_attn_fwd_normed_workspace_bytes(B, T, H, Hkv, D, dt)), q.device, workspace)
+    _call("nc_attn_fwd_normed", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window), dt,
+          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
+    return o
+
+
 def attn_fwd_lse(q, k, v, *, window: int, rope_base: float = 10000.0, pos_offset: int = 0,
                  out=None, lse=None, workspace=None):
     """attn_fwd that also returns the row log-sum-exp lse (B,T,H) float32,
@@ -312,6 +336,11 @@ def attn_fwd_noalloc(q, k, v, *, window: int, out, rope_base: float = 10000.0, p
         _call("nc_attn_fwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, Hkv, D, int(window),
               float(rope_base), int(pos_offset), _dt(q), _stream(q))
     return o
+
+
+def attn_fwd_normed_workspace_bytes(B, T, H, Hkv, D, dtype=torch.bfloat16) -> int:
+    dt = NC_F32 if dtype == torch.float32 else NC_BF16
+    return int(lib().nc_attn_fwd_normed_workspace_bytes(B, T, H, Hkv, D, dt))
 
 
 def attn_bwd_workspace_bytes(B, T, H, Hkv, D, dtype=torch.bfloat16) -> int:

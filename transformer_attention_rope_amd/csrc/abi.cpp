@@ -255,6 +255,30 @@ nc_status nc_attn_fwd(const void* q, const void* k, const void* v, void* o, int 
   return nc_attn_core(q, v, o, B, T, H, Hkv, D, window, dt, ws, ws_bytes, stream);
 }
 
+size_t nc_attn_fwd_normed_workspace_bytes(int B, int T, int H, int Hkv, int D, nc_dtype dtype) {
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || D < 2 || (dtype != NC_BF16 && dtype != NC_F32)) return 0;
+  const size_t n = part_bytes(B, T, H, Hkv, D, T, dtype);
+  return n ? round_up(n) : 0;
+}
+
+nc_status nc_attn_fwd_normed(const void* q, const void* k, const void* v, void* o, int B, int T,
+                             int H, int Hkv, int D, int window, nc_dtype dt, void* ws,
+                             size_t ws_bytes, void* stream) {
+  nc_status s = check_fwd_sizes(B, T, H, Hkv, D, dt);
+  if (s != NC_OK) return s;
+  if (window < 1) return fail(NC_ERR_INVALID, "window must be >= 1 (got %d)", window);
+  const char* names[] = {"q", "k", "v", "o"};
+  const void* ptrs[] = {q, k, v, o};
+  if ((s = check_ptrs(names, ptrs, 4)) != NC_OK) return s;
+  const size_t need = nc_attn_fwd_normed_workspace_bytes(B, T, H, Hkv, D, dt);
+  if (need > 0 && (s = check_ws(ws, ws_bytes, need)) != NC_OK) return s;
+  // no table: the kernel takes the q rows as rotated and normalised
+  hipError_t e = nc::launch_attn_core(q, k, v, o, B, T, H, Hkv, D, window, nullptr, T, 0,
+                                      need > 0 ? ws : nullptr, need, to_dt(dt), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_core launch");
+  return ok();
+}
+
 nc_status nc_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int T, int H, int Hkv, int D, int window, double rope_base, int pos_offset,
                           nc_dtype dt, void* ws, size_t ws_bytes, void* stream) {

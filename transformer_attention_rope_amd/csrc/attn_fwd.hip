@@ -562,7 +562,9 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
         col_row(i * RPI + qr0, tr, hr);
         const int tc = tr < q_end ? tr : q_end - 1;
         qw[ii] = ld16(qg + ((size_t)(qo_row0 + tc) * p.H + hr) * D + qc * 8);
-        tq[ii] = ld16(tab + (size_t)(tc - p.kofs) * (D / 2) + qc * 4);
+        // no table: q rows arrive rotated and normalised; (cos, sin) = (1, 0)
+        tq[ii] = tab != nullptr ? ld16(tab + (size_t)(tc - p.kofs) * (D / 2) + qc * 4)
+                                : u32x4_t{0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u};
       }
       if (bt == 0) {
         gload(ic<0>{}, kt0);
@@ -583,7 +585,7 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
           ss += ye * ye + yo * yo;
         }
         ss = dpp_group_sum<C::CPR>(ss);
-        const float sc = p.qscale * rsq(ss * (1.0f / D) + kEps);
+        const float sc = tab != nullptr ? p.qscale * rsq(ss * (1.0f / D) + kEps) : p.qscale;
         u32x4_t w;
 #pragma unroll
         for (int m = 0; m < 4; ++m) w[m] = pack_bf2(x[2 * m] * sc, x[2 * m + 1] * sc);
@@ -1068,14 +1070,14 @@ __global__ void __launch_bounds__(128) attn_fwd_f32_kernel(FwdArgs p) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
-      const float2 cs = trow[i];
+      const float2 cs = p.tabq != nullptr ? trow[i] : make_float2(1.f, 0.f);
       const float xe = qrow[2 * i], xo = qrow[2 * i + 1];
       const float ye = xe * cs.x - xo * cs.y, yo = xe * cs.y + xo * cs.x;
       qv[2 * i] = ye;
       qv[2 * i + 1] = yo;
       ss += ye * ye + yo * yo;
     }
-    const float sc = p.qscale / sqrtf(ss * (1.0f / D) + kEps);
+    const float sc = p.tabq != nullptr ? p.qscale / sqrtf(ss * (1.0f / D) + kEps) : p.qscale;
 #pragma unroll
     for (int d = 0; d < D; ++d) qv[d] *= sc;
   }
