@@ -57,6 +57,7 @@ struct QkvCfg {
   static constexpr int STAGE = XT + WT;
   static constexpr int XCOPY = XT * 2 / 1024;   // 1 KB copies per x tile
   static constexpr int WCOPY = WT * 2 / 1024;   // per weight tile
+  static constexpr int CPWMAX = (XCOPY + WCOPY + NW - 1) / NW;  // copies per wave per chunk, at most
 };
 
 // LDS chunk of logical 16-byte chunk c of row r in a tile of KC-column rows:
@@ -105,18 +106,21 @@ __global__ void __launch_bounds__(256, 2) qkv_bf16_kernel(QkvArgs p) {
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(hs.w + (size_t)hs.hh * D * p.C, (uint32_t)D * rowb);
   const int nkc = p.C / C::KC;
 
+  // Copy f (x tile first, then the weight tile) is issued by wave f mod NW:
+  // this wave's copies are f = i*NW + wave, and only their offsets are kept.
   auto issue = [&](int kc, int buf) __attribute__((always_inline)) {
     uint16_t* st = smem + buf * C::STAGE;
-    constexpr int NI = C::XCOPY + C::WCOPY;
 #pragma unroll
-    for (int f = 0; f < NI; ++f) {
-      if (f % C::NW != wave) continue;
-      const int ff = f < C::XCOPY ? f : f - C::XCOPY;
+    for (int i = 0; i < C::CPWMAX; ++i) {
+      const int f = i * C::NW + wave;
+      if (f >= C::XCOPY + C::WCOPY) break;  // uniform
+      const bool isx = f < C::XCOPY;
+      const int ff = isx ? f : f - C::XCOPY;
       const int e = ff * 64 + lane;
       const int r = e / C::CPRK, c = e % C::CPRK;
       const uint32_t off = (uint32_t)r * rowb + (uint32_t)kc * (C::KC * 2) +
                            (uint32_t)((c ^ ((r / C::RPS) % C::CPRK)) * 16);
-      if (f < C::XCOPY) lds_copy16(rx, st + ff * 512, off);
+      if (isx) lds_copy16(rx, st + ff * 512, off);
       else lds_copy16(rw, st + C::XT + ff * 512, off);
     }
   };
