@@ -63,6 +63,10 @@ CASES = [
     (1, 257, 256, 16, 4, 64, 0, torch.bfloat16),
     (2, 129, 768, 6, 6, 128, 3, torch.bfloat16),
     (1, 513, 1024, 3, 1, 128, 0, torch.bfloat16),
+    # head counts that leave the last 128-row group part empty
+    (1, 90, 128, 3, 3, 64, 2, torch.bfloat16),
+    (2, 70, 192, 6, 3, 32, 0, torch.bfloat16),
+    (1, 40, 64, 5, 1, 64, 0, torch.bfloat16),
     (1, 64, 64, 2, 2, 32, 0, torch.float32),
     (2, 33, 128, 4, 2, 64, 7, torch.float32),
     (1, 20, 64, 2, 1, 128, 0, torch.float32),

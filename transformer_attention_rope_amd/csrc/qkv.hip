@@ -16,18 +16,21 @@
 // works on fp32 accumulators in registers: the RoPE pairs (d, d+1) sit in the
 // same lane, and the RMSNorm sum needs one cross-lane add (lanes n, n + 32).
 // Nothing round-trips through memory between the product and q', k'.
-//  * A workgroup owns 256 tokens (4 waves x 64) and one head (D output dims):
-//    every weight fragment read from LDS feeds two MFMAs (two 32-token blocks).
+//  * A workgroup owns 256 tokens (4 waves x 64) and a group of 128 weight
+//    rows: one head at D = 128, two at 64, four at 32 (a group stays inside
+//    one of the three matrices; rows of heads past its last read as zero and
+//    are not stored). Every weight fragment read from LDS feeds two MFMAs
+//    (two 32-token blocks).
 //  * The x and weight tiles of each 32-column chunk of the input dimension go
 //    memory -> LDS with 16-byte buffer-to-LDS copies (no registers),
 //    double-buffered, one barrier per chunk; rows of 64 bytes are XOR-
 //    swizzled so the row-strided fragment reads spread over all LDS banks.
-//    48 KB of LDS and at most 256 registers per wave at D = 128, so two or
-//    three workgroups share a compute unit and hide each other's waits.
+//    48 KB of LDS and 168 registers per wave, so three workgroups share a
+//    compute unit and hide each other's waits.
 //  * XCD-aware order: workgroup b runs on XCD b mod 8; XCD x takes a
-//    contiguous run of token blocks, and within it all heads of a token block
-//    back to back, so the block's x rows are read from HBM once into that
-//    XCD's L2 and served from there to every head.
+//    contiguous run of token blocks, and within it all row groups of a token
+//    block back to back, so the block's x rows are read from HBM once into
+//    that XCD's L2 and served from there to every group.
 // fp32 path: exact fp32 arithmetic on the vector ALUs, one thread per
 // (token, head), not a performance path.
 #include "device_common.hpp"
@@ -42,18 +45,22 @@ struct QkvArgs {
   const void* tab;                 // (cos, sin) of positions pos_offset + t: [T][D/2]
   int M, T, C, H, Hkv, NH;         // NH = H + 2 Hkv output heads
   int ntb, tbx;                    // token blocks; token blocks per XCD
+  int ngq, ngk, NG;                // row groups of w_q, of w_k (= of w_v); NG = ngq + 2 ngk
 };
 
 template <int D>
 struct QkvCfg {
   static constexpr int NW = 4, CB = 2;
   static constexpr int BT = 64 * NW;            // tokens per workgroup
+  static constexpr int RG = 128;                // weight rows (output columns) per workgroup
+  static constexpr int HPG = RG / D;            // heads per row group
   static constexpr int KC = 32;                 // input columns per LDS chunk
   static constexpr int CPRK = KC / 8;           // 16-byte chunks per tile row
   static constexpr int RPS = 256 / (KC * 2);    // tile rows per 256-byte span of the LDS banks
-  static constexpr int DB = D / 32;
+  static constexpr int DB = RG / 32;            // 32-row blocks of the group
+  static constexpr int DBH = D / 32;            // of one head
   static constexpr int XT = BT * KC;            // bf16 elements of the x tile
-  static constexpr int WT = D * KC;             // of the weight tile
+  static constexpr int WT = RG * KC;            // of the weight tile
   static constexpr int STAGE = XT + WT;
   static constexpr int XCOPY = XT * 2 / 1024;   // 1 KB copies per x tile
   static constexpr int WCOPY = WT * 2 / 1024;   // per weight tile
@@ -69,7 +76,7 @@ __device__ __forceinline__ int q_chunk(int r, int c) {
   return r * C::CPRK + (c ^ ((r / C::RPS) % C::CPRK));
 }
 
-// output head -> (matrix, head within it)
+// row group -> (matrix, its head count, first head of the group)
 struct HeadSel {
   const uint16_t* w;
   uint16_t* out;
@@ -87,23 +94,25 @@ __global__ void __launch_bounds__(256, 2) qkv_bf16_kernel(QkvArgs p) {
 
   const int bx = (int)blockIdx.x;
   const int xcd = bx & 7, l = bx >> 3;
-  const int tb = xcd * p.tbx + l / p.NH;
-  const int head = l % p.NH;
-  if (tb >= p.ntb || l / p.NH >= p.tbx) return;  // padding of the XCD ranges
+  const int tb = xcd * p.tbx + l / p.NG;
+  const int grp = l % p.NG;
+  if (tb >= p.ntb || l / p.NG >= p.tbx) return;  // padding of the XCD ranges
 
   HeadSel hs;
-  if (head < p.H) {
-    hs = {(const uint16_t*)p.wq, (uint16_t*)p.q, p.H, head, true};
-  } else if (head < p.H + p.Hkv) {
-    hs = {(const uint16_t*)p.wk, (uint16_t*)p.k, p.Hkv, head - p.H, true};
+  if (grp < p.ngq) {
+    hs = {(const uint16_t*)p.wq, (uint16_t*)p.q, p.H, grp * C::HPG, true};
+  } else if (grp < p.ngq + p.ngk) {
+    hs = {(const uint16_t*)p.wk, (uint16_t*)p.k, p.Hkv, (grp - p.ngq) * C::HPG, true};
   } else {
-    hs = {(const uint16_t*)p.wv, (uint16_t*)p.v, p.Hkv, head - p.H - p.Hkv, false};
+    hs = {(const uint16_t*)p.wv, (uint16_t*)p.v, p.Hkv, (grp - p.ngq - p.ngk) * C::HPG, false};
   }
   const int m0 = tb * C::BT;
   const uint32_t rowb = (uint32_t)p.C * 2;
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc((const uint16_t*)p.x + (size_t)m0 * p.C, (uint32_t)min(C::BT, p.M - m0) * rowb);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(hs.w + (size_t)hs.hh * D * p.C, (uint32_t)D * rowb);
+  // rows of heads past the matrix's last read as zero, and are not stored
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(hs.w + (size_t)hs.hh * D * p.C,
+                                              (uint32_t)(min(C::HPG, hs.nh - hs.hh) * D) * rowb);
   const int nkc = p.C / C::KC;
 
   // Copy f (x tile first, then the weight tile) is issued by wave f mod NW:
@@ -163,52 +172,58 @@ __global__ void __launch_bounds__(256, 2) qkv_bf16_kernel(QkvArgs p) {
     sync();
   }
 
-  // ---- epilogue: the lane holds token m, dims 32 db + 8 (r/4) + 4 hf + r%4
+  // ---- epilogue: the lane holds token m, group rows 32 db + 8 (r/4) + 4 hf + r%4;
+  // head j of the group is row blocks db = j*DBH .. j*DBH + DBH-1
   const uint32_t* tab = (const uint32_t*)p.tab;
 #pragma unroll
   for (int cb = 0; cb < C::CB; ++cb) {
     const int m = m0 + wave * 64 + cb * 32 + n;
     const bool valid = m < p.M;
     const int t = (valid ? m : 0) % p.T;
-    uint16_t* orow = hs.out + ((size_t)(valid ? m : 0) * hs.nh + hs.hh) * D;
-    float y[C::DB][16];
-    if (hs.rot) {
-      float ss = 0.f;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int j = 0; j < C::HPG; ++j) {
+      if (hs.hh + j >= hs.nh) break;  // uniform
+      uint16_t* orow = hs.out + ((size_t)(valid ? m : 0) * hs.nh + hs.hh + j) * D;
+      float y[C::DBH][16];
+      if (hs.rot) {
+        float ss = 0.f;
+#pragma unroll
+        for (int dh = 0; dh < C::DBH; ++dh)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = dh * 32 + 8 * r4 + 4 * hf;
+            const u32x2_t cs = *reinterpret_cast<const u32x2_t*>(tab + (size_t)t * (D / 2) + d / 2);
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              const float xe = acc[j * C::DBH + dh][cb][4 * r4 + 2 * mm];
+              const float xo = acc[j * C::DBH + dh][cb][4 * r4 + 2 * mm + 1];
+              const float c = h_lo(cs[mm]), sn = h_hi(cs[mm]);
+              const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+              y[dh][4 * r4 + 2 * mm] = ye;
+              y[dh][4 * r4 + 2 * mm + 1] = yo;
+              ss += ye * ye + yo * yo;
+            }
+          }
+        const float rn = rsq(sum_halves(ss) * (1.0f / D) + kEps);
+#pragma unroll
+        for (int dh = 0; dh < C::DBH; ++dh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[dh][r] *= rn;
+      } else {
+#pragma unroll
+        for (int dh = 0; dh < C::DBH; ++dh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[dh][r] = acc[j * C::DBH + dh][cb][r];
+      }
+#pragma unroll
+      for (int dh = 0; dh < C::DBH; ++dh)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = db * 32 + 8 * r4 + 4 * hf;
-          const u32x2_t cs = *reinterpret_cast<const u32x2_t*>(tab + (size_t)t * (D / 2) + d / 2);
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const float xe = acc[db][cb][4 * r4 + 2 * mm], xo = acc[db][cb][4 * r4 + 2 * mm + 1];
-            const float c = h_lo(cs[mm]), sn = h_hi(cs[mm]);
-            const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
-            y[db][4 * r4 + 2 * mm] = ye;
-            y[db][4 * r4 + 2 * mm + 1] = yo;
-            ss += ye * ye + yo * yo;
-          }
+          const u32x2_t w = {pack_bf2(y[dh][4 * r4], y[dh][4 * r4 + 1]),
+                             pack_bf2(y[dh][4 * r4 + 2], y[dh][4 * r4 + 3])};
+          if (valid) st8(orow + dh * 32 + 8 * r4 + 4 * hf, w);
         }
-      const float rn = rsq(sum_halves(ss) * (1.0f / D) + kEps);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[db][r] *= rn;
-    } else {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[db][r] = acc[db][cb][r];
     }
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const u32x2_t w = {pack_bf2(y[db][4 * r4], y[db][4 * r4 + 1]),
-                           pack_bf2(y[db][4 * r4 + 2], y[db][4 * r4 + 3])};
-        if (valid) st8(orow + db * 32 + 8 * r4 + 4 * hf, w);
-      }
   }
 }
 
@@ -261,7 +276,10 @@ static hipError_t qkv_d(QkvArgs a, Dtype dt, hipStream_t stream) {
     using C = QkvCfg<D>;
     a.ntb = (a.M + C::BT - 1) / C::BT;
     a.tbx = (a.ntb + 7) / 8;
-    const long long grid = 8LL * a.tbx * a.NH;
+    a.ngq = (a.H + C::HPG - 1) / C::HPG;
+    a.ngk = (a.Hkv + C::HPG - 1) / C::HPG;
+    a.NG = a.ngq + 2 * a.ngk;
+    const long long grid = 8LL * a.tbx * a.NG;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(qkv_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
