@@ -42,6 +42,8 @@
 //
 // fp32 path: exact fp32 arithmetic on the vector ALUs, one thread per key
 // row (dK, dV) or query row (dQ), not a performance path.
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -252,6 +254,19 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_bf16_kernel(BwdArgs p) {
   }
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at
+// compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void bw_static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void bw_static_for(F&& f) {
+  bw_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int I>
+using bw_ic = std::integral_constant<int, I>;
+
 // =====================================================================
 // kernel A (bf16): dK, dV per (b, g, 128 keys)
 // =====================================================================
@@ -382,6 +397,40 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_kv_bf16_kernel
     // Every product runs on every step (a conditional update of the dK, dV
     // accumulators makes the compiler copy all of them between register
     // files); sub-tiles the wave cannot see are masked to zero below.
+    //
+    // The step is written out as its NM MFMAs in a fixed order, with a
+    // scheduling barrier after each: the scores S, dP of sub-tile 0, those of
+    // sub-tile 1, then dV, dK of sub-tile 0 and of sub-tile 1. MFMA m takes
+    // fragment m, read from LDS LA MFMAs earlier, so no MFMA waits on its own
+    // read. The softmax of sub-tile 0 (8 units) sits between the score MFMAs
+    // of sub-tile 1, that of sub-tile 1 between the dV, dK MFMAs of sub-tile
+    // 0: vector work that no nearby MFMA depends on, issued while the matrix
+    // unit is busy.
+    constexpr int NSU = 2 * C::KS;   // score MFMAs per sub-tile (S and dP per k-step)
+    constexpr int NGU = 4 * C::DB;   // dV, dK MFMAs per sub-tile
+    constexpr int NM = 2 * NSU + 2 * NGU;
+    constexpr int LA = D == 128 ? 8 : 3;  // fragment look-ahead in MFMAs
+    f32x4_t l2v[2][4], dlv[2][4];
+    int lo[2];
+    unsigned span[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // register r holds query tq = t0 + 32 u + 8 (r / 4) + 4 hf + r % 4 against key `key`:
+      // visible iff 0 <= tq - key < W and tq < T, i.e. e = 8 (r / 4) + r % 4 lies in
+      // [key - base, min(key - base + W, T - base)), base = t0 + 32 u + 4 hf
+      const int base = t0 + 32 * u + 4 * hf;
+      lo[u] = key - base;
+      const int hi = min(lo[u] + p.W, p.T - base);
+      span[u] = hi > lo[u] ? (unsigned)(hi - lo[u]) : 0u;  // empty past T
+    }
+    // the sub-tile's lse and delta, read a few MFMAs before its softmax
+    auto load_stats = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        l2v[u][r4] = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 8 * r4 + 4 * hf);
+        dlv[u][r4] = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 32 + 8 * r4 + 4 * hf);
+      }
+    };
     f32x16_t sa[2], pa[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -390,57 +439,73 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_kv_bf16_kernel
         sa[u][r] = 0.f;
         pa[u][r] = 0.f;
       }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        sa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(qt, u, s), kf[s], sa[u], 0, 0, 0);
-        pa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowfrag(dt, u, s), vf[s], pa[u], 0, 0, 0);
-      }
     uint32_t pw[2][4][2], sw[2][4][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // register r holds query tq = t0 + 32 u + 8 (r / 4) + 4 hf + r % 4 against key `key`:
-      // visible iff 0 <= tq - key < W and tq < T, i.e. e = 8 (r / 4) + r % 4 lies in
-      // [key - base, min(key - base + W, T - base)), base = t0 + 32 u + 4 hf
-      const int base = t0 + 32 * u + 4 * hf;
-      const int lo = key - base;
-      const int hi = min(lo + p.W, p.T - base);
-      const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;  // empty past T
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 8 * r4 + 4 * hf);
-        const f32x4_t dl = *reinterpret_cast<const f32x4_t*>(stat + 64 * u + 32 + 8 * r4 + 4 * hf);
-        float pv[4], sv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * r4 + i;
-          const bool vis = (unsigned)(8 * r4 + i - lo) < span;
-          const float pr = vis ? fast_exp2(sa[u][r] - l2[i]) : 0.f;
-          pv[i] = pr;
-          sv[i] = pr * (pa[u][r] - dl[i]);
-        }
-        pw[u][r4][0] = pack_bf2(pv[0], pv[1]);
-        pw[u][r4][1] = pack_bf2(pv[2], pv[3]);
-        sw[u][r4][0] = pack_bf2(sv[0], sv[1]);
-        sw[u][r4][1] = pack_bf2(sv[2], sv[3]);
+    // fragment of MFMA m
+    auto frag = [&](auto mc) __attribute__((always_inline)) -> bf16x8_t {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 2 * NSU) {
+        constexpr int u = m / NSU, s = (m % NSU) / 2;
+        return rowfrag((m & 1) ? dt : qt, u, s);
+      } else {
+        constexpr int mm = m - 2 * NSU, u = mm / NGU, r = mm % NGU;
+        constexpr int s2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+        return trfrag((r & 1) ? qtt : dtt, db, u, s2);
       }
-    }
-    // k-step s2 of sub-tile u takes registers 8 s2 .. 8 s2 + 7
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t bp = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{pw[u][2 * s2][0], pw[u][2 * s2][1], pw[u][2 * s2 + 1][0], pw[u][2 * s2 + 1][1]});
-        const bf16x8_t bs = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{sw[u][2 * s2][0], sw[u][2 * s2][1], sw[u][2 * s2 + 1][0], sw[u][2 * s2 + 1][1]});
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(dtt, db, u, s2), bp, dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(qtt, db, u, s2), bs, dka[db], 0, 0, 0);
+    };
+    auto mfma = [&](auto mc, const bf16x8_t& a) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 2 * NSU) {
+        constexpr int u = m / NSU, s = (m % NSU) / 2;
+        if constexpr (m & 1) pa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[s], pa[u], 0, 0, 0);
+        else sa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], sa[u], 0, 0, 0);
+      } else {
+        constexpr int mm = m - 2 * NSU, u = mm / NGU, r = mm % NGU;
+        constexpr int s2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+        // k-step s2 of sub-tile u takes registers 8 s2 .. 8 s2 + 7
+        if constexpr (r & 1) {
+          const bf16x8_t bs = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{sw[u][2 * s2][0], sw[u][2 * s2][1], sw[u][2 * s2 + 1][0], sw[u][2 * s2 + 1][1]});
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, dka[db], 0, 0, 0);
+        } else {
+          const bf16x8_t bp = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{pw[u][2 * s2][0], pw[u][2 * s2][1], pw[u][2 * s2 + 1][0], pw[u][2 * s2 + 1][1]});
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, dva[db], 0, 0, 0);
         }
       }
+    };
+    // softmax unit k of sub-tile u: registers 4 r4 + 2 h, 4 r4 + 2 h + 1 (r4 = k / 2, h = k % 2)
+    auto unit = [&](int u, int k) __attribute__((always_inline)) {
+      const int r4 = k >> 1, h = k & 1;
+      float pv[2], sv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = 2 * h + j, r = 4 * r4 + i;
+        const bool vis = (unsigned)(8 * r4 + i - lo[u]) < span[u];
+        const float pr = vis ? fast_exp2(sa[u][r] - l2v[u][r4][i]) : 0.f;
+        pv[j] = pr;
+        sv[j] = pr * (pa[u][r] - dlv[u][r4][i]);
+      }
+      pw[u][r4][h] = pack_bf2(pv[0], pv[1]);
+      sw[u][r4][h] = pack_bf2(sv[0], sv[1]);
+    };
+    bf16x8_t fr[NM];
+    bw_static_for<LA>([&](auto jc) { fr[decltype(jc)::value] = frag(jc); });
+    __builtin_amdgcn_sched_barrier(0);
+    bw_static_for<NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m + LA < NM) fr[m + LA] = frag(bw_ic<m + LA>{});
+      mfma(mc, fr[m]);
+      if constexpr (m == NSU - 3) load_stats(0);
+      if constexpr (m == 2 * NSU - 3) load_stats(1);
+      // sub-tile 0's units after score MFMAs NSU+1 .. 2 NSU-1, sub-tile 1's
+      // after dV, dK MFMAs 2 NSU+1 .. 2 NSU+NGU-1
+      bw_static_for<8>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (m == NSU + 1 + k * (NSU - 1) / 8) unit(0, k);
+        if constexpr (m == 2 * NSU + 1 + k * (NGU - 1) / 8) unit(1, k);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
     wg_sync();
   }
 
