@@ -113,7 +113,9 @@ struct BfCfg {
   // per compute unit) or 8 (two per SIMD)
   static constexpr int NW = NW_;
   static constexpr int NT = 64 * NW;       // threads per workgroup
-  static constexpr int CB = NW == 8 ? 1 : 2;  // 32-column blocks per wave
+  // 32-column blocks per wave: one with two waves per SIMD (8 waves, or 4
+  // waves at D <= 64 with two workgroups per compute unit), else two
+  static constexpr int CB = (NW == 8 || (NW == 4 && D <= 64)) ? 1 : 2;
   static constexpr int NC = 32 * CB * NW;  // query columns per workgroup: 256, or 128 with 2 waves
   static constexpr int BN = 64;            // keys per tile
   static constexpr int KS = D / 16;        // MFMA k-steps of K Q^T
@@ -999,12 +1001,15 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
 
 template <int D, int NW>
 constexpr bool fwd_has_lse() { return !(D == 128 && NW == 4); }
+// resident bf16 workgroups per compute unit
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_kernel(FwdArgs p) {
+constexpr int wg_per_cu() { return (NW == 2 || (NW == 4 && D <= 64)) ? 2 : 1; }
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, (wg_per_cu<D, NW>())) attn_fwd_bf16_kernel(FwdArgs p) {
   attn_fwd_bf16_body<D, NW, false, fwd_has_lse<D, NW>() ? kLseIfGiven : kLseNone>(p);
 }
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bf16_split_kernel(FwdArgs p) {
+__global__ void __launch_bounds__(64 * NW, (wg_per_cu<D, NW>())) attn_fwd_bf16_split_kernel(FwdArgs p) {
   attn_fwd_bf16_body<D, NW, true>(p);
 }
 
@@ -1157,16 +1162,18 @@ static int ilog2(int x) {
 // (measured on the d12 W = 512 layer: 48.8 us against 52.4). With the full
 // causal band the longest query tiles set the time either way and the
 // 4-wave form, which splits the staging work four ways, is faster (61.0 us
-// against 64.4).
+// against 64.4). At D <= 64 the narrow band likewise takes 4 waves of one
+// column block (128 columns) with two workgroups per unit: GQA W = 512
+// layer 103 -> 97 us, while the full band stays with 8 waves (167 us
+// against 168-172).
 template <int D>
 constexpr int fwd_waves() { return D == 128 ? 4 : 8; }
 // (For a chunk whose queries start at position kofs, the window bites for
 // most of its query tiles once it is at most kofs + T/2: 2W <= T + 2 kofs.
 // Measured on a 512-token d12 chunk at offset 1536 with W = 512: 30.2 us with
 // two waves against 32.1.)
-template <int D>
 static bool fwd_narrow(int T, int W, int kofs) {
-  return D == 128 && 2 * (long long)W <= T + 2 * (long long)kofs;
+  return 2 * (long long)W <= T + 2 * (long long)kofs;
 }
 
 // Key-tile slices. A launch of fewer workgroups than half the device holds
@@ -1183,8 +1190,6 @@ static bool fwd_narrow(int T, int W, int kofs) {
 constexpr int kCUs = 256;  // compute units of the MI355X
 constexpr int kMinSliceTiles = 8;
 constexpr int kMaxSplits = 16;
-template <int NW>
-constexpr int wg_per_cu() { return NW == 2 ? 2 : 1; }  // resident bf16 workgroups per unit
 
 static int fwd_splits(long long grid, int cap, int tiles) {
   if (grid <= 0 || 2 * grid > cap || tiles < 3 * kMinSliceTiles) return 1;
@@ -1229,7 +1234,7 @@ static int plan_bf16(FwdArgs& a, int hpw, size_t part_bytes) {
   a.bp_log2 = ilog2(C::NC / hpw);
   a.nqt = (a.T + (1 << a.bp_log2) - 1) >> a.bp_log2;
   if (!fwd_can_split<D, NW>() || a.part == nullptr) return 1;
-  const int ns = fwd_splits((long long)a.nqt * a.B * a.ngroups, kCUs * wg_per_cu<NW>(), max_key_tiles(a));
+  const int ns = fwd_splits((long long)a.nqt * a.B * a.ngroups, kCUs * wg_per_cu<D, NW>(), max_key_tiles(a));
   return part_bytes_for(ns, a.rows, D) > part_bytes ? 1 : ns;
 }
 
@@ -1271,8 +1276,9 @@ static size_t part_bytes_d(int B, int T, int H, int Hkv, int Tk) {
   const int tiles = Tk / 64 + 2;  // at least the key tiles of any query tile
   int ns = 1;
   if constexpr (fwd_can_split<D, fwd_waves<D>()>())
-    ns = fwd_splits(bf16_grid<D, fwd_waves<D>()>(B, T, H, hpw), kCUs * wg_per_cu<fwd_waves<D>()>(), tiles);
-  if constexpr (D == 128) ns = max(ns, fwd_splits(bf16_grid<D, 2>(B, T, H, hpw), kCUs * wg_per_cu<2>(), tiles));
+    ns = fwd_splits(bf16_grid<D, fwd_waves<D>()>(B, T, H, hpw), kCUs * wg_per_cu<D, fwd_waves<D>()>(), tiles);
+  constexpr int NWN = D == 128 ? 2 : 4;  // the narrow-band form
+  ns = max(ns, fwd_splits(bf16_grid<D, NWN>(B, T, H, hpw), kCUs * wg_per_cu<D, NWN>(), tiles));
   return part_bytes_for(ns, (long long)B * T * H, D);
 }
 
@@ -1287,8 +1293,11 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, size_t part_bytes, hipStream_t
       // the narrow band, a launch that is cut into slices, or one that writes
       // the row log-sum-exp
       FwdArgs a2 = a;
-      if (fwd_narrow<D>(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
+      if (fwd_narrow(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
         return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
+    } else {
+      // the narrow band: 4 waves of one column block, two workgroups per unit
+      if (fwd_narrow(a.T, a.W, a.kofs)) return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
     }
     return launch_bf16<D, fwd_waves<D>()>(a, hpw, part_bytes, stream);
   } else {
