@@ -1,6 +1,8 @@
 // Prefill attention forward for gfx950: GQA, causal sliding-window band,
 // softmax, bf16 MFMA; q is rotated and normalised in the kernel, k arrives
-// rotated and normalised from the input stage (attn_prep_kernel).
+// rotated and normalised from the input stage (attn_prep_kernel). Without a
+// (cos, sin) table (nc_attn_fwd_normed) q arrives rotated and normalised too
+// and the kernel only scales it.
 //
 // What is computed ("从文本到聊天模型" (onehacker.top) §5.4 score = Q K^T,
 // softmax, weighted sum of V; §5.5 causal mask; §5.6 RoPE;
@@ -51,8 +53,10 @@
 //    MFMAs execute, so this work hides under the matrix pipe. Tiles crossing
 //    a wave's band edge are masked in place; tiles outside it are skipped
 //    (the wave only stages). Heaviest query tiles are dispatched first.
-//  * At D = 128 a band of at most half the sequence runs a 2-wave form (128
-//    columns, two workgroups per compute unit), whose tiles are half as long.
+//  * A band of at most half the sequence runs a form of 128 columns with two
+//    workgroups per compute unit (2 waves at D = 128, 4 waves of one column
+//    block at D <= 64): one workgroup's loads at its start and stores at its
+//    end overlap the other's tiles.
 //  * A launch too small to fill the device (a chunk at a large offset, a batch
 //    of one) cuts each query tile's key tiles into slices run by separate
 //    workgroups; each writes unnormalised fp32 rows and row sums, which the
