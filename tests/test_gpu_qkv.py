@@ -164,3 +164,40 @@ def test_normed_equals_fwd_after_rope_qknorm(dtype):
         assert d.max() <= 1e-5
     else:
         assert d.max() <= 2e-2 and d.mean() <= 2e-3
+
+
+NORMED = [
+    # B, T, H, Hkv, D, W, dtype
+    (1, 1, 2, 1, 32, 1, torch.bfloat16),
+    (2, 257, 8, 1, 64, 100, torch.bfloat16),
+    (1, 130, 16, 1, 32, 7, torch.bfloat16),
+    (1, 300, 4, 2, 128, 300, torch.bfloat16),
+    (3, 77, 6, 6, 128, 64, torch.bfloat16),
+    (1, 65, 4, 2, 64, 30, torch.float32),
+    (2, 40, 2, 2, 128, 40, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", NORMED, ids=lambda c: "B{}T{}H{}Hkv{}D{}W{}-{}".format(
+    *c[:6], str(c[6]).split(".")[-1]))
+def test_attn_fwd_normed_small(case):
+    """nc_attn_fwd_normed on rows that are already rotated and normalised (the
+    oracle's q', k' rounded to the element type) against oracle.attention_core of
+    the same rounded rows: one query, one-key windows, 16 query heads per K/V
+    head, every D, fp32."""
+    B, T, H, Hkv, D, W, dtype = case
+    _say(f"attn_fwd_normed {case}")
+    q, k, v = wl.small_prefill(B, T, H, Hkv, D, seed=T + 3 * H + D, dtype=torch.float32)
+    qn, kn = oracle.rope_qknorm(q, k, 10000.0, 0)
+    qn = torch.from_numpy(qn).to(dtype)
+    kn = torch.from_numpy(kn).to(dtype)
+    v = v.to(dtype)
+    o = nc.attn_fwd_normed(qn.to(DEV), kn.to(DEV), v.to(DEV), window=W)
+    torch.cuda.synchronize()
+    ref = oracle.attention_core(qn.double().numpy(), kn.double().numpy(), v.double().numpy(), W)
+    d = np.abs(_np(o) - ref)
+    print(f"[err] o: max {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    if dtype == torch.float32:
+        assert d.max() <= 1e-5
+    else:
+        assert d.max() <= 2e-2 and d.mean() <= 2e-3
