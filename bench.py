@@ -713,7 +713,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(kern_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(),
-                     "kernel": "attn_fwd_bf16_kernel<128, 4>",
+                     "kernel": "attn_fwd_bf16_kernel<128, 8>",
                      "kernel_us": round(out["kern_ms"] * 1e3, 2),
                      "flops_per_launch": flops},
         "device_copy_GB_per_s": round(copy_gbs, 1) if copy_gbs else None,

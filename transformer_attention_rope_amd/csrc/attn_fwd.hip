@@ -21,11 +21,12 @@
 //    than re-rotating and re-normalising it on each visit.
 //  * A workgroup owns 256 query columns: hpw query heads of one K/V group
 //    times 256/hpw consecutive positions, so a K/V tile staged in LDS serves
-//    every head of the group. At D = 128 it is 4 waves (one per SIMD), each
-//    owning 64 columns as two 32-column blocks, so every K or V fragment read
-//    from LDS feeds two MFMAs and the accumulators may use the whole register
-//    file (VGPRs and AGPRs). At D <= 64 it is 8 waves (two per SIMD) of one
-//    32-column block each: one wave's MFMAs run while the other waits.
+//    every head of the group. It is 8 waves (two per SIMD) of one 32-column
+//    block each: one wave's MFMAs run while the other waits. At D = 128 that
+//    fits the 256 registers of a wave with a fragment look-ahead of 3 MFMAs
+//    and without the log-sum-exp output (calls that ask for it run the
+//    2-wave form below, whose waves own two 32-column blocks each and may
+//    use the whole register file, VGPRs and AGPRs).
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    the K tile is the A operand (LDS), the rotated, normalised, pre-scaled Q
 //    is the B operand (registers, loaded once). In the accumulator layout a
@@ -206,7 +207,9 @@ template <int D, int NW, int KIND, bool STAGE, int H>
 struct TileSched {
   using C = BfCfg<D, NW>;
   // fragment look-ahead in MFMAs: 8 fragments either way
-  static constexpr int MAXS = 24, MAXL = 16, LAM = C::CB == 2 ? 16 : 6;
+  // (3 at D = 128 with one column block: the 8-wave form fits 256 registers
+  // only with so short a look-ahead)
+  static constexpr int MAXS = 24, MAXL = 16, LAM = C::CB == 2 ? 16 : (D == 128 ? 3 : 6);
   static constexpr int diag(int cb) { return C::CB == 2 ? cb : H; }
   static constexpr bool present(int rb, int cb) {
     return !((KIND == kDiag && rb > diag(cb)) || (KIND == kWin && rb < diag(cb)));
@@ -355,7 +358,7 @@ struct TileSchedTab {
 // of its query tile's key tiles and writes unnormalised fp32 partial rows
 // (attn_split_combine_kernel adds them up); without, it writes o itself.
 // LSE: whether the epilogue writes the row log-sum-exp (kLseNone: never;
-// kLseIfGiven: when p.lse is set). The 4-wave D = 128 body has no registers
+// kLseIfGiven: when p.lse is set). The 8-wave D = 128 body has no registers
 // to spare for it (with the write it spills), so it is built without; forward
 // calls that ask for the log-sum-exp at D = 128 run the 2-wave body.
 enum { kLseNone = 0, kLseIfGiven = 1 };
@@ -1004,7 +1007,7 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const FwdArgs& p) {
 }
 
 template <int D, int NW>
-constexpr bool fwd_has_lse() { return !(D == 128 && NW == 4); }
+constexpr bool fwd_has_lse() { return !(D == 128 && NW >= 4); }
 // resident bf16 workgroups per compute unit
 template <int D, int NW>
 constexpr int wg_per_cu() { return (NW == 2 || (NW == 4 && D <= 64)) ? 2 : 1; }
@@ -1154,10 +1157,11 @@ static int ilog2(int x) {
   return r;
 }
 
-// Waves per workgroup of the bf16 kernel: two per SIMD where one column
-// block per wave fits the halved register budget (D <= 64; measured 8-16%
-// faster than one wave per SIMD on the GQA D=64 layers), one per SIMD at
-// D = 128, whose accumulators need more than 256 registers per wave. At
+// Waves per workgroup of the bf16 kernel: 8, two per SIMD with one column
+// block each (at D <= 64 measured 8-16% faster than one wave per SIMD with
+// two blocks on the GQA layers; at D = 128, with a fragment look-ahead of 3
+// MFMAs so that it fits 256 registers, 58.8-59.6 us against 62.4-62.7 us on
+// the d12 L layer, and the step 68.9-69.1 against 72.9-73.6 us). At
 // D = 128 a window of at most half the sequence gives every query tile about
 // the same number of key tiles, and 1.5 tiles of 256 columns per compute unit
 // leave half the units idle for the last round; there two workgroups of 2
@@ -1165,13 +1169,13 @@ static int ilog2(int x) {
 // large, and one workgroup's prologue and epilogue overlap the other's tiles
 // (measured on the d12 W = 512 layer: 48.8 us against 52.4). With the full
 // causal band the longest query tiles set the time either way and the
-// 4-wave form, which splits the staging work four ways, is faster (61.0 us
-// against 64.4). At D <= 64 the narrow band likewise takes 4 waves of one
+// 256-column form is faster (one wave per SIMD: 61.0 us against 64.4). At
+// D <= 64 the narrow band likewise takes 4 waves of one
 // column block (128 columns) with two workgroups per unit: GQA W = 512
 // layer 103 -> 97 us, while the full band stays with 8 waves (167 us
 // against 168-172).
 template <int D>
-constexpr int fwd_waves() { return D == 128 ? 4 : 8; }
+constexpr int fwd_waves() { return 8; }
 // (For a chunk whose queries start at position kofs, the window bites for
 // most of its query tiles once it is at most kofs + T/2: 2W <= T + 2 kofs.
 // Measured on a 512-token d12 chunk at offset 1536 with W = 512: 30.2 us with
@@ -1218,11 +1222,10 @@ static size_t part_bytes_for(int nsplit, long long rows, int D) {
   return nsplit > 1 ? (size_t)nsplit * (size_t)rows * (size_t)(D + 1) * sizeof(float) : 0;
 }
 
-// The 4-wave D = 128 body with the slice bookkeeping does not fit its
-// registers; sliced D = 128 launches use the 2-wave kernel, which does (two
-// workgroups of half the columns per compute unit).
+// Sliced D = 128 launches use the 2-wave kernel (two workgroups of half the
+// columns per compute unit), whose registers hold the slice bookkeeping.
 template <int D, int NW>
-constexpr bool fwd_can_split() { return !(D == 128 && NW == 4); }
+constexpr bool fwd_can_split() { return !(D == 128 && NW >= 4); }
 
 template <int D, int NW>
 static long long bf16_grid(int B, int T, int H, int hpw) {
