@@ -54,10 +54,12 @@
 //    MFMAs execute, so this work hides under the matrix pipe. Tiles crossing
 //    a wave's band edge are masked in place; tiles outside it are skipped
 //    (the wave only stages). Heaviest query tiles are dispatched first.
-//  * A band of at most half the sequence runs a form of 128 columns with two
-//    workgroups per compute unit (2 waves at D = 128, 4 waves of one column
-//    block at D <= 64): one workgroup's loads at its start and stores at its
-//    end overlap the other's tiles.
+//  * A band of at most half the sequence runs a form of 128 columns, 4 waves
+//    of one column block, with two workgroups per compute unit: two waves per
+//    SIMD again, and one workgroup's loads at its start and stores at its end
+//    overlap the other's tiles. At D = 128 a 2-wave form (two column blocks
+//    per wave, one wave per SIMD) serves the calls that ask for the row
+//    log-sum-exp and the launches cut into key-tile slices.
 //  * A launch too small to fill the device (a chunk at a large offset, a batch
 //    of one) cuts each query tile's key tiles into slices run by separate
 //    workgroups; each writes unnormalised fp32 rows and row sums, which the
@@ -119,8 +121,8 @@ struct BfCfg {
   static constexpr int NW = NW_;
   static constexpr int NT = 64 * NW;       // threads per workgroup
   // 32-column blocks per wave: one with two waves per SIMD (8 waves, or 4
-  // waves at D <= 64 with two workgroups per compute unit), else two
-  static constexpr int CB = (NW == 8 || (NW == 4 && D <= 64)) ? 1 : 2;
+  // waves with two workgroups per compute unit), two in the 2-wave form
+  static constexpr int CB = (NW == 8 || NW == 4) ? 1 : 2;
   static constexpr int NC = 32 * CB * NW;  // query columns per workgroup: 256, or 128 with 2 waves
   static constexpr int BN = 64;            // keys per tile
   static constexpr int KS = D / 16;        // MFMA k-steps of K Q^T
@@ -151,7 +153,7 @@ struct BfCfg {
   // workgroup (two V micro-blocks per thread): there one set (tile kt+1
   // loads at the start of tile kt and is transposed at its end) keeps the
   // kernel within its registers without spills
-  static constexpr int VS = ((NW == 8 || NW == 2) && D == 128) ? 1 : 2;
+  static constexpr int VS = D == 128 ? 1 : 2;
   static constexpr int NQL = QR * CPR / 64;  // 16-byte row chunks per lane for them
 };
 
@@ -1010,7 +1012,7 @@ template <int D, int NW>
 constexpr bool fwd_has_lse() { return !(D == 128 && NW >= 4); }
 // resident bf16 workgroups per compute unit
 template <int D, int NW>
-constexpr int wg_per_cu() { return (NW == 2 || (NW == 4 && D <= 64)) ? 2 : 1; }
+constexpr int wg_per_cu() { return (NW == 2 || NW == 4) ? 2 : 1; }
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW, (wg_per_cu<D, NW>())) attn_fwd_bf16_kernel(FwdArgs p) {
   attn_fwd_bf16_body<D, NW, false, fwd_has_lse<D, NW>() ? kLseIfGiven : kLseNone>(p);
@@ -1157,23 +1159,20 @@ static int ilog2(int x) {
   return r;
 }
 
-// Waves per workgroup of the bf16 kernel: 8, two per SIMD with one column
-// block each (at D <= 64 measured 8-16% faster than one wave per SIMD with
-// two blocks on the GQA layers; at D = 128, with a fragment look-ahead of 3
-// MFMAs so that it fits 256 registers, 58.8-59.6 us against 62.4-62.7 us on
-// the d12 L layer, and the step 68.9-69.1 against 72.9-73.6 us). At
-// D = 128 a window of at most half the sequence gives every query tile about
-// the same number of key tiles, and 1.5 tiles of 256 columns per compute unit
-// leave half the units idle for the last round; there two workgroups of 2
-// waves (128 columns each) share a unit instead, so the tiles are half as
-// large, and one workgroup's prologue and epilogue overlap the other's tiles
-// (measured on the d12 W = 512 layer: 48.8 us against 52.4). With the full
-// causal band the longest query tiles set the time either way and the
-// 256-column form is faster (one wave per SIMD: 61.0 us against 64.4). At
-// D <= 64 the narrow band likewise takes 4 waves of one
-// column block (128 columns) with two workgroups per unit: GQA W = 512
-// layer 103 -> 97 us, while the full band stays with 8 waves (167 us
-// against 168-172).
+// Waves per workgroup of the bf16 kernel. The full band: 8 waves, two per
+// SIMD, one 32-column block each (256 columns, one workgroup per compute
+// unit). Against one wave per SIMD with two blocks: 8-16% faster on the GQA
+// D = 64 layers; at D = 128, with a fragment look-ahead of 3 MFMAs so that it
+// fits 256 registers, 58.8-59.6 us against 62.4-62.7 us on the d12 L layer.
+// A window of at most half the sequence gives every query tile about the
+// same number of key tiles, and 1.5 tiles of 256 columns per compute unit
+// leave half the units idle for the last round. There 4 waves of one block
+// (128 columns) run as two workgroups per unit, again two waves per SIMD, and
+// one workgroup's loads and stores overlap the other's tiles: d12 W = 512
+// layer 49.1 -> 37.1 us (against the 2-wave form, one wave per SIMD with two
+// blocks, which stays at D = 128 for log-sum-exp calls and sliced launches);
+// GQA W = 512 layer 103 -> 97 us. On the full band the 256-column form is
+// faster (GQA W = 2048: 167 us against 168-172).
 template <int D>
 constexpr int fwd_waves() { return 8; }
 // (For a chunk whose queries start at position kofs, the window bites for
@@ -1300,8 +1299,9 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, size_t part_bytes, hipStream_t
       // the narrow band, a launch that is cut into slices, or one that writes
       // the row log-sum-exp
       FwdArgs a2 = a;
-      if (fwd_narrow(a.T, a.W, a.kofs) || plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
+      if (plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
         return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
+      if (fwd_narrow(a.T, a.W, a.kofs)) return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
     } else {
       // the narrow band: 4 waves of one column block, two workgroups per unit
       if (fwd_narrow(a.T, a.W, a.kofs)) return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
