@@ -59,7 +59,7 @@
 //    SIMD again, and one workgroup's loads at its start and stores at its end
 //    overlap the other's tiles. At D = 128 a 2-wave form (two column blocks
 //    per wave, one wave per SIMD) serves the calls that ask for the row
-//    log-sum-exp and the launches cut into key-tile slices.
+//    log-sum-exp.
 //  * A launch too small to fill the device (a chunk at a large offset, a batch
 //    of one) cuts each query tile's key tiles into slices run by separate
 //    workgroups; each writes unnormalised fp32 rows and row sums, which the
@@ -1170,7 +1170,7 @@ static int ilog2(int x) {
 // (128 columns) run as two workgroups per unit, again two waves per SIMD, and
 // one workgroup's loads and stores overlap the other's tiles: d12 W = 512
 // layer 49.1 -> 37.1 us (against the 2-wave form, one wave per SIMD with two
-// blocks, which stays at D = 128 for log-sum-exp calls and sliced launches);
+// blocks, which stays at D = 128 for log-sum-exp calls);
 // GQA W = 512 layer 103 -> 97 us. On the full band the 256-column form is
 // faster (GQA W = 2048: 167 us against 168-172).
 template <int D>
@@ -1221,10 +1221,13 @@ static size_t part_bytes_for(int nsplit, long long rows, int D) {
   return nsplit > 1 ? (size_t)nsplit * (size_t)rows * (size_t)(D + 1) * sizeof(float) : 0;
 }
 
-// Sliced D = 128 launches use the 2-wave kernel (two workgroups of half the
-// columns per compute unit), whose registers hold the slice bookkeeping.
+// Sliced D = 128 launches use the 4-wave kernel of 128 columns (two
+// workgroups per compute unit), whose registers hold the slice bookkeeping
+// (242 VGPRs; the 8-wave one is at 256 without it). Measured on the d12
+// 512-token chunk at offset 1536, W = 2048: 48.5 us against 53.9 with the
+// 2-wave form.
 template <int D, int NW>
-constexpr bool fwd_can_split() { return !(D == 128 && NW >= 4); }
+constexpr bool fwd_can_split() { return !(D == 128 && NW == 8); }
 
 template <int D, int NW>
 static long long bf16_grid(int B, int T, int H, int hpw) {
@@ -1283,7 +1286,7 @@ static size_t part_bytes_d(int B, int T, int H, int Hkv, int Tk) {
   int ns = 1;
   if constexpr (fwd_can_split<D, fwd_waves<D>()>())
     ns = fwd_splits(bf16_grid<D, fwd_waves<D>()>(B, T, H, hpw), kCUs * wg_per_cu<D, fwd_waves<D>()>(), tiles);
-  constexpr int NWN = D == 128 ? 2 : 4;  // the narrow-band form
+  constexpr int NWN = 4;  // the narrow-band and sliced form
   ns = max(ns, fwd_splits(bf16_grid<D, NWN>(B, T, H, hpw), kCUs * wg_per_cu<D, NWN>(), tiles));
   return part_bytes_for(ns, (long long)B * T * H, D);
 }
@@ -1296,12 +1299,12 @@ static hipError_t attn_fwd_d(FwdArgs a, Dtype dt, size_t part_bytes, hipStream_t
     a.hpw_log2 = ilog2(hpw);
     a.ngroups = a.H / hpw;
     if constexpr (D == 128) {
-      // the narrow band, a launch that is cut into slices, or one that writes
-      // the row log-sum-exp
+      // the row log-sum-exp: the 2-wave form; the narrow band or a launch cut
+      // into slices: 4 waves of one column block, two workgroups per unit
       FwdArgs a2 = a;
-      if (plan_bf16<D, 2>(a2, hpw, part_bytes) > 1 || a.lse != nullptr)
-        return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
-      if (fwd_narrow(a.T, a.W, a.kofs)) return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
+      if (a.lse != nullptr) return launch_bf16<D, 2>(a, hpw, part_bytes, stream);
+      if (fwd_narrow(a.T, a.W, a.kofs) || plan_bf16<D, 4>(a2, hpw, part_bytes) > 1)
+        return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
     } else {
       // the narrow band: 4 waves of one column block, two workgroups per unit
       if (fwd_narrow(a.T, a.W, a.kofs)) return launch_bf16<D, 4>(a, hpw, part_bytes, stream);
