@@ -234,6 +234,43 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
 
+  const int h0 = g * a.G + hg * GP;
+  const int nh = min(GP, a.G - hg * GP);
+  const Elem* qg = (const Elem*)a.q;
+
+  // ---- the rows this wave rotates (q heads, then the appended k row, one
+  // ---- wave per row, one (even, odd) pair per lane; D/2 <= 64) and v_new:
+  // ---- loaded first, before the sequence length, so that their latency
+  // ---- overlaps that load, the K/V loads and the angles (every chunk of the
+  // ---- sequence loads the appended row; the one that owns it uses it)
+  constexpr int MAXR = (GP + 1 + 3) / 4;  // rows per wave
+  float rx[MAXR][2];
+  Elem vn0 = Elem(0), vn1 = Elem(0);
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int r = wave + 4 * j;
+    rx[j][0] = rx[j][1] = 0.f;
+    if (r <= nh && lane < D / 2) {
+      const bool is_k = r == nh;
+      const Elem* src = is_k ? (const Elem*)a.k_new + ((size_t)b * a.Hkv + g) * D
+                             : qg + ((size_t)b * a.H + h0 + r) * D;
+      rx[j][0] = TR::to_f(src[2 * lane]);
+      rx[j][1] = TR::to_f(src[2 * lane + 1]);
+      if (is_k) {
+        const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
+        vn0 = vsrc[2 * lane];
+        vn1 = vsrc[2 * lane + 1];
+        if (a.ve_new != nullptr) {  // value embedding: v_new + gate * ve_new, rounded once
+          const Elem* esrc = (const Elem*)a.ve_new + ((size_t)b * a.Hkv + g) * D;
+          const float gg = TR::to_f(((const Elem*)a.ve_gate)[(size_t)b * a.Hkv + g]);
+          vn0 = TR::from_f(TR::to_f(vn0) + gg * TR::to_f(esrc[2 * lane]));
+          vn1 = TR::from_f(TR::to_f(vn1) + gg * TR::to_f(esrc[2 * lane + 1]));
+        }
+      }
+    }
+  }
+
+
   const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], Lp, a.Tmax);
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
@@ -241,6 +278,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   const int nch = dec_chunks(L, lo, SH && a.cut ? Lp : 0, SH ? a.Cp : a.C, a.C, split, ks0, ks1);
   if (split >= nch) return;
   const bool owns_new = ks1 == L;
+  const int nrows = nh + (owns_new ? 1 : 0);
+  const float qscale = kLog2e / sqrtf((float)D);
   // The chunk's keys as one or two segments [sk0, sk1): with a shared prompt
   // and no cut, a chunk spanning the prompt's end runs its prompt rows first,
   // then (second segment) the sequence's own rows, with one softmax state.
@@ -248,10 +287,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   int sk0 = ks0, sk1 = two_seg ? Lp : ks1;
   bool in_prompt = SH && ks0 < Lp;  // the segment's rows are the shared prompt's
 
-  const int h0 = g * a.G + hg * GP;
-  const int nh = min(GP, a.G - hg * GP);
-
-  const Elem* qg = (const Elem*)a.q;
   Elem* kc = (Elem*)a.k_cache;
   Elem* vc = (Elem*)a.v_cache;
 
@@ -292,38 +327,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   };
   issue(0, 0);
   if constexpr (NBUF == 3) issue(1, 1);  // rows past the chunk read as zero
-
-  // ---- the rows this wave rotates (q heads, then the appended k row, one
-  // ---- wave per row, one (even, odd) pair per lane; D/2 <= 64) and v_new:
-  // ---- loaded now, so that their latency overlaps the K/V loads and the angles
-  const float qscale = kLog2e / sqrtf((float)D);
-  const int nrows = nh + (owns_new ? 1 : 0);
-  constexpr int MAXR = (GP + 1 + 3) / 4;  // rows per wave
-  float rx[MAXR][2];
-  Elem vn0 = Elem(0), vn1 = Elem(0);
-#pragma unroll
-  for (int j = 0; j < MAXR; ++j) {
-    const int r = wave + 4 * j;
-    rx[j][0] = rx[j][1] = 0.f;
-    if (r < nrows && lane < D / 2) {
-      const bool is_k = r == nh;
-      const Elem* src = is_k ? (const Elem*)a.k_new + ((size_t)b * a.Hkv + g) * D
-                             : qg + ((size_t)b * a.H + h0 + r) * D;
-      rx[j][0] = TR::to_f(src[2 * lane]);
-      rx[j][1] = TR::to_f(src[2 * lane + 1]);
-      if (is_k) {
-        const Elem* vsrc = (const Elem*)a.v_new + ((size_t)b * a.Hkv + g) * D;
-        vn0 = vsrc[2 * lane];
-        vn1 = vsrc[2 * lane + 1];
-        if (a.ve_new != nullptr) {  // value embedding: v_new + gate * ve_new, rounded once
-          const Elem* esrc = (const Elem*)a.ve_new + ((size_t)b * a.Hkv + g) * D;
-          const float gg = TR::to_f(((const Elem*)a.ve_gate)[(size_t)b * a.Hkv + g]);
-          vn0 = TR::from_f(TR::to_f(vn0) + gg * TR::to_f(esrc[2 * lane]));
-          vn1 = TR::from_f(TR::to_f(vn1) + gg * TR::to_f(esrc[2 * lane + 1]));
-        }
-      }
-    }
-  }
 
   // ---- cos/sin at position pos: the angle is formed and reduced modulo
   // ---- 2*pi in fp64, then evaluated in fp32 on [-pi, pi]
