@@ -271,6 +271,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   }
 
 
+  // theta_i = base^(-2i/D) of this lane's pair, formed while the length loads
+  const double theta = tid < D / 2 ? exp2(-(double)tid / (D / 2) * a.log2_base) : 0.0;
   const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], Lp, a.Tmax);
   const int pos = L - 1;
   const int lo = L > a.W ? L - a.W : 0;
@@ -331,7 +333,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
   // ---- cos/sin at position pos: the angle is formed and reduced modulo
   // ---- 2*pi in fp64, then evaluated in fp32 on [-pi, pi]
   if (tid < D / 2) {
-    const double theta = exp2(-(double)tid / (D / 2) * a.log2_base);
     const double ang = (double)pos * theta;
     const double kq = rint(ang * 0.15915494309189535);
     double r = fma(-kq, 6.283185307179586, ang);
