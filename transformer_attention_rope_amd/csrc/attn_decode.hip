@@ -270,7 +270,6 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(DecArgs a) {
     }
   }
 
-
   // theta_i = base^(-2i/D) of this lane's pair, formed while the length loads
   const double theta = tid < D / 2 ? exp2(-(double)tid / (D / 2) * a.log2_base) : 0.0;
   const int L = a.order ? s_len[b] : clamp_len(a.seqlens[b], Lp, a.Tmax);
